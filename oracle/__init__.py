@@ -1,0 +1,20 @@
+"""CPU oracle for the per-expert mixed-precision MoE expert layer (PagedWeight).
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package. The GPU library never imports, links or
+calls it, and it shares no code with the library: the only common dependency
+is the seeded input generator in ``synth``.
+
+Plain, slow and written to be checked by eye against the pages:
+
+* ``quant``  Eq. 2 of the PagedWeight page (section "Implementation Details"):
+             per-expert scale, codes, the page byte layout, the loss table.
+* ``alloc``  Eq. 1 of the PagedWeight page (section "Quality-Aware
+             Quantization"): brute force and an exact dynamic programme.
+* ``moe``    the forward pass of section "Dynamic Paging": top-k router,
+             SwiGLU experts on dequantized weights, weighted combine.
+
+All floating-point arithmetic is float64 except where a rounding step is part
+of the definition (the fp32 scale, the bf16 activations).
+"""
+from . import quant, alloc, moe  # noqa: F401

@@ -1,0 +1,170 @@
+/*
+ * pagedweight.h -- C ABI of the per-expert mixed-precision MoE expert layer
+ * (PagedWeight) for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (PagedWeight page):
+ *   - section "Implementation Details", Eq. 2: each expert's SwiGLU weights
+ *     are quantized uniformly and symmetrically with one scale per expert,
+ *     s_e = max|w| / (2^(b_e-1) - 1), q = round(w / s_e), b_e in {3, 4, 8};
+ *   - section "Quality-Aware Quantization", Eq. 1: the bit-widths solve
+ *     min sum_e p_e L_e(b_e)  s.t.  sum_e b_e W_e <= B;
+ *   - section "Dynamic Paging": codes live in pages of a GPU page pool, a
+ *     page table maps expert id -> page (section "Implementation Details",
+ *     "Memory Management"), the router picks the experts a token needs and
+ *     their pages are dequantized on the fly inside the expert FFN.
+ *
+ * Conventions (every entry point):
+ *   - Returns pw_status: 0 on success, a negative code on error. Nothing
+ *     aborts or throws. pw_last_error(ctx) gives a message for the last
+ *     failed call on that context.
+ *   - Device pointers are BORROWED: the caller (for example PyTorch) owns
+ *     the memory and keeps it alive while the context uses it. Host
+ *     pointers are read or written only during the call.
+ *   - Layouts are row-major and contiguous.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All device
+ *     work is enqueued on it in call order; a later call on the same stream
+ *     sees the results of an earlier one. Calls on different streams must be
+ *     ordered by the caller.
+ *   - A context is not thread-safe: serialise calls on one context.
+ *   - On error the page table and the pool contents stay as they were.
+ *   - Shapes: d_model and d_ff must be multiples of 128, 1 <= top_k <= 32,
+ *     top_k <= num_experts <= 1024.
+ */
+#ifndef PAGEDWEIGHT_H
+#define PAGEDWEIGHT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PW_OK = 0,
+    PW_ERR_INVALID_ARG = -1,       /* null pointer, bad shape, bad value      */
+    PW_ERR_UNSUPPORTED_BITS = -2,  /* a bit-width outside {3, 4, 8}           */
+    PW_ERR_INFEASIBLE_BUDGET = -3, /* B < 3 * sum_e W_e                       */
+    PW_ERR_NONFINITE_WEIGHTS = -4, /* NaN or Inf in the bound masters         */
+    PW_ERR_POOL_CAPACITY = -5,     /* the pages do not fit the bound pool     */
+    PW_ERR_WORKSPACE = -6,         /* no workspace bound, or too small        */
+    PW_ERR_STATE = -7,             /* call out of order (e.g. forward before
+                                      any quantization, or no masters bound)  */
+    PW_ERR_HIP = -8                /* a HIP runtime call failed               */
+} pw_status;
+
+typedef enum { PW_MASTER_F32 = 0, PW_MASTER_F16 = 1 } pw_master_dtype;
+
+/* One MoE layer. W_e = 3 * d_model * d_ff weights per expert. */
+typedef struct {
+    int32_t num_experts;   /* E                                                 */
+    int32_t d_model;       /* d                                                 */
+    int32_t d_ff;          /* F                                                 */
+    int32_t top_k;         /* k experts per token                               */
+    int32_t renorm;        /* 0: g = softmax over all E experts;
+                              1: softmax renormalised over the k chosen         */
+    int32_t max_tokens;    /* largest T passed to pw_moe_forward                */
+    int32_t master_dtype;  /* pw_master_dtype of the bound masters              */
+} pw_layer_desc;
+
+/* Host copy of one page-table entry. */
+typedef struct {
+    uint64_t offset;   /* byte offset of the page in the pool (256-B aligned)  */
+    uint64_t nbytes;   /* page bytes = 3 * d * F * bits / 8                    */
+    float scale;       /* s_e, the fp32 value nearest max|w| / (2^(b-1) - 1)   */
+    uint8_t bits;      /* 3, 4 or 8; 0 = no page yet                           */
+    uint8_t pad_[3];
+} pw_page_entry;
+
+/* Per-kernel timing gathered by pw_profile (milliseconds, summed). */
+typedef struct {
+    double route_ms;     /* router + grouping kernels          */
+    double gate_up_ms;   /* gate/up + SwiGLU kernels           */
+    double down_ms;      /* down-projection kernels            */
+    double combine_ms;   /* weighted combine kernel            */
+    int64_t forwards;    /* pw_moe_forward calls timed         */
+} pw_profile_data;
+
+typedef struct pw_ctx pw_ctx;   /* opaque, owned by the library */
+
+/* Validate `desc` and create a context. No device memory is touched until
+ * the first call that needs the GPU (that call uses the current device). */
+pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out);
+void pw_destroy(pw_ctx* ctx);
+
+/* Bind the fp32 or fp16 masters (device): w1 and w3 are [E, F, d] (gate,
+ * up), w2 is [E, d, F] (down). Invalidates cached max|w| and losses;
+ * existing pages stay valid until the next quantization. */
+pw_status pw_bind_masters(pw_ctx* ctx, const void* w1, const void* w3, const void* w2);
+
+/* Pool bytes needed for the given host bits[E] (each page 256-B aligned);
+ * 0 if a bit-width is unsupported. */
+uint64_t pw_pool_bytes_for_bits(const pw_ctx* ctx, const uint8_t* bits);
+
+/* Bind the device page pool: `pool` 256-B aligned, `capacity_bytes` usable.
+ * Rebinding drops all pages (the next quantization rewrites them). */
+pw_status pw_bind_pool(pw_ctx* ctx, void* pool, uint64_t capacity_bytes);
+
+/* Device workspace bytes needed by every call for max_tokens. */
+uint64_t pw_workspace_bytes(const pw_ctx* ctx);
+pw_status pw_bind_workspace(pw_ctx* ctx, void* ws, uint64_t bytes);
+
+/* Quantize every expert at the host bits[E] (each in {3, 4, 8}) from the
+ * masters into the pool and upload the page table. The first call after
+ * pw_bind_masters measures max|w| per expert on the device and waits for
+ * it (one stream synchronisation). Eq. 2; layout of a page: the W1 codes,
+ * then W3, then W2, each row-major [out, in] as a little-endian
+ * LSB-first bitstream of b-bit codes u = q + 2^(b-1). */
+pw_status pw_quantize_experts(pw_ctx* ctx, const uint8_t* bits, void* stream);
+
+/* Move the weight budget: solve Eq. 1 on the host for budget_bits B with
+ * host importance[E] (>= 0) and host loss[E][3] (L for b = 3, 4, 8) or
+ * NULL to use the measured per-expert MSE of Eq. 2 (computed on the
+ * device once per binding of the masters; the first such call waits for
+ * it). Only experts whose bit-width changes are re-quantized from the
+ * masters and re-placed; the new page table is uploaded after their pages
+ * are written. bits_out (host [E]) receives the allocation if non-NULL. */
+pw_status pw_set_budget(pw_ctx* ctx, uint64_t budget_bits, const double* importance,
+                        const double* loss, uint8_t* bits_out, void* stream);
+
+/* Forward pass of the expert layer (section "Dynamic Paging"):
+ * x bf16 [T, d] and logits fp32 [T, E] in, y fp32 [T, d] out (overwritten).
+ * Per token: the top_k largest logits (equal values -> lower expert index),
+ * g = softmax weight (see desc.renorm), y = sum_j g_j * W2 (silu(W1 x) *
+ * (W3 x)) with W = s_e * q read from the pages. 0 <= T <= max_tokens; T = 0
+ * does nothing. Asynchronous: no host synchronisation. */
+pw_status pw_moe_forward(pw_ctx* ctx, const void* x, const float* logits, int32_t T,
+                         float* y, void* stream);
+
+/* Router and grouping only (the first steps of pw_moe_forward), for
+ * inspection: ids int32 [T, k] (descending logit order), g fp32 [T, k] and
+ * counts int32 [E] (tokens routed to each expert), all device pointers. */
+pw_status pw_route(pw_ctx* ctx, const float* logits, int32_t T, int32_t* ids, float* g,
+                   int32_t* counts, void* stream);
+
+/* Host copy of the page table (entries [E]). */
+pw_status pw_get_page_table(const pw_ctx* ctx, pw_page_entry* out);
+
+/* Measured loss table L[E][3] (b = 3, 4, 8; float64) into host memory,
+ * computing it first if needed. Synchronises `stream`. */
+pw_status pw_get_loss_table(pw_ctx* ctx, double* out, void* stream);
+
+/* Eq. 1 solved exactly on the host (no context, no GPU): W[E] weights per
+ * expert, p[E] importance, L[E][3] losses, budget B in bits. Writes
+ * bits_out[E]. Among allocations with the same objective it returns the
+ * one with the fewest total bits. */
+pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, const double* L,
+                              uint64_t budget_bits, uint8_t* bits_out);
+
+/* Timing of the forward kernels with HIP events on the forward's stream.
+ * enable = 1 starts (and clears) collection, 0 stops it. pw_profile_read
+ * waits for the recorded events and returns the sums. */
+pw_status pw_profile(pw_ctx* ctx, int32_t enable);
+pw_status pw_profile_read(pw_ctx* ctx, pw_profile_data* out);
+
+const char* pw_last_error(const pw_ctx* ctx);
+const char* pw_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDWEIGHT_H */

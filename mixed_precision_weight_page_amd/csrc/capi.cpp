@@ -1,0 +1,621 @@
+// C ABI of the per-expert mixed-precision MoE expert layer: context, page
+// pool placement, page-table upload, and the order of kernel launches.
+// The operations follow the PagedWeight page: Eq. 2 (section
+// "Implementation Details") for the quantizer, Eq. 1 (section
+// "Quality-Aware Quantization") for the allocation, the page table of
+// "Memory Management" and the on-the-fly dequantization of section
+// "Dynamic Paging".
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pw_internal.h"
+
+using namespace pw;
+
+struct pw_ctx {
+    pw_layer_desc desc{};
+    int E = 0, d = 0, F = 0, k = 0;
+    int64_t M = 0;        // F * d weights per matrix
+    uint64_t We = 0;      // 3 * M weights per expert
+    Layout lay{};
+
+    const void* w1 = nullptr;
+    const void* w3 = nullptr;
+    const void* w2 = nullptr;
+    uint64_t masters_gen = 0;   // bumped by every pw_bind_masters
+    uint8_t* pool = nullptr;
+    uint64_t pool_cap = 0;
+    uint8_t* ws = nullptr;
+    uint64_t ws_bytes = 0;
+
+    // host mirror of the page table
+    std::vector<pw_page_entry> table;
+    bool pages_valid = false;
+    uint64_t pages_gen = 0;     // masters generation the pages were packed from
+
+    // per-expert statistics of the bound masters
+    bool absmax_valid = false, loss_valid = false;
+    std::vector<float> absmax;
+    std::vector<double> loss;
+
+    // device state (allocated on first device use)
+    int device = -1;
+    uint8_t* dev = nullptr;     // two tables (each off/scale/bits/list), absmax, flags, loss
+    uint8_t* host_stage = nullptr;   // pinned: table upload + statistics readback
+    hipEvent_t upload_done = nullptr;
+    int cur = 0;                // active device table
+
+    // profiling
+    bool profiling = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    int64_t forwards_timed = 0;
+
+    std::string err;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+pw_status fail(pw_ctx* c, pw_status s, const char* fmt, ...) {
+    if (c) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        c->err = buf;
+        if (getenv("PW_LOG")) fprintf(stderr, "[pagedweight] %s\n", buf);
+    }
+    return s;
+}
+
+#define HIP_TRY(ctx, expr)                                                                    \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail(ctx, PW_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));     \
+    } while (0)
+
+// device block: per table [off u64 E][scale f32 E][bits i32 E][list i32 E]
+size_t table_bytes(int E) { return align_up((size_t)E * 20, kAlign); }
+size_t dev_bytes(int E) { return 2 * table_bytes(E) + align_up((size_t)E * 4 + 16, kAlign) + (size_t)E * 24; }
+
+DevTable dev_table(pw_ctx* c, int which) {
+    uint8_t* b = c->dev + which * table_bytes(c->E);
+    DevTable t;
+    t.off = reinterpret_cast<uint64_t*>(b);
+    t.scale = reinterpret_cast<float*>(b + (size_t)c->E * 8);
+    t.bits = reinterpret_cast<int32_t*>(b + (size_t)c->E * 12);
+    return t;
+}
+int32_t* dev_list(pw_ctx* c, int which) {
+    return reinterpret_cast<int32_t*>(c->dev + which * table_bytes(c->E) + (size_t)c->E * 16);
+}
+uint32_t* dev_absmax(pw_ctx* c) { return reinterpret_cast<uint32_t*>(c->dev + 2 * table_bytes(c->E)); }
+uint32_t* dev_flags(pw_ctx* c) { return dev_absmax(c) + c->E; }
+double* dev_loss(pw_ctx* c) {
+    return reinterpret_cast<double*>(c->dev + 2 * table_bytes(c->E) + align_up((size_t)c->E * 4 + 16, kAlign));
+}
+
+pw_status ensure_device(pw_ctx* c) {
+    if (c->dev) {
+        int cur = -1;
+        HIP_TRY(c, hipGetDevice(&cur));
+        if (cur != c->device)
+            return fail(c, PW_ERR_STATE, "context belongs to device %d, current device is %d",
+                        c->device, cur);
+        return PW_OK;
+    }
+    HIP_TRY(c, hipGetDevice(&c->device));
+    void* p = nullptr;
+    HIP_TRY(c, hipMalloc(&p, dev_bytes(c->E)));
+    c->dev = static_cast<uint8_t*>(p);
+    HIP_TRY(c, hipMemset(c->dev, 0, dev_bytes(c->E)));
+    void* h = nullptr;
+    HIP_TRY(c, hipHostMalloc(&h, dev_bytes(c->E), hipHostMallocDefault));
+    c->host_stage = static_cast<uint8_t*>(h);
+    HIP_TRY(c, hipEventCreateWithFlags(&c->upload_done, hipEventDisableTiming));
+    HIP_TRY(c, hipEventRecord(c->upload_done, nullptr));
+    return PW_OK;
+}
+
+FwdWork fwd_work(pw_ctx* c) {
+    FwdWork w;
+    uint8_t* b = c->ws;
+    w.ids = reinterpret_cast<int32_t*>(b + c->lay.ids);
+    w.g = reinterpret_cast<float*>(b + c->lay.g);
+    w.rank = reinterpret_cast<int32_t*>(b + c->lay.rank);
+    w.pos = reinterpret_cast<int32_t*>(b + c->lay.pos);
+    w.sorted = reinterpret_cast<int32_t*>(b + c->lay.sorted);
+    w.cnt = reinterpret_cast<int32_t*>(b + c->lay.cnt);
+    w.off = reinterpret_cast<int32_t*>(b + c->lay.off);
+    w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
+    w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
+    w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
+    w.O = reinterpret_cast<float*>(b + c->lay.O);
+    return w;
+}
+
+float scale_for(float m, int b) {
+    return m == 0.0f ? 0.0f : (float)((double)m / (double)qmax_of(b));
+}
+
+uint64_t page_bytes(const pw_ctx* c, int b) { return align_up(c->We * (uint64_t)b / 8, kPageAlign); }
+
+// max|w| per expert (one stream synchronisation per binding of the masters)
+pw_status ensure_absmax(pw_ctx* c, hipStream_t s) {
+    if (c->absmax_valid) return PW_OK;
+    const int f16 = c->desc.master_dtype == PW_MASTER_F16;
+    HIP_TRY(c, hipMemsetAsync(dev_absmax(c), 0, (size_t)c->E * 4 + 16, s));
+    HIP_TRY(c, launch_absmax(c->w1, c->w3, c->w2, f16, c->E, c->M, dev_absmax(c), dev_flags(c), s));
+    HIP_TRY(c, hipEventSynchronize(c->upload_done));
+    HIP_TRY(c, hipMemcpyAsync(c->host_stage, dev_absmax(c), (size_t)c->E * 4 + 16,
+                              hipMemcpyDeviceToHost, s));
+    HIP_TRY(c, hipStreamSynchronize(s));
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(c->host_stage);
+    if (h[c->E] != 0) return fail(c, PW_ERR_NONFINITE_WEIGHTS, "masters contain NaN or Inf");
+    c->absmax.resize(c->E);
+    for (int e = 0; e < c->E; ++e) {
+        uint32_t u = h[e];
+        float f;
+        std::memcpy(&f, &u, 4);
+        c->absmax[e] = f;
+    }
+    c->absmax_valid = true;
+    return PW_OK;
+}
+
+pw_status ensure_loss(pw_ctx* c, hipStream_t s) {
+    if (c->loss_valid) return PW_OK;
+    pw_status st = ensure_absmax(c, s);
+    if (st != PW_OK) return st;
+    if (!c->ws || c->ws_bytes < c->lay.total)
+        return fail(c, PW_ERR_WORKSPACE, "measuring losses needs a workspace of %llu bytes",
+                    (unsigned long long)c->lay.total);
+    const int f16 = c->desc.master_dtype == PW_MASTER_F16;
+    HIP_TRY(c, launch_loss(c->w1, c->w3, c->w2, f16, c->E, c->M, dev_absmax(c),
+                           reinterpret_cast<double*>(c->ws + c->lay.partial), dev_loss(c), s));
+    HIP_TRY(c, hipEventSynchronize(c->upload_done));
+    HIP_TRY(c, hipMemcpyAsync(c->host_stage, dev_loss(c), (size_t)c->E * 24, hipMemcpyDeviceToHost, s));
+    HIP_TRY(c, hipStreamSynchronize(s));
+    c->loss.assign(reinterpret_cast<const double*>(c->host_stage),
+                   reinterpret_cast<const double*>(c->host_stage) + 3 * c->E);
+    c->loss_valid = true;
+    return PW_OK;
+}
+
+// Place the pages of the new allocation. Unchanged experts keep their
+// pages; changed experts go first-fit (largest first) into the space the
+// unchanged pages leave; if that fails every page is rewritten densely in
+// expert order. Returns the list of experts to pack.
+pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
+                std::vector<int32_t>& list) {
+    const int E = c->E;
+    const bool fresh = !c->pages_valid || c->pages_gen != c->masters_gen;
+    nt.assign(E, pw_page_entry{});
+    std::vector<char> changed(E, 1);
+    for (int e = 0; e < E; ++e) {
+        nt[e].bits = bits[e];
+        nt[e].nbytes = c->We * bits[e] / 8;
+        nt[e].scale = scale_for(c->absmax[e], bits[e]);
+        if (!fresh && c->table[e].bits == bits[e]) {
+            changed[e] = 0;
+            nt[e].offset = c->table[e].offset;
+        }
+    }
+    bool ok = !fresh;
+    if (ok) {
+        // free space = pool minus the unchanged pages
+        std::vector<std::pair<uint64_t, uint64_t>> used;
+        for (int e = 0; e < E; ++e)
+            if (!changed[e]) used.push_back({nt[e].offset, nt[e].offset + page_bytes(c, bits[e])});
+        std::sort(used.begin(), used.end());
+        std::vector<std::pair<uint64_t, uint64_t>> holes;
+        uint64_t at = 0;
+        for (auto& u : used) {
+            if (u.first > at) holes.push_back({at, u.first});
+            at = std::max(at, u.second);
+        }
+        if (c->pool_cap > at) holes.push_back({at, c->pool_cap});
+        std::vector<int> order;
+        for (int e = 0; e < E; ++e)
+            if (changed[e]) order.push_back(e);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int a, int b) { return bits[a] > bits[b]; });
+        for (int e : order) {
+            const uint64_t need = page_bytes(c, bits[e]);
+            bool placed = false;
+            for (auto& h : holes) {
+                if (h.second - h.first >= need) {
+                    nt[e].offset = h.first;
+                    h.first += need;
+                    placed = true;
+                    break;
+                }
+            }
+            if (!placed) { ok = false; break; }
+        }
+    }
+    if (!ok) {
+        uint64_t at = 0;
+        for (int e = 0; e < E; ++e) {
+            nt[e].offset = at;
+            at += page_bytes(c, bits[e]);
+            changed[e] = 1;
+        }
+        if (at > c->pool_cap)
+            return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, pool holds %llu",
+                        (unsigned long long)at, (unsigned long long)c->pool_cap);
+    }
+    list.clear();
+    for (int e = 0; e < E; ++e)
+        if (changed[e]) list.push_back(e);
+    return PW_OK;
+}
+
+// Quantize at the given bits: place, upload the new table (into the idle
+// device copy), pack the changed experts, then make the new table current.
+pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s) {
+    std::vector<pw_page_entry> nt;
+    std::vector<int32_t> list;
+    pw_status st = place(c, bits, nt, list);
+    if (st != PW_OK) return st;
+    if (list.empty()) return PW_OK;
+    const int E = c->E;
+    const int next = 1 - c->cur;
+    HIP_TRY(c, hipEventSynchronize(c->upload_done));   // staging buffer free again
+    uint8_t* h = c->host_stage;
+    for (int e = 0; e < E; ++e) {
+        std::memcpy(h + (size_t)e * 8, &nt[e].offset, 8);
+        std::memcpy(h + (size_t)E * 8 + (size_t)e * 4, &nt[e].scale, 4);
+        const int32_t b = nt[e].bits;
+        std::memcpy(h + (size_t)E * 12 + (size_t)e * 4, &b, 4);
+    }
+    std::memcpy(h + (size_t)E * 16, list.data(), list.size() * 4);
+    c->pages_valid = false;   // until the pack is enqueued
+    HIP_TRY(c, hipMemcpyAsync(dev_table(c, next).off, h, (size_t)E * 16 + list.size() * 4,
+                              hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipEventRecord(c->upload_done, s));
+    const int f16 = c->desc.master_dtype == PW_MASTER_F16;
+    HIP_TRY(c, launch_pack(c->w1, c->w3, c->w2, f16, c->M, dev_table(c, next), dev_list(c, next),
+                           (int)list.size(), c->pool, s));
+    c->table = nt;
+    c->cur = next;
+    c->pages_valid = true;
+    c->pages_gen = c->masters_gen;
+    return PW_OK;
+}
+
+pw_status check_bits(pw_ctx* c, const uint8_t* bits) {
+    if (!bits) return fail(c, PW_ERR_INVALID_ARG, "bits is NULL");
+    for (int e = 0; e < c->E; ++e)
+        if (bits_index(bits[e]) < 0)
+            return fail(c, PW_ERR_UNSUPPORTED_BITS, "expert %d: %d bits (supported: 3, 4, 8)", e,
+                        (int)bits[e]);
+    return PW_OK;
+}
+
+pw_status need_masters_pool(pw_ctx* c) {
+    if (!c->w1 || !c->w3 || !c->w2) return fail(c, PW_ERR_STATE, "no masters bound");
+    if (!c->pool) return fail(c, PW_ERR_STATE, "no pool bound");
+    return PW_OK;
+}
+
+hipEvent_t next_event(pw_ctx* c) {
+    if (c->ev_used == c->ev_pool.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        c->ev_pool.push_back(e);
+    }
+    return c->ev_pool[c->ev_used++];
+}
+
+}  // namespace
+
+namespace pw {
+Layout workspace_layout(int E, int d, int F, int k, int max_tokens) {
+    Layout L{};
+    const uint64_t P = (uint64_t)max_tokens * k;
+    uint64_t at = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t o = at;
+        at = align_up(at + bytes, kAlign);
+        return o;
+    };
+    L.ids = take(4 * P);
+    L.g = take(4 * P);
+    L.rank = take(4 * P);
+    L.pos = take(4 * P);
+    L.sorted = take(4 * P);
+    L.cnt = take(4 * (uint64_t)E);
+    L.off = take(4 * (uint64_t)(E + 1));
+    L.act = take(4 * (uint64_t)E);
+    L.n_act = take(4);
+    L.H = take(2 * P * (uint64_t)F);
+    L.O = take(4 * P * (uint64_t)d);
+    L.fwd_end = at;
+    // the loss pass reuses the same memory (calls on one stream are ordered)
+    const uint64_t nblk = 3 * (uint64_t)F * d / kStatChunk;
+    L.partial = 0;
+    L.stats_end = align_up(8 * 3 * nblk * (uint64_t)E, kAlign);
+    L.total = std::max(L.fwd_end, L.stats_end);
+    return L;
+}
+}  // namespace pw
+
+extern "C" {
+
+const char* pw_status_str(int32_t s) {
+    switch (s) {
+        case PW_OK: return "ok";
+        case PW_ERR_INVALID_ARG: return "invalid argument";
+        case PW_ERR_UNSUPPORTED_BITS: return "unsupported bit-width";
+        case PW_ERR_INFEASIBLE_BUDGET: return "infeasible budget";
+        case PW_ERR_NONFINITE_WEIGHTS: return "non-finite weights";
+        case PW_ERR_POOL_CAPACITY: return "pool capacity exceeded";
+        case PW_ERR_WORKSPACE: return "workspace missing or too small";
+        case PW_ERR_STATE: return "call out of order";
+        case PW_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out) {
+    if (!desc || !out) return PW_ERR_INVALID_ARG;
+    *out = nullptr;
+    const pw_layer_desc& d = *desc;
+    if (d.num_experts < 1 || d.num_experts > kMaxExperts || d.d_model < kRowAlign ||
+        d.d_ff < kRowAlign || d.d_model % kRowAlign || d.d_ff % kRowAlign || d.top_k < 1 ||
+        d.top_k > kMaxTopK || d.top_k > d.num_experts || d.max_tokens < 0 ||
+        (d.renorm != 0 && d.renorm != 1) ||
+        (d.master_dtype != PW_MASTER_F32 && d.master_dtype != PW_MASTER_F16))
+        return PW_ERR_INVALID_ARG;
+    if ((int64_t)d.max_tokens * d.top_k > (int64_t)1 << 30) return PW_ERR_INVALID_ARG;
+    pw_ctx* c = new (std::nothrow) pw_ctx;
+    if (!c) return PW_ERR_INVALID_ARG;
+    c->desc = d;
+    c->E = d.num_experts;
+    c->d = d.d_model;
+    c->F = d.d_ff;
+    c->k = d.top_k;
+    c->M = (int64_t)d.d_model * d.d_ff;
+    c->We = 3 * (uint64_t)c->M;
+    c->lay = workspace_layout(c->E, c->d, c->F, c->k, d.max_tokens);
+    c->table.assign(c->E, pw_page_entry{});
+    *out = c;
+    return PW_OK;
+}
+
+void pw_destroy(pw_ctx* c) {
+    if (!c) return;
+    for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+    if (c->upload_done) {
+        (void)hipEventSynchronize(c->upload_done);
+        (void)hipEventDestroy(c->upload_done);
+    }
+    if (c->host_stage) (void)hipHostFree(c->host_stage);
+    if (c->dev) (void)hipFree(c->dev);
+    delete c;
+}
+
+pw_status pw_bind_masters(pw_ctx* c, const void* w1, const void* w3, const void* w2) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!w1 || !w3 || !w2) return fail(c, PW_ERR_INVALID_ARG, "null master pointer");
+    const uintptr_t a = 16;
+    if ((uintptr_t)w1 % a || (uintptr_t)w3 % a || (uintptr_t)w2 % a)
+        return fail(c, PW_ERR_INVALID_ARG, "masters must be 16-byte aligned");
+    c->w1 = w1;
+    c->w3 = w3;
+    c->w2 = w2;
+    c->masters_gen++;
+    c->absmax_valid = c->loss_valid = false;
+    return PW_OK;
+}
+
+uint64_t pw_pool_bytes_for_bits(const pw_ctx* c, const uint8_t* bits) {
+    if (!c || !bits) return 0;
+    uint64_t t = 0;
+    for (int e = 0; e < c->E; ++e) {
+        if (bits_index(bits[e]) < 0) return 0;
+        t += page_bytes(c, bits[e]);
+    }
+    return t;
+}
+
+pw_status pw_bind_pool(pw_ctx* c, void* pool, uint64_t cap) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!pool || (uintptr_t)pool % kPageAlign)
+        return fail(c, PW_ERR_INVALID_ARG, "pool must be non-NULL and 256-byte aligned");
+    c->pool = static_cast<uint8_t*>(pool);
+    c->pool_cap = cap;
+    c->pages_valid = false;
+    c->table.assign(c->E, pw_page_entry{});
+    return PW_OK;
+}
+
+uint64_t pw_workspace_bytes(const pw_ctx* c) { return c ? c->lay.total : 0; }
+
+pw_status pw_bind_workspace(pw_ctx* c, void* ws, uint64_t bytes) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!ws || (uintptr_t)ws % kAlign) return fail(c, PW_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (bytes < c->lay.total)
+        return fail(c, PW_ERR_WORKSPACE, "workspace of %llu bytes, need %llu",
+                    (unsigned long long)bytes, (unsigned long long)c->lay.total);
+    c->ws = static_cast<uint8_t*>(ws);
+    c->ws_bytes = bytes;
+    return PW_OK;
+}
+
+pw_status pw_quantize_experts(pw_ctx* c, const uint8_t* bits, void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    pw_status st = check_bits(c, bits);
+    if (st != PW_OK) return st;
+    if ((st = need_masters_pool(c)) != PW_OK) return st;
+    uint64_t need = 0;
+    for (int e = 0; e < c->E; ++e) need += page_bytes(c, bits[e]);
+    if (need > c->pool_cap)
+        return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, pool holds %llu",
+                    (unsigned long long)need, (unsigned long long)c->pool_cap);
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = ensure_absmax(c, s)) != PW_OK) return st;
+    return apply_bits(c, bits, s);
+}
+
+pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importance,
+                        const double* loss, uint8_t* bits_out, void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!importance) return fail(c, PW_ERR_INVALID_ARG, "importance is NULL");
+    pw_status st = need_masters_pool(c);
+    if (st != PW_OK) return st;
+    if (budget_bits < 3 * c->We * (uint64_t)c->E)
+        return fail(c, PW_ERR_INFEASIBLE_BUDGET, "budget %llu bits < 3 bits per weight",
+                    (unsigned long long)budget_bits);
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = ensure_absmax(c, s)) != PW_OK) return st;
+    const double* L = loss;
+    if (!L) {
+        if ((st = ensure_loss(c, s)) != PW_OK) return st;
+        L = c->loss.data();
+    }
+    std::vector<uint64_t> W(c->E, c->We);
+    std::vector<uint8_t> bits(c->E);
+    st = solve_allocation(c->E, W.data(), importance, L, budget_bits, bits.data(), &c->err);
+    if (st != PW_OK) return st;
+    if ((st = apply_bits(c, bits.data(), s)) != PW_OK) return st;
+    if (bits_out) std::memcpy(bits_out, bits.data(), c->E);
+    return PW_OK;
+}
+
+static pw_status forward_checks(pw_ctx* c, const void* logits, int32_t T) {
+    if (T < 0 || T > c->desc.max_tokens)
+        return fail(c, PW_ERR_INVALID_ARG, "T = %d outside [0, %d]", T, c->desc.max_tokens);
+    if (T > 0 && !logits) return fail(c, PW_ERR_INVALID_ARG, "null logits");
+    if (!c->ws) return fail(c, PW_ERR_WORKSPACE, "no workspace bound");
+    return PW_OK;
+}
+
+pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, float* g,
+                   int32_t* counts, void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    pw_status st = forward_checks(c, logits, T);
+    if (st != PW_OK) return st;
+    if (T == 0) return PW_OK;
+    if (!ids || !g || !counts) return fail(c, PW_ERR_INVALID_ARG, "null output pointer");
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const FwdWork w = fwd_work(c);
+    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
+    HIP_TRY(c, launch_route(ra, w, s));
+    const size_t P = (size_t)T * c->k;
+    HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(c, hipMemcpyAsync(g, w.g, P * 4, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(c, hipMemcpyAsync(counts, w.cnt, (size_t)c->E * 4, hipMemcpyDeviceToDevice, s));
+    return PW_OK;
+}
+
+pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t T, float* y,
+                         void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    pw_status st = forward_checks(c, logits, T);
+    if (st != PW_OK) return st;
+    if (!c->pages_valid) return fail(c, PW_ERR_STATE, "no quantized pages: call pw_quantize_experts or pw_set_budget first");
+    if (T == 0) return PW_OK;
+    if (!x || !y) return fail(c, PW_ERR_INVALID_ARG, "null x or y");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16)
+        return fail(c, PW_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const FwdWork w = fwd_work(c);
+    hipEvent_t ev[5] = {};
+    if (c->profiling) {
+        for (auto& e : ev)
+            if (!(e = next_event(c))) return fail(c, PW_ERR_HIP, "hipEventCreate failed");
+        HIP_TRY(c, hipEventRecord(ev[0], s));
+    }
+    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
+    HIP_TRY(c, launch_route(ra, w, s));
+    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[1], s));
+    FfnArgs fa;
+    fa.pool = c->pool;
+    fa.tab = dev_table(c, c->cur);
+    fa.w = w;
+    fa.x = static_cast<const uint16_t*>(x);
+    fa.d = c->d;
+    fa.F = c->F;
+    fa.k = c->k;
+    fa.max_act = std::min<int64_t>(c->E, (int64_t)T * c->k);
+    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, c->F), s));
+    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[2], s));
+    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->d), s));
+    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[3], s));
+    HIP_TRY(c, launch_combine(w, T, c->d, c->k, y, s));
+    if (c->profiling) {
+        HIP_TRY(c, hipEventRecord(ev[4], s));
+        c->forwards_timed++;
+    }
+    return PW_OK;
+}
+
+pw_status pw_get_page_table(const pw_ctx* c, pw_page_entry* out) {
+    if (!c || !out) return PW_ERR_INVALID_ARG;
+    std::memcpy(out, c->table.data(), sizeof(pw_page_entry) * c->E);
+    return PW_OK;
+}
+
+pw_status pw_get_loss_table(pw_ctx* c, double* out, void* stream) {
+    if (!c || !out) return PW_ERR_INVALID_ARG;
+    if (!c->w1) return fail(c, PW_ERR_STATE, "no masters bound");
+    pw_status st = ensure_device(c);
+    if (st != PW_OK) return st;
+    if ((st = ensure_loss(c, static_cast<hipStream_t>(stream))) != PW_OK) return st;
+    std::memcpy(out, c->loss.data(), sizeof(double) * 3 * c->E);
+    return PW_OK;
+}
+
+pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, const double* L,
+                              uint64_t budget_bits, uint8_t* bits_out) {
+    return solve_allocation(E, W, p, L, budget_bits, bits_out, nullptr);
+}
+
+pw_status pw_profile(pw_ctx* c, int32_t enable) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    c->profiling = enable != 0;
+    if (enable) {
+        c->ev_used = 0;
+        c->forwards_timed = 0;
+    }
+    return PW_OK;
+}
+
+pw_status pw_profile_read(pw_ctx* c, pw_profile_data* out) {
+    if (!c || !out) return PW_ERR_INVALID_ARG;
+    std::memset(out, 0, sizeof *out);
+    if (c->ev_used) HIP_TRY(c, hipEventSynchronize(c->ev_pool[c->ev_used - 1]));
+    double* slot[4] = {&out->route_ms, &out->gate_up_ms, &out->down_ms, &out->combine_ms};
+    for (size_t i = 0; i + 5 <= c->ev_used; i += 5)
+        for (int j = 0; j < 4; ++j) {
+            float ms = 0.f;
+            HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_pool[i + j], c->ev_pool[i + j + 1]));
+            *slot[j] += ms;
+        }
+    out->forwards = c->forwards_timed;
+    return PW_OK;
+}
+
+const char* pw_last_error(const pw_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/pagedweight.h"
+
+namespace pw {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kRowAlign = 128;         // codes per row are a multiple of this
+constexpr int kPageAlign = 256;        // page offsets and sizes
+constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
+
+// supported bit-widths, in loss-table order
+__host__ __device__ constexpr int bits_of_index(int i) { return i == 0 ? 3 : i == 1 ? 4 : 8; }
+__host__ __device__ constexpr int bits_index(int b) { return b == 3 ? 0 : b == 4 ? 1 : b == 8 ? 2 : -1; }
+__host__ __device__ constexpr int qmax_of(int b) { return (1 << (b - 1)) - 1; }
+
+// Device page table (structure of arrays, one entry per expert).
+struct DevTable {
+    uint64_t* off;
+    float* scale;
+    int32_t* bits;
+};
+
+// Forward-pass scratch carved out of the bound workspace.
+struct FwdWork {
+    int32_t* ids;      // [P] expert of pair p = t*k + j
+    float* g;          // [P] routing weight
+    int32_t* rank;     // [P] rank of the pair among its expert's pairs
+    int32_t* pos;      // [P] position of the pair in expert-sorted order
+    int32_t* sorted;   // [P] pair at each sorted position
+    int32_t* cnt;      // [E] tokens per expert
+    int32_t* off;      // [E+1] exclusive prefix of cnt
+    int32_t* act;      // [E] experts with cnt > 0, ascending
+    int32_t* n_act;    // [1]
+    _Float16* H;       // [P, F] SwiGLU output per sorted pair
+    float* O;          // [P, d] down-projection output per sorted pair (scaled by s_e)
+};
+
+struct Layout {
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, H, O, fwd_end;
+    uint64_t partial, stats_end;
+    uint64_t total;
+};
+
+Layout workspace_layout(int E, int d, int F, int k, int max_tokens);
+
+// ---- launchers (kernels_*.hip) ----
+hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16, int E,
+                         int64_t M, uint32_t* absmax, uint32_t* flags, hipStream_t s);
+hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, int E,
+                       int64_t M, const uint32_t* absmax, double* partial, double* loss,
+                       hipStream_t s);
+hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int64_t M,
+                       DevTable tab, const int32_t* list, int nlist, uint8_t* pool,
+                       hipStream_t s);
+
+struct RouteArgs {
+    const float* logits;
+    int T, E, k, renorm;
+};
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, hipStream_t s);
+
+struct FfnPlan {
+    int wr, wk;       // waves along rows x waves along K (wr * wk = 4)
+    int kc;           // K codes staged in LDS per chunk
+    int nt_alloc;     // token rows staged in LDS
+    size_t lds;       // dynamic LDS bytes
+};
+FfnPlan plan_ffn(int K, int T, int rows);
+
+struct FfnArgs {
+    const uint8_t* pool;
+    DevTable tab;
+    FwdWork w;
+    const uint16_t* x;   // bf16 [T, d]
+    int d, F, k, max_act;
+};
+hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
+hipError_t launch_combine(const FwdWork& w, int T, int d, int k, float* y, hipStream_t s);
+
+// ---- host allocator (alloc.cpp) ----
+pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,
+                           uint64_t B, uint8_t* bits_out, std::string* err);
+
+}  // namespace pw

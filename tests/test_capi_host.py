@@ -1,0 +1,185 @@
+"""Host-only checks of libpagedweight.so: it loads, it exports every function
+include/pagedweight.h declares, its allocator solves Eq. 1 like the oracle,
+and its argument and state checks fail with the documented status codes.
+No call here touches a GPU."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+from mixed_precision_weight_page_amd import pagedweight as pwb
+from oracle import alloc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedweight.h")
+
+PW_OK, INVALID, UNSUPPORTED, INFEASIBLE, NONFINITE, CAPACITY, WORKSPACE, STATE, HIP = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pw_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pwb.library_path()):
+        pytest.skip("library not built")
+    return pwb.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in pwb._SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(L):
+    for s in range(-8, 1):
+        assert L.pw_status_str(s).decode()
+    assert L.pw_status_str(-99).decode() == "unknown status"
+
+
+def test_solver_matches_oracle_bruteforce(L):
+    rng = random.Random(5)
+    for trial in range(200):
+        E = rng.randint(1, 6)
+        W = [rng.choice([3, 6, 9])] * E if trial % 2 else [rng.choice([2, 4, 6, 10]) for _ in range(E)]
+        p = [rng.random() for _ in range(E)]
+        Ls = []
+        for _ in range(E):
+            a = rng.uniform(1e-4, 1e-2)
+            b = a + rng.uniform(1e-3, 0.3)
+            Ls.append([b + rng.uniform(1e-3, 1.0), b, a])
+        B = rng.randint(3 * sum(W) - 3, 8 * sum(W) + 3)
+        if B < 3 * sum(W):
+            with pytest.raises(pwb.PagedWeightError) as ei:
+                pwb.solve_allocation(W, p, Ls, B)
+            assert ei.value.status == INFEASIBLE
+            continue
+        got = pwb.solve_allocation(W, p, Ls, B).tolist()
+        want, obj = alloc.solve_bruteforce(p, Ls, W, B)
+        assert alloc.used_bits(got, W) <= B
+        assert alloc.objective(got, p, Ls) == pytest.approx(obj, rel=1e-12)
+        assert got == want
+
+
+def test_solver_matches_oracle_dp_at_layer_scale(L):
+    # 128 experts of equal size, budgets of 3.5..8 bits on average
+    rng = np.random.default_rng(7)
+    E, We = 128, 4_718_592
+    p = (np.arange(1, E + 1) ** -1.1)
+    p /= p.sum()
+    l8 = rng.uniform(1e-9, 1e-8, E)
+    l4 = l8 + rng.uniform(1e-6, 1e-5, E)
+    l3 = l4 + rng.uniform(1e-6, 2e-5, E)
+    Ls = np.stack([l3, l4, l8], 1)
+    for avg in (3.5, 4, 5, 6, 8):
+        B = int(avg * 2) * E * We // 2
+        got = pwb.solve_allocation([We] * E, p, Ls, B)
+        want, obj = alloc.solve_dp(p, Ls.tolist(), [We] * E, B)
+        assert int((got.astype(np.int64) * We).sum()) <= B
+        assert alloc.objective(got, p, Ls) == pytest.approx(obj, rel=1e-12)
+        assert got.tolist() == want
+
+
+def test_hand_worked_allocation(L):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "eq1_allocation.json")))
+    for case in g["cases"]:
+        if case.get("infeasible"):
+            with pytest.raises(pwb.PagedWeightError):
+                pwb.solve_allocation(g["W"], g["p"], g["L"], case["B"])
+        else:
+            assert pwb.solve_allocation(g["W"], g["p"], g["L"], case["B"]).tolist() == case["bits"]
+
+
+def test_solver_argument_errors(L):
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        pwb.solve_allocation([0, 1], [1, 1], [[1, 1, 1]] * 2, 100)
+    assert ei.value.status == INVALID
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        pwb.solve_allocation([1, 1], [-1, 1], [[1, 1, 1]] * 2, 100)
+    assert ei.value.status == INVALID
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        pwb.solve_allocation([1, 1], [1, 1], [[np.nan, 1, 1]] * 2, 100)
+    assert ei.value.status == INVALID
+
+
+def make_ctx(L, **kw):
+    d = dict(num_experts=4, d_model=128, d_ff=256, top_k=2, renorm=0, max_tokens=8, master_dtype=0)
+    d.update(kw)
+    desc = pwb.LayerDesc(**d)
+    ctx = ctypes.c_void_p()
+    st = L.pw_create(ctypes.byref(desc), ctypes.byref(ctx))
+    return st, ctx
+
+
+def test_create_rejects_bad_shapes(L):
+    for bad in (dict(d_model=100), dict(d_ff=0), dict(top_k=0), dict(top_k=5),
+                dict(num_experts=2000), dict(renorm=2), dict(master_dtype=7),
+                dict(max_tokens=-1)):
+        st, ctx = make_ctx(L, **bad)
+        assert st == INVALID, bad
+    st, ctx = make_ctx(L)
+    assert st == PW_OK
+    L.pw_destroy(ctx)
+
+
+def test_state_and_argument_errors_without_gpu(L):
+    st, ctx = make_ctx(L)
+    assert st == PW_OK
+    E, d, F = 4, 128, 256
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced by these calls
+    bits = (ctypes.c_uint8 * E)(3, 4, 8, 4)
+    imp = (ctypes.c_double * E)(0.4, 0.3, 0.2, 0.1)
+    # forward before anything
+    assert L.pw_moe_forward(ctx, fake, fake, 1, fake, None) == WORKSPACE
+    # quantize before masters / pool
+    assert L.pw_quantize_experts(ctx, bits, None) == STATE
+    assert L.pw_set_budget(ctx, 10**9, imp, None, None, None) == STATE
+    assert L.pw_bind_masters(ctx, fake, None, fake) == INVALID
+    assert L.pw_bind_masters(ctx, fake, fake, fake) == PW_OK
+    assert L.pw_bind_pool(ctx, ctypes.c_void_p(1 << 20 | 8), 1 << 20) == INVALID   # misaligned
+    need = L.pw_pool_bytes_for_bits(ctx, bits)
+    assert need == sum(3 * d * F * b // 8 for b in (3, 4, 8, 4))
+    assert L.pw_bind_pool(ctx, fake, need - 256) == PW_OK
+    # unsupported bits, and a pool one page too small
+    bad = (ctypes.c_uint8 * E)(3, 5, 8, 4)
+    assert L.pw_quantize_experts(ctx, bad, None) == UNSUPPORTED
+    assert L.pw_pool_bytes_for_bits(ctx, bad) == 0
+    assert L.pw_quantize_experts(ctx, bits, None) == CAPACITY
+    assert b"pool" in L.pw_last_error(ctx)
+    # budget below 3 bits per weight
+    We = 3 * d * F
+    assert L.pw_set_budget(ctx, 3 * We * E - 1, imp, None, None, None) == INFEASIBLE
+    assert L.pw_set_budget(ctx, 10**9, None, None, None, None) == INVALID
+    # workspace: too small is refused, right size accepted
+    wsb = L.pw_workspace_bytes(ctx)
+    assert wsb > 0
+    assert L.pw_bind_workspace(ctx, fake, wsb - 1) == WORKSPACE
+    assert L.pw_bind_workspace(ctx, fake, wsb) == PW_OK
+    # forward: T out of range, then no pages yet
+    assert L.pw_moe_forward(ctx, fake, fake, 9, fake, None) == INVALID
+    assert L.pw_moe_forward(ctx, fake, fake, -1, fake, None) == INVALID
+    assert L.pw_moe_forward(ctx, fake, fake, 1, fake, None) == STATE
+    # T = 0 before quantization is still a state error; page table is empty
+    entries = (pwb.PageEntry * E)()
+    assert L.pw_get_page_table(ctx, entries) == PW_OK
+    assert all(e.bits == 0 for e in entries)
+    L.pw_destroy(ctx)
+
+
+def test_python_binding_raises_with_status(L):
+    layer = pwb.PagedMoELayer(4, 128, 256, 2, max_tokens=8)
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        layer.quantize_experts([3, 4, 8, 4], stream=0)
+    assert ei.value.status == STATE
+    assert "masters" in str(ei.value)

@@ -1,0 +1,218 @@
+"""GPU parity of the HIP path against the CPU oracle at sizes the oracle
+finishes in seconds: codes, scales and pages bit-exact, router choices
+exact, loss table within 1e-12 relative, outputs within the layer
+tolerance (normwise 2e-3, max-abs 1e-2 of max |y_ref|)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from layer_cases import (check_pages, compare_y, cpu_threads, log, make_layer, oracle_bits,
+                         oracle_y)
+from oracle import alloc, moe, quant
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WORKLOADS["tiny"]
+# a decode_fine-shaped layer scaled down: outliers, many experts, top-8
+SMALL_FINE = synth.WORKLOADS["decode_fine"].scaled(name="small_fine", E=32, d=256, F=384, T=40)
+# fp16 masters, for the re-precision path
+SMALL_DYN = synth.WORKLOADS["dynamic"].scaled(name="small_dyn", E=16, d=256, F=256, T=24)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cpu_threads()
+
+
+def test_tiny_pages_and_forward():
+    wl = TINY
+    masters = synth.expert_weights(wl)
+    x, logits = synth.tokens(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    log("tiny: quantize_experts")
+    layer.quantize_experts(wl.bits)
+    torch.cuda.synchronize()
+    check_pages(layer, pool, masters, wl.bits)
+    log("tiny: forward")
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    torch.cuda.synchronize()
+    compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), "tiny")
+
+
+def test_router_matches_oracle():
+    for wl, T in ((TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300)):
+        masters = tuple(torch.zeros(1) for _ in range(3))
+        from mixed_precision_weight_page_amd import PagedMoELayer
+        layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=T)
+        layer.alloc_workspace()
+        _, logits = synth.tokens(wl, T=T)
+        # plant exact ties: equal logits must resolve to the lower index
+        logits[0, :] = 0.25
+        logits[1, 3] = logits[1, 5] = logits[1].max() + 1.0
+        ids, g, counts = layer.route(logits.cuda())
+        torch.cuda.synchronize()
+        rid, rg = moe.route(logits, wl.k)
+        assert torch.equal(ids.cpu().long(), rid), wl.name
+        assert torch.allclose(g.cpu().double(), rg, rtol=2e-6, atol=1e-7), wl.name
+        want = torch.bincount(rid.reshape(-1), minlength=wl.E)
+        assert torch.equal(counts.cpu().long(), want)
+        del masters
+
+
+def test_router_renorm():
+    wl = SMALL_FINE.scaled(renorm=1)
+    from mixed_precision_weight_page_amd import PagedMoELayer
+    layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=40, renorm=1)
+    layer.alloc_workspace()
+    _, logits = synth.tokens(wl, T=40)
+    ids, g, _ = layer.route(logits.cuda())
+    rid, rg = moe.route(logits, wl.k, renorm=True)
+    assert torch.equal(ids.cpu().long(), rid)
+    assert torch.allclose(g.cpu().double(), rg, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("wl", [TINY, SMALL_FINE, SMALL_DYN], ids=lambda w: w.name)
+def test_loss_table_matches_oracle(wl):
+    masters = synth.expert_weights(wl)
+    layer, _ = make_layer(wl, masters, max_tokens=8)
+    got = layer.get_loss_table()
+    _, want = quant.loss_table(*masters)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+    assert np.all(got[:, 2] < got[:, 1])   # 8 bits beat 4 bits
+
+
+@pytest.mark.parametrize("wl", [SMALL_FINE, SMALL_DYN], ids=lambda w: w.name)
+def test_set_budget_pages_and_forward(wl):
+    masters = synth.expert_weights(wl)
+    x, logits = synth.tokens(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    B = wl.budget_bits(4.0)
+    log(f"{wl.name}: set_budget")
+    bits = layer.set_budget(B, synth.importance(wl))
+    torch.cuda.synchronize()
+    want, _ = oracle_bits(wl, masters, B)
+    assert bits.tolist() == want
+    assert int(bits.astype(np.int64).sum()) * wl.W_e <= B
+    check_pages(layer, pool, masters, bits)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, bits), wl.name)
+
+
+def test_ragged_token_counts():
+    # experts with more than 16 tokens (several token blocks), a ragged tail,
+    # a single token, and T = 0
+    wl = synth.WORKLOADS["tiny"].scaled(name="ragged", E=4, d=256, F=256, k=2, T=45,
+                                        bits=(3, 4, 8, 4))
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=64)
+    layer.quantize_experts(wl.bits)
+    for T in (45, 1, 17, 64):
+        x, logits = synth.tokens(wl, T=T)
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"T={T}")
+    empty = torch.empty(0, wl.d, dtype=torch.bfloat16, device="cuda")
+    y0 = layer.moe_forward(empty, torch.empty(0, wl.E, device="cuda"))
+    assert y0.shape == (0, wl.d)
+
+
+def test_deterministic_outputs():
+    wl = SMALL_FINE
+    masters = synth.expert_weights(wl)
+    x, logits = synth.tokens(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    layer.set_budget(wl.budget_bits(4.0), synth.importance(wl))
+    xc, lc = x.cuda(), logits.cuda()
+    y1 = layer.moe_forward(xc, lc).clone()
+    p1 = pool.clone()
+    layer2, pool2 = make_layer(wl, masters, max_tokens=wl.T)
+    layer2.set_budget(wl.budget_bits(4.0), synth.importance(wl))
+    y2 = layer2.moe_forward(xc, lc)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(p1, pool2)
+    assert layer.get_page_table() == layer2.get_page_table()
+
+
+def test_reprecision_schedule():
+    """Budget stepped through avg 8, 6, 4, 3.5, 5 bits on fp16 masters:
+    after every step the pages equal a fresh oracle quantization from the
+    masters, experts whose bits did not change keep their bytes, and the
+    forward pass matches the oracle."""
+    wl = SMALL_DYN
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    _, L = quant.loss_table(*masters)
+    p = synth.importance(wl)
+    prev_bits, prev_pool, prev_table = None, None, None
+    for step, avg in enumerate(wl.schedule):
+        B = wl.budget_bits(avg)
+        bits = layer.set_budget(B, p)
+        torch.cuda.synchronize()
+        want, _ = alloc.solve(p, L.tolist(), [wl.W_e] * wl.E, B)
+        assert bits.tolist() == want, avg
+        check_pages(layer, pool, masters, bits)
+        table = layer.get_page_table()
+        if prev_bits is not None:
+            for e in range(wl.E):
+                if bits[e] == prev_bits[e] and table[e]["offset"] == prev_table[e]["offset"]:
+                    o, n = table[e]["offset"], table[e]["nbytes"]
+                    assert torch.equal(pool[o:o + n].cpu(), prev_pool[o:o + n])
+        x, logits = synth.tokens(wl, step=step)
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, bits), f"avg {avg}")
+        prev_bits, prev_pool, prev_table = bits, pool.cpu(), table
+
+
+def test_failed_budget_keeps_previous_table():
+    wl = SMALL_DYN
+    masters = synth.expert_weights(wl)
+    from mixed_precision_weight_page_amd import PagedWeightError
+    # a pool that holds everything at 4 bits but not at 8
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T,
+                             pool_bytes=int(wl.E * wl.W_e * 4 // 8))
+    p = synth.importance(wl)
+    bits = layer.set_budget(wl.budget_bits(4.0), p)
+    before = layer.get_page_table()
+    snap = pool.cpu()
+    with pytest.raises(PagedWeightError) as ei:
+        layer.set_budget(wl.budget_bits(8.0), p)
+    assert ei.value.status == -5
+    assert layer.get_page_table() == before
+    torch.cuda.synchronize()
+    assert torch.equal(pool.cpu(), snap)
+    x, logits = synth.tokens(wl)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, bits), "after failed budget")
+
+
+def test_nonfinite_masters_rejected():
+    wl = TINY
+    w1, w3, w2 = synth.expert_weights(wl)
+    w2 = w2.clone()
+    w2[3, 7, 9] = float("nan")
+    from mixed_precision_weight_page_amd import PagedWeightError
+    layer, _ = make_layer(wl, (w1, w3, w2), max_tokens=wl.T)
+    with pytest.raises(PagedWeightError) as ei:
+        layer.quantize_experts(wl.bits)
+    assert ei.value.status == -4
+
+
+def test_zero_expert_and_lossless_grid():
+    # expert 1 all zero (s = 0); expert 0 on the 8-bit grid (lossless)
+    wl = synth.WORKLOADS["tiny"].scaled(name="grid", E=3, d=128, F=128, k=2, T=8, bits=(8, 4, 3))
+    w1, w3, w2 = (m.clone() for m in synth.expert_weights(wl))
+    for m in (w1, w3, w2):
+        m[1].zero_()
+        m[0] = torch.round(m[0] / 2 ** -9).clamp(-127, 127) * 2 ** -9
+    w1[0, 0, 0] = 127 * 2 ** -9
+    masters = (w1, w3, w2)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    check_pages(layer, pool, masters, wl.bits)
+    assert layer.get_page_table()[1]["scale"] == 0.0
+    x, logits = synth.tokens(wl)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), "grid")

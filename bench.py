@@ -1,0 +1,322 @@
+"""Throughput of the per-expert mixed-precision MoE expert layer on one MI355X.
+
+Default workload (one JSON line): decode on the coarse MoE layer, E=8,
+d_model=4096, d_ff=14336 SwiGLU, top-2, 16 tokens per step, bit-widths from
+the exact allocator at an average of 4.5 bits/weight with Zipf(1.0)
+importance. A step is one pw_moe_forward: route, group, fused dequant +
+gate/up + SwiGLU, dequant + down, combine. Batches of 1 and 4 tokens are
+reported in "sweep".
+
+Inputs are resident in HBM before timing starts. Each step reads a
+different copy of the packed pool (several contexts over the same masters)
+so that weights come from HBM, not from the 256 MB Infinity Cache.
+
+roofline: the gate/up kernel (two thirds of the packed bytes), algorithmic
+bytes = packed W1 + W3 bytes of the experts the step routes to, divided by
+the kernel's mean duration from HIP events on the forward's stream.
+cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample.
+
+Other workloads: --workload decode_fine | prefill | dynamic | tiny.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s + achieved packed-weight HBM GB/s (% of peak), 1×MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_coarse",
+                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "tiny"])
+    ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")
+    ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, T: int):
+    """HBM bytes per gate/up launch from the committed PMC summary, or None
+    if there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_{workload}_T{T}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+class Bench:
+    def __init__(self, wl, max_tokens, npools, log):
+        import torch
+
+        import synth
+        from mixed_precision_weight_page_amd import PagedMoELayer
+        self.torch = torch
+        self.wl = wl
+        t0 = time.time()
+        self.masters = synth.expert_weights(wl, device="cuda", seed=0)
+        torch.cuda.synchronize()
+        log(f"masters on device ({time.time() - t0:.1f}s)")
+        self.layers, self.pools = [], []
+        bits = None
+        for i in range(npools):
+            layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=max_tokens,
+                                  renorm=wl.renorm, master_dtype=wl.master)
+            layer.bind_masters(*self.masters)
+            pool = layer.alloc_pool(layer.pool_bytes_for_bits([8] * wl.E))
+            layer.alloc_workspace()
+            if wl.bits is not None:
+                bits = list(wl.bits)
+                layer.quantize_experts(bits)
+            elif bits is None:
+                bits = layer.set_budget(wl.budget_bits(), synth.importance(wl)).tolist()
+            else:
+                layer.quantize_experts(bits)
+            self.layers.append(layer)
+            self.pools.append(pool)
+        torch.cuda.synchronize()
+        self.bits = bits
+        log(f"bits {bits} ({time.time() - t0:.1f}s)")
+
+    def batches(self, T, n, seed=1):
+        import synth
+        return [synth.tokens(self.wl, T=T, device="cuda", seed=seed, step=i) for i in range(n)]
+
+    def routed_bytes(self, logits):
+        """Packed bytes (W1+W3, W2) of the experts the batch routes to."""
+        _, _, counts = self.layers[0].route(logits)
+        active = (counts.cpu() > 0).nonzero().flatten().tolist()
+        wl = self.wl
+        gu = sum(2 * wl.F * wl.d * self.bits[e] // 8 for e in active)
+        dn = sum(wl.d * wl.F * self.bits[e] // 8 for e in active)
+        return gu, dn, len(active)
+
+    def run(self, T, steps, warmup, profile=True):
+        torch = self.torch
+        nb = 8
+        batches = self.batches(T, nb)
+        ys = [torch.empty((T, self.wl.d), dtype=torch.float32, device="cuda") for _ in range(nb)]
+        bytes_gu, bytes_dn, n_act = [], [], []
+        for x, lg in batches:
+            a, b, c = self.routed_bytes(lg)
+            bytes_gu.append(a)
+            bytes_dn.append(b)
+            n_act.append(c)
+        L = len(self.layers)
+        for i in range(warmup):
+            x, lg = batches[i % nb]
+            self.layers[i % L].moe_forward(x, lg, ys[i % nb])
+        torch.cuda.synchronize()
+        for layer in self.layers:
+            layer.profile(profile)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            x, lg = batches[i % nb]
+            self.layers[i % L].moe_forward(x, lg, ys[i % nb])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        prof = {"gate_up_ms": 0.0, "down_ms": 0.0, "route_ms": 0.0, "combine_ms": 0.0}
+        if profile:
+            for layer in self.layers:
+                p = layer.profile_read()
+                layer.profile(False)
+                for k in prof:
+                    prof[k] += p[k]
+        tot_gu = sum(bytes_gu[i % nb] for i in range(steps))
+        tot_dn = sum(bytes_dn[i % nb] for i in range(steps))
+        return dict(T=T, steps=steps, elapsed=elapsed, prof=prof, bytes_gu=tot_gu,
+                    bytes_dn=tot_dn, mean_active=sum(n_act[i % nb] for i in range(steps)) / steps)
+
+
+def cpu_baseline(bench, T, log):
+    """Oracle forward (float64, from the fp32 masters) on one batch."""
+    import torch
+
+    from oracle import moe
+    threads = min(16, os.cpu_count() or 1)
+    torch.set_num_threads(threads)
+    x, lg = bench.batches(T, 1, seed=99)[0]
+    x, lg = x.cpu(), lg.cpu()
+    ids, _ = moe.route(lg, bench.wl.k)
+    experts = sorted(set(ids.flatten().tolist()))
+    t0 = time.time()
+    w = [m[experts].cpu() for m in bench.masters]   # only the routed experts
+    remap = {e: i for i, e in enumerate(experts)}
+    bits = bench.bits
+    getter = moe.quantized_experts(*w, [bits[e] for e in experts])
+    t_copy = time.time() - t0
+    t0 = time.time()
+    y = moe.forward(x, lg, bench.wl.k, lambda e: getter(remap[e]))
+    dt = time.time() - t0
+    log(f"oracle forward T={T}: {dt:.1f}s (+{t_copy:.1f}s host copy), {len(experts)} experts")
+    return {"value": T / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"one {T}-token batch of the same layer: quantize the {len(experts)} routed "
+                      f"experts from fp32 masters and run the float64 forward (host copy of the "
+                      f"masters excluded)"}, y
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    wl = synth.WORKLOADS[args.workload]
+    if args.workload == "dynamic":
+        return bench_dynamic(args, wl, log)
+    T = args.tokens or wl.T
+    sweep_T = [t for t in synth.DECODE_COARSE_BATCHES if t != T] if args.workload == "decode_coarse" else []
+    max_tokens = max([T] + sweep_T)
+    npools = args.pools if args.workload != "prefill" else 2
+    b = Bench(wl, max_tokens, npools, log)
+    r = b.run(T, args.steps, args.warmup)
+    tokens_per_s = T * r["steps"] / r["elapsed"]
+    ms = 1e3 * r["elapsed"] / r["steps"]
+    gu_ms = r["prof"]["gate_up_ms"] / r["steps"]
+    dn_ms = r["prof"]["down_ms"] / r["steps"]
+    gu_gbps = r["bytes_gu"] / r["steps"] / (gu_ms * 1e-3) / 1e9 if gu_ms > 0 else None
+    fwd_gbps = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
+    traffic = traffic_from_profiles(args.workload, T)
+    if args.workload == "prefill":
+        pairs = T * wl.k
+        flops = 2.0 * pairs * 2 * wl.d * wl.F          # gate/up: 2 flops per weight per pair
+        achieved = flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
+                "kernel": "gate_up (fused dequant + W1/W3 + SwiGLU)"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": (gu_gbps or 0) / HBM_PEAK_GBPS, "traffic": traffic,
+                "kernel": "gate_up (fused dequant + W1/W3 + SwiGLU)",
+                "bytes_per_launch": r["bytes_gu"] / r["steps"],
+                "launch_ms": gu_ms}
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: E={wl.E}, d_model={wl.d}, d_ff={wl.F} SwiGLU, "
+                               f"top-{wl.k}, {T} tokens per step, "
+                               + (f"avg {wl.budget_avg} bits/weight" if wl.budget_avg else f"bits {list(wl.bits)}"),
+                   "E": wl.E, "d_model": wl.d, "d_ff": wl.F, "top_k": wl.k, "tokens": T,
+                   "bits": b.bits, "pools_rotated": npools},
+        "packed_weight_GBps": fwd_gbps,
+        "packed_weight_frac_of_hbm": fwd_gbps / HBM_PEAK_GBPS,
+        "kernels_ms_per_step": {k: v / r["steps"] for k, v in r["prof"].items()},
+        "down_GBps": r["bytes_dn"] / r["steps"] / (dn_ms * 1e-3) / 1e9 if dn_ms > 0 else None,
+        "mean_active_experts": r["mean_active"],
+        "roofline": roof,
+    }
+    if not args.no_sweep and sweep_T:
+        sw = {}
+        for t in sweep_T:
+            rs = b.run(t, args.steps, args.warmup)
+            g = rs["prof"]["gate_up_ms"] / rs["steps"]
+            sw[f"T={t}"] = {"tokens_per_s": t * rs["steps"] / rs["elapsed"],
+                            "ms_per_step": 1e3 * rs["elapsed"] / rs["steps"],
+                            "packed_weight_GBps": (rs["bytes_gu"] + rs["bytes_dn"]) / rs["elapsed"] / 1e9,
+                            "gate_up_GBps": rs["bytes_gu"] / rs["steps"] / (g * 1e-3) / 1e9 if g else None,
+                            "mean_active_experts": rs["mean_active"]}
+        out["sweep"] = sw
+    if not args.no_cpu_baseline:
+        sample_T = T if args.workload != "prefill" else 64
+        cb, _ = cpu_baseline(b, sample_T, log)
+        if args.workload == "prefill":
+            cb["sample"] += " (64 of the 4096 tokens)"
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+def bench_dynamic(args, wl, log):
+    """40 decode steps of 64 tokens; the budget moves every 8 steps through
+    avg 8, 6, 4, 3.5, 5 bits (re-quantization from the fp16 masters between
+    steps). Reports end-to-end tokens/s and the requantize rate."""
+    import torch
+
+    import synth
+    from mixed_precision_weight_page_amd import PagedMoELayer
+    masters = synth.expert_weights(wl, device="cuda")
+    layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=wl.T, master_dtype=wl.master)
+    layer.bind_masters(*masters)
+    layer.alloc_pool(layer.pool_bytes_for_bits([8] * wl.E))
+    layer.alloc_workspace()
+    p = synth.importance(wl)
+    layer.set_budget(wl.budget_bits(wl.schedule[-1]), p)   # losses measured, warm
+    steps = len(wl.schedule) * wl.steps_per_phase
+    batches = [synth.tokens(wl, device="cuda", step=i) for i in range(steps)]
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        layer.moe_forward(*batches[0], y)
+    torch.cuda.synchronize()
+    prev = None
+    req_bytes = 0
+    t0 = time.perf_counter()
+    t_req = 0.0
+    for i in range(steps):
+        if i % wl.steps_per_phase == 0:
+            ta = time.perf_counter()
+            bits = layer.set_budget(wl.budget_bits(wl.schedule[i // wl.steps_per_phase]), p)
+            torch.cuda.synchronize()
+            t_req += time.perf_counter() - ta
+            changed = [e for e in range(wl.E) if prev is None or bits[e] != prev[e]]
+            req_bytes += sum(wl.W_e * (2 + bits[e] / 8) for e in changed)
+            prev = bits
+        layer.moe_forward(*batches[i], y)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    out = {"metric": METRIC, "value": wl.T * steps / el, "unit": "tokens/s", "n_gpus": 1,
+           "steps": steps, "warmup": args.warmup, "ms_per_step": 1e3 * el / steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": "dynamic: E=128, d_model=2048, d_ff=768, top-8, 64 tokens, fp16 "
+                                  "masters, budget avg 8->6->4->3.5->5 bits every 8 steps"},
+           "requant_GBps": req_bytes / t_req / 1e9 if t_req else None,
+           "requant_s_total": t_req}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

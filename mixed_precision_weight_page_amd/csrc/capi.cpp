@@ -25,6 +25,7 @@ struct pw_ctx {
     pw_layer_desc desc{};
     int E = 0, d = 0, F = 0, k = 0;
     int64_t M = 0;        // F * d weights per matrix
+    int nsplit = 1;       // K-splits of the down product
     uint64_t We = 0;      // 3 * M weights per expert
     Layout lay{};
 
@@ -325,7 +326,7 @@ hipEvent_t next_event(pw_ctx* c) {
 }  // namespace
 
 namespace pw {
-Layout workspace_layout(int E, int d, int F, int k, int max_tokens) {
+Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) {
     Layout L{};
     const uint64_t P = (uint64_t)max_tokens * k;
     uint64_t at = 0;
@@ -344,7 +345,7 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens) {
     L.act = take(4 * (uint64_t)E);
     L.n_act = take(4);
     L.H = take(2 * P * (uint64_t)F);
-    L.O = take(4 * P * (uint64_t)d);
+    L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
     L.fwd_end = at;
     // the loss pass reuses the same memory (calls on one stream are ordered)
     const uint64_t nblk = 3 * (uint64_t)F * d / kStatChunk;
@@ -392,7 +393,8 @@ pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out) {
     c->k = d.top_k;
     c->M = (int64_t)d.d_model * d.d_ff;
     c->We = 3 * (uint64_t)c->M;
-    c->lay = workspace_layout(c->E, c->d, c->F, c->k, d.max_tokens);
+    c->nsplit = down_splits(c->F, (int64_t)d.max_tokens * d.top_k);
+    c->lay = workspace_layout(c->E, c->d, c->F, c->k, d.max_tokens, c->nsplit);
     c->table.assign(c->E, pw_page_entry{});
     *out = c;
     return PW_OK;
@@ -519,7 +521,7 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     hipStream_t s = static_cast<hipStream_t>(stream);
     const FwdWork w = fwd_work(c);
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
-    HIP_TRY(c, launch_route(ra, w, s));
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s));
     const size_t P = (size_t)T * c->k;
     HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(c, hipMemcpyAsync(g, w.g, P * 4, hipMemcpyDeviceToDevice, s));
@@ -547,7 +549,7 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         HIP_TRY(c, hipEventRecord(ev[0], s));
     }
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
-    HIP_TRY(c, launch_route(ra, w, s));
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s));
     if (c->profiling) HIP_TRY(c, hipEventRecord(ev[1], s));
     FfnArgs fa;
     fa.pool = c->pool;
@@ -558,11 +560,12 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     fa.F = c->F;
     fa.k = c->k;
     fa.max_act = std::min<int64_t>(c->E, (int64_t)T * c->k);
-    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, c->F), s));
+    fa.P = c->desc.max_tokens * c->k;
+    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s));
     if (c->profiling) HIP_TRY(c, hipEventRecord(ev[2], s));
-    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->d), s));
+    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s));
     if (c->profiling) HIP_TRY(c, hipEventRecord(ev[3], s));
-    HIP_TRY(c, launch_combine(w, T, c->d, c->k, y, s));
+    HIP_TRY(c, launch_combine(w, T, c->d, c->k, fa.P, c->nsplit, y, s));
     if (c->profiling) {
         HIP_TRY(c, hipEventRecord(ev[4], s));
         c->forwards_timed++;

@@ -2,24 +2,24 @@
 // Paging": the routed experts' pages are dequantized on the fly; Eq. 2 gives
 // the dequantized weight s_e * q). SwiGLU: h = silu(W1 x) * (W3 x), o = W2 h.
 //
-// One workgroup = one 16*WR-row tile of one active expert, all of the
-// expert's tokens. Four waves: WR along rows, WK along K (partial sums are
-// added in LDS in a fixed order). Codes stream from the page with one
-// 4B-byte load per lane per 128-code step (B = bits), prefetched PD steps
-// ahead; they are turned into exact fp16 integers q in registers
-// (magic-exponent OR, then one packed fp16 subtract) and multiplied on the
+// One workgroup = one 64-row tile of one active expert, all of the expert's
+// tokens; each of its four waves streams 16 rows over the full K. Codes
+// stream from the page with one 4B-byte load per lane per 128-code step
+// (B = bits), prefetched several steps ahead; they are masked into fp16
+// subnormals u * 2^-24 (exact) in registers and multiplied on the
 // matrix cores (v_mfma_f32_16x16x32_f16: 16 weight rows x 16 token columns,
 // K = 32), accumulating in fp32. Token rows are staged once per K chunk in
 // LDS as fp16, permuted so that each lane's 8 K-slots line up with the
-// order in which its codes unpack. The per-expert scale is applied in the
-// epilogue, so every product is exact and only fp32 accumulation rounds.
+// order in which its codes unpack. The per-expert scale, the 2^24 and the
+// code offset are applied in the epilogue, so every product is exact and
+// only fp32 accumulation rounds.
 //
 // Why matrix cores for a memory-bound skinny product: with T_e tokens per
 // expert a VALU dot product costs T_e/2 instructions per weight (packed
 // dot2), which exceeds the VALU issue budget at HBM speed (about 2.5
 // lane-instructions per 4-bit weight at 8 TB/s) as soon as T_e > 2. The
 // MFMA does the multiply-adds for up to 16 tokens at once and leaves the
-// VALU only the unpack (about 1.4 instructions per 4-bit weight).
+// VALU only the unpack (under one instruction per 4-bit weight).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -34,8 +34,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kStep = 128;   // codes per wave per step (4 K-groups x 32)
-constexpr int kPD = 4;       // steps of codes in flight per wave
-constexpr uint32_t kMagic = 0x64006400u;   // two fp16 1024.0
+constexpr float kTwo24 = 16777216.0f;      // codes enter the MFMA as u * 2^-24
 
 template <int B>
 struct Codes {
@@ -60,61 +59,35 @@ __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
     return c;
 }
 
-__device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                           _Float16 bias) {
+// Four dwords, each holding two codes u in its 16-bit halves, read as eight
+// fp16 values: a half with bits u (u < 1024, exponent field 0) is the
+// subnormal u * 2^-24, exact. The MFMA then sums u * x; the epilogue scales
+// by 2^24 and removes the offset 2^(B-1) * sum(x) of u = q + 2^(B-1).
+__device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     union {
         uint32_t u[4];
         half8_t h;
     } x;
     x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
-    return x.h - bias;   // 1024 + u - (1024 + 2^(B-1)) = q, exact in fp16
+    return x.h;
 }
 
-// The 16 fp16 pairs (each "1024 + code") of a 3-bit group of 32 codes held
-// in three dwords; pair p = (slot 2p, slot 2p+1) of the staging permutation.
+// The 16 code pairs (one code per 16-bit half) of a 3-bit group of 32 codes
+// held in three dwords; pair p = (slot 2p, slot 2p+1) of the staging
+// permutation.
 __device__ __forceinline__ void pairs3(const uint32_t* w, uint32_t p[16]) {
     const uint32_t M3 = 0x00070007u;
     const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
     const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
     const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
 #pragma unroll
-    for (int j = 0; j < 5; ++j) p[j] = ((v01 >> (3 * j)) & M3) | kMagic;          // (j, j+16)
-    p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u) |
-           kMagic;                                                                 // (5, 21)
+    for (int j = 0; j < 5; ++j) p[j] = (v01 >> (3 * j)) & M3;                                 // (j, j+16)
+    p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u);   // (5, 21)
 #pragma unroll
-    for (int j = 6; j < 10; ++j) p[j] = ((v02 >> (3 * j - 16)) & M3) | kMagic;    // (j+16, j)
-    p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u) |
-            kMagic;                                                                // (10, 26)
+    for (int j = 6; j < 10; ++j) p[j] = (v02 >> (3 * j - 16)) & M3;                           // (j+16, j)
+    p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u);    // (10, 26)
 #pragma unroll
-    for (int j = 11; j < 16; ++j) p[j] = ((v12 >> (3 * j - 32)) & M3) | kMagic;   // (j, j+16)
-}
-
-// A fragments (8 fp16 K-slots per lane) for the 4 MFMAs of one step.
-template <int B>
-__device__ __forceinline__ void unpack(const Codes<B>& c, half8_t f[4]) {
-    if constexpr (B == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = c.w[i];
-            f[i] = to_frag((w & 0x000f000fu) | kMagic, ((w >> 4) & 0x000f000fu) | kMagic,
-                           ((w >> 8) & 0x000f000fu) | kMagic, ((w >> 12) & 0x000f000fu) | kMagic,
-                           (_Float16)1032.0f);
-        }
-    } else if constexpr (B == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w0 = c.w[2 * i], w1 = c.w[2 * i + 1];
-            f[i] = to_frag((w0 & 0x00ff00ffu) | kMagic, ((w0 >> 8) & 0x00ff00ffu) | kMagic,
-                           (w1 & 0x00ff00ffu) | kMagic, ((w1 >> 8) & 0x00ff00ffu) | kMagic,
-                           (_Float16)1152.0f);
-        }
-    } else {
-        uint32_t p[16];
-        pairs3(c.w, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f[i] = to_frag(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3], (_Float16)1028.0f);
-    }
+    for (int j = 11; j < 16; ++j) p[j] = (v12 >> (3 * j - 32)) & M3;                          // (j, j+16)
 }
 
 // Code (within a 32-code group) whose activation goes to LDS slot s.
@@ -182,13 +155,88 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
     }
 }
 
-// MODE 0: gate/up + SwiGLU (NMAT = 2: W1, W3); MODE 1: down (NMAT = 1: W2).
-template <int MODE, int B, int WR, int WK>
-__device__ __forceinline__ void ffn_tile(const FfnArgs& a, const FfnPlan& pl, int e, int rt,
-                                         _Float16* xs, int* tok) {
+// Steps of codes in flight per wave: 8 x 16 B (4-bit), 8 x 12 B (3-bit),
+// 4 x 32 B (8-bit) per matrix and lane.
+template <int B>
+__device__ __forceinline__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
+
+// A fragment i (K-slots 8i..8i+7 of the lane's 32 codes) of a 4- or 8-bit step
+template <int B>
+__device__ __forceinline__ half8_t frag(const Codes<B>& c, int i) {
+    if constexpr (B == 4) {
+        const uint32_t w = c.w[i];
+        return to_frag(w & 0x000f000fu, (w >> 4) & 0x000f000fu, (w >> 8) & 0x000f000fu,
+                       (w >> 12) & 0x000f000fu);
+    } else {
+        const uint32_t w0 = c.w[2 * i], w1 = c.w[2 * i + 1];
+        return to_frag(w0 & 0x00ff00ffu, (w0 >> 8) & 0x00ff00ffu, w1 & 0x00ff00ffu,
+                       (w1 >> 8) & 0x00ff00ffu);
+    }
+}
+
+// The four MFMAs of one 128-code step for each matrix; bp points at the
+// step's 128 staged activations of this lane's token row and K-group.
+template <int B, int NMAT>
+__device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* bp,
+                                         f32x4 (&acc)[NMAT]) {
+    if constexpr (B == 3) {
+        uint32_t pr[NMAT][16];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) pairs3(cur[m].w, pr[m]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    to_frag(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]),
+                    bfr, acc[m], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag<B>(cur[m], i), bfr, acc[m], 0, 0, 0);
+        }
+    }
+}
+
+// MODE 0: gate/up + SwiGLU (NMAT = 2: W1, W3); MODE 1: down (NMAT = 1: W2),
+// over K-steps [ks0, ks0 + nsteps) (the down product may be split along K
+// across workgroups; split `sp` writes its own partial output).
+// The workgroup covers rows [64 rt, 64 rt + 64) of expert e; wave w owns 16
+// of them. Codes are prefetched PD steps ahead in a register ring; the main
+// loop issues its loads unconditionally so the ring stays full, and LDS
+// chunks of the token rows are staged before the first load when K fits.
+// Add the staged chunk's per-row sums to rsum: wave w sums rows w, w+4, ...
+// (fixed order: strided lane sums, then a butterfly), so results repeat
+// bit for bit.
+__device__ __forceinline__ void add_row_sums(const _Float16* xs, int stride, int nt, int kc,
+                                             float* rsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int n = wave; n < nt; n += kThreads / 64) {
+        const half8_t* row = reinterpret_cast<const half8_t*>(xs + n * stride);
+        float acc = 0.0f;
+        for (int i = lane; i < kc / 8; i += 64) {
+            const half8_t v = row[i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += (float)v[j];
+        }
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) rsum[n] += acc;
+    }
+}
+
+template <int MODE, int B>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e, int rt, int sp,
+                                         int ks0, int nsteps, _Float16* xs, int* tok,
+                                         float* rsum) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
+    constexpr int PD = prefetch_depth<B>();
+    constexpr int SB = kStep * B / 8;   // bytes of one step of one row
     const int K = MODE == 0 ? a.d : a.F;
-    const int rows_total = MODE == 0 ? a.F : a.d;
     const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
     const int64_t row_bytes = (int64_t)K * B / 8;
     const uint8_t* page = a.pool + a.tab.off[e];
@@ -196,85 +244,92 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, const FfnPlan& pl, in
     const int Te = a.w.cnt[e];
     const int base = a.w.off[e];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wr = wave % WR, wk = wave / WR;
     const int r = lane & 15, g = lane >> 4;
-    const int row0 = rt * 16 * WR + 16 * wr;
+    const int row0 = rt * 64 + 16 * wave;
     const uint8_t* ap[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-        ap[m] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)(row0 + r) * row_bytes + 4 * B * g;
-    const int stride = pl.kc + 8;
-    const int kcp = pl.kc / WK;
-    const int nsteps = kcp / kStep;
-    const int nchunks = K / pl.kc;
+        ap[m] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)(row0 + r) * row_bytes +
+                (int64_t)ks0 * SB + 4 * B * g;
 
     for (int tb = 0; tb < Te; tb += 16) {
         const int nt = min(16, Te - tb);
+        // steps per LDS chunk: all of them if nt rows fit, else a multiple of
+        // PD (the host sizes the LDS for at least PD steps of 16 rows)
+        int spc = nsteps;
+        if (nt * (nsteps * kStep + 8) * 2 > lds_bytes)
+            spc = ((lds_bytes / (2 * nt) - 8) / (kStep * PD)) * PD;
+        const int stride = spc * kStep + 8;
+        __syncthreads();   // previous token block done with tok, rsum and xs
+        if (threadIdx.x < 16) rsum[threadIdx.x] = 0.0f;
         if constexpr (MODE == 0) {
-            __syncthreads();
             if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
         }
+        __syncthreads();
+        stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
+        __syncthreads();
+        add_row_sums(xs, stride, nt, min(spc, nsteps) * kStep, rsum);
         f32x4 acc[NMAT];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const _Float16* bp = xs + min(r, nt - 1) * stride + 32 * g + wk * kcp;
-        for (int c = 0; c < nchunks; ++c) {
-            __syncthreads();
-            stage<MODE, B>(xs, stride, a, tok, base + tb, nt, c * pl.kc, pl.kc);
-            __syncthreads();
-            const int64_t kb = (int64_t)(c * pl.kc + wk * kcp) * B / 8;   // byte offset of the part
-            Codes<B> buf[NMAT][kPD];
+        Codes<B> buf[NMAT][PD];
 #pragma unroll
-            for (int j = 0; j < kPD; ++j)
-                if (j < nsteps)
+        for (int j = 0; j < PD; ++j)
 #pragma unroll
-                    for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + kb + j * kStep * B / 8);
-            for (int s0 = 0; s0 < nsteps; s0 += kPD) {
+            for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
+        // B-fragment row of this lane's token (columns past nt repeat a real row)
+        const _Float16* bp0 = xs + min(r, nt - 1) * stride + 32 * g;
+        int s0 = 0;
+        for (; s0 + 2 * PD <= nsteps; s0 += PD) {
+            if (s0 != 0 && s0 % spc == 0) {
+                __syncthreads();
+                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                               min(spc, nsteps - s0) * kStep);
+                __syncthreads();
+                add_row_sums(xs, stride, nt, min(spc, nsteps - s0) * kStep, rsum);
+            }
+            const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
-                for (int j = 0; j < kPD; ++j) {
-                    const int st = s0 + j;
-                    if (st < nsteps) {
-                        half8_t f[NMAT][4];
+            for (int j = 0; j < PD; ++j) {
+                Codes<B> cur[NMAT];
 #pragma unroll
-                        for (int m = 0; m < NMAT; ++m) unpack<B>(buf[m][j], f[m]);
-                        if (st + kPD < nsteps)
+                for (int m = 0; m < NMAT; ++m) {
+                    cur[m] = buf[m][j];
+                    buf[m][j] = load_codes<B>(ap[m] + (int64_t)(s0 + j + PD) * SB);
+                }
+                step_mma<B, NMAT>(cur, bp + j * kStep, acc);
+            }
+        }
+        for (; s0 < nsteps; s0 += PD) {   // last 1..2 groups: no loads past the end
+            if (s0 != 0 && s0 % spc == 0) {
+                __syncthreads();
+                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                               min(spc, nsteps - s0) * kStep);
+                __syncthreads();
+                add_row_sums(xs, stride, nt, min(spc, nsteps - s0) * kStep, rsum);
+            }
+            const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
-                            for (int m = 0; m < NMAT; ++m)
-                                buf[m][j] = load_codes<B>(ap[m] + kb + (int64_t)(st + kPD) * kStep * B / 8);
+            for (int j = 0; j < PD; ++j) {
+                const int st = s0 + j;
+                if (st < nsteps) {
+                    Codes<B> cur[NMAT];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + st * kStep + 8 * i);
-#pragma unroll
-                            for (int m = 0; m < NMAT; ++m)
-                                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[m][i], bfr, acc[m], 0, 0, 0);
-                        }
+                    for (int m = 0; m < NMAT; ++m) {
+                        cur[m] = buf[m][j];
+                        if (st + PD < nsteps) buf[m][j] = load_codes<B>(ap[m] + (int64_t)(st + PD) * SB);
                     }
+                    step_mma<B, NMAT>(cur, bp + j * kStep, acc);
                 }
             }
         }
-        if constexpr (WK > 1) {
-            // add the K-parts in LDS: parts 1..WK-1 store, part 0 adds in order
-            __syncthreads();
-            float* red = reinterpret_cast<float*>(xs);
-            if (wk > 0)
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        red[((((wk - 1) * WR + wr) * NMAT + m) * 4 + v) * 64 + lane] = acc[m][v];
-            __syncthreads();
-            if (wk == 0)
-                for (int p = 1; p < WK; ++p)
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[m][v] += red[((((p - 1) * WR + wr) * NMAT + m) * 4 + v) * 64 + lane];
-        }
-        // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n
-        if (wk == 0 && r < nt) {
+        __syncthreads();   // rsum complete
+        // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n.
+        // sum_k x q = 2^24 acc - 2^(B-1) sum_k x
+        if (r < nt) {
             const int pos = base + tb + r;
             const int orow = row0 + 4 * g;
+            const float off = (float)(1 << (B - 1)) * rsum[r];
             if constexpr (MODE == 0) {
                 union {
                     uint2 u;
@@ -282,48 +337,57 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, const FfnPlan& pl, in
                 } hv;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float av = s * acc[0][v];
-                    const float cv = s * acc[1][v];
+                    const float av = s * fmaf(acc[0][v], kTwo24, -off);
+                    const float cv = s * fmaf(acc[1][v], kTwo24, -off);
                     hv.h[v] = (_Float16)(av / (1.0f + expf(-av)) * cv);
                 }
                 *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + orow) = hv.u;
             } else {
                 float4 o;
-                o.x = s * acc[0][0]; o.y = s * acc[0][1]; o.z = s * acc[0][2]; o.w = s * acc[0][3];
-                *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + orow) = o;
+                o.x = s * fmaf(acc[0][0], kTwo24, -off);
+                o.y = s * fmaf(acc[0][1], kTwo24, -off);
+                o.z = s * fmaf(acc[0][2], kTwo24, -off);
+                o.w = s * fmaf(acc[0][3], kTwo24, -off);
+                *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + pos) * a.d + orow) = o;
             }
         }
     }
-    (void)rows_total;
 }
 
-template <int MODE, int WR, int WK>
-__global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, FfnPlan pl, int tiles_per_expert) {
+// grid: (active expert, 64-row tile, K split) flattened; experts beyond the
+// device-side active count exit at once.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     __shared__ int tok[16];
-    const int ai = blockIdx.x / tiles_per_expert;
+    __shared__ float rsum[16];
+    const int per_expert = tiles * nsplit;
+    const int ai = blockIdx.x / per_expert;
     if (ai >= a.w.n_act[0]) return;
-    const int rt = blockIdx.x - ai * tiles_per_expert;
+    const int rem = blockIdx.x - ai * per_expert;
+    const int rt = rem / nsplit, sp = rem - rt * nsplit;
     const int e = a.w.act[ai];
     const int b = a.tab.bits[e];
-    if (b == 4) ffn_tile<MODE, 4, WR, WK>(a, pl, e, rt, xs, tok);
-    else if (b == 8) ffn_tile<MODE, 8, WR, WK>(a, pl, e, rt, xs, tok);
-    else ffn_tile<MODE, 3, WR, WK>(a, pl, e, rt, xs, tok);
+    const int total = (MODE == 0 ? a.d : a.F) / kStep;
+    const int nsteps = total / nsplit;
+    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
+    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
+    else ffn_tile<MODE, 3>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
 }
 
 template <int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     const int rows = MODE == 0 ? a.F : a.d;
-    const int tpe = rows / (16 * p.wr);
-    const dim3 grid((unsigned)(a.max_act * tpe));
-    if (p.wr == 4) ffn_kernel<MODE, 4, 1><<<grid, kThreads, p.lds, s>>>(a, p, tpe);
-    else if (p.wr == 2) ffn_kernel<MODE, 2, 2><<<grid, kThreads, p.lds, s>>>(a, p, tpe);
-    else ffn_kernel<MODE, 1, 4><<<grid, kThreads, p.lds, s>>>(a, p, tpe);
+    const int tiles = rows / 64;
+    const dim3 grid((unsigned)(a.max_act * tiles * p.nsplit));
+    ffn_kernel<MODE><<<grid, kThreads, p.lds, s>>>(a, (int)p.lds, tiles, p.nsplit);
     return hipGetLastError();
 }
 
-// y[t] = sum_j g[t,j] * O[pos(t,j)] in slot order; grid (ceil(d/1024), T)
-__global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int k, float* y) {
+// y[t] = sum_j g[t,j] * (sum_s O[s][pos(t,j)]) in slot and split order;
+// grid (ceil(d/1024), T)
+__global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int k, int P, int nsplit,
+                                                           float* y) {
     const int t = blockIdx.y;
     const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (col >= d) return;
@@ -331,7 +395,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
     for (int j = 0; j < k; ++j) {
         const int p = t * k + j;
         const float gj = w.g[p];
-        const float4 o = *reinterpret_cast<const float4*>(w.O + (int64_t)w.pos[p] * d + col);
+        const float* src = w.O + (int64_t)w.pos[p] * d + col;
+        float4 o = *reinterpret_cast<const float4*>(src);
+        for (int sp = 1; sp < nsplit; ++sp) {
+            const float4 q = *reinterpret_cast<const float4*>(src + (int64_t)sp * P * d);
+            o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+        }
         acc.x = fmaf(gj, o.x, acc.x);
         acc.y = fmaf(gj, o.y, acc.y);
         acc.z = fmaf(gj, o.z, acc.z);
@@ -342,30 +411,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
 
 }  // namespace
 
-// Pick the wave split and the LDS chunk for a product with K codes, at most
-// T tokens per expert and `rows` output rows per expert.
-FfnPlan plan_ffn(int K, int T, int rows) {
+// LDS for the staged token rows: all of the K range for up to min(T, 16)
+// tokens if that fits 48 KB, else 48 KB (the kernel then stages K in chunks
+// sized by the expert's actual token count).
+FfnPlan plan_ffn(int K, int T, int nsplit) {
     FfnPlan p;
     p.nt_alloc = T < 16 ? (T < 1 ? 1 : T) : 16;
-    // few tokens: split K across the waves (more waves in flight per
-    // expert, little activation staging); many tokens: split rows
-    if (T <= 2) { p.wr = 1; p.wk = 4; }
-    else if (T <= 8) { p.wr = 2; p.wk = 2; }
-    else { p.wr = 4; p.wk = 1; }
-    while (p.wr < 4 && (K / kRowAlign) % p.wk != 0) { p.wr *= 2; p.wk /= 2; }
-    while (p.wr > 1 && rows % (16 * p.wr) != 0) { p.wr /= 2; p.wk *= 2; }
-    // chunk: the largest divisor of K (in 128-code blocks, a multiple of wk)
-    // whose fp16 rows fit the LDS budget
-    const size_t budget = 40 * 1024;
-    const int nblk = K / kRowAlign;
-    int best = p.wk;
-    for (int c = p.wk; c <= nblk; c += p.wk)
-        if (nblk % c == 0 && (size_t)p.nt_alloc * (c * kRowAlign + 8) * 2 <= budget) best = c;
-    p.kc = best * kRowAlign;
-    const size_t xs = (size_t)p.nt_alloc * (p.kc + 8) * 2;
-    const size_t red = (size_t)(p.wk - 1) * p.wr * 2 * 4 * 64 * 4;
-    p.lds = xs > red ? xs : red;
+    p.nsplit = nsplit;
+    const size_t full = (size_t)p.nt_alloc * (K / nsplit + 8) * 2;
+    const size_t cap = 48 * 1024;
+    p.lds = full < cap ? full : cap;
     return p;
+}
+
+// Small batches of a layer with a long down-projection K (large d_ff) would
+// leave most CUs idle with one workgroup per 64 output rows: split K so that
+// each workgroup streams at most 16 steps (2048 codes). Large batches keep
+// one split (the partial outputs would cost more traffic than they save).
+int down_splits(int F, int64_t max_pairs) {
+    const int nblk = F / kStep;
+    if (max_pairs > 2048) return 1;
+    for (int n = 1; n <= nblk; ++n)
+        if (nblk % n == 0 && nblk / n <= 16) return n;
+    return 1;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
@@ -375,9 +443,10 @@ hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_ffn<1>(a, p, s);
 }
 
-hipError_t launch_combine(const FwdWork& w, int T, int d, int k, float* y, hipStream_t s) {
+hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,
+                          hipStream_t s) {
     dim3 grid((unsigned)((d + 4 * kThreads - 1) / (4 * kThreads)), (unsigned)T);
-    combine_kernel<<<grid, kThreads, 0, s>>>(w, d, k, y);
+    combine_kernel<<<grid, kThreads, 0, s>>>(w, d, k, P, nsplit, y);
     return hipGetLastError();
 }
 

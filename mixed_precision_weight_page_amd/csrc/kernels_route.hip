@@ -2,14 +2,16 @@
 // router determines which experts each token needs, and those experts'
 // pages are fetched through the page table).
 //
-//   route_kernel     one wave per token: top-k of the logits (equal values ->
-//                    lower expert index), softmax weights g.
-//   rank_kernel      one block per expert: stable rank of its (token, slot)
-//                    pairs in token order (block-wide scan), and its count.
-//   finalize_kernel  one block: expert offsets (exclusive scan), the list of
-//                    active experts, and the expert-sorted pair order.
-// No host synchronisation: every later kernel reads the counts from device
-// memory and its grid is sized for the worst case.
+// Per token: the k largest logits (equal values -> lower expert index) and
+// softmax weights g. Then a stable counting sort of the (token, slot) pairs
+// by expert: rank of a pair = number of earlier tokens routed to the same
+// expert; offsets = exclusive prefix of the per-expert counts. The list of
+// active experts is ordered 8-bit pages first, then 4-bit, then 3-bit (each
+// by expert id), so the longest tiles are dispatched first.
+//
+// Small batches (T <= kFusedMaxT) run everything in one workgroup; larger
+// ones use three kernels (route, per-expert rank, finalize). No host
+// synchronisation: later kernels read the counts from device memory.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -20,28 +22,27 @@ namespace pw {
 namespace {
 
 constexpr int kMaxPerLane = kMaxExperts / 64;  // 16 logits per lane
+constexpr int kBlock = 1024;
+constexpr int kWaves = kBlock / 64;
 
 __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
     return v > v2 || (v == v2 && e < e2);
 }
 
-// grid ceil(T / 4), 256 threads: wave w of block b handles token 4b + w.
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+// One wave routes token t: writes ids/g (and the ids to s_ids if given).
+__device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t,
+                                            int* s_ids) {
     const int lane = threadIdx.x & 63;
-    if (t >= a.T) return;
     const float* row = a.logits + (int64_t)t * a.E;
-    float v[kMaxPerLane];
     const int per = (a.E + 63) / 64;
+    float v[kMaxPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + 64 * i;
         v[i] = (i < per && e < a.E) ? row[e] : -INFINITY;
     }
-    // full softmax denominator needs the max and the values before masking
-    float my_id = 0.0f;   // this lane keeps slot j == lane
-    float my_val = -INFINITY;
-    float top = -INFINITY;
+    int my_id = 0;
+    float my_val = -INFINITY, top = -INFINITY;
     uint32_t taken = 0;   // bit i: v[i] already chosen
     for (int j = 0; j < a.k; ++j) {
         float bv = -INFINITY;
@@ -61,9 +62,8 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
         }
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (j == 0) top = bv;
-        if (lane == j) { my_id = (float)be; my_val = bv; }
+        if (lane == j) { my_id = be; my_val = bv; }
     }
-    // softmax over all experts (or over the chosen k when renormalising)
     float sum_all = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
@@ -74,9 +74,114 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
     float den = a.renorm ? mine : sum_all;
     for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
     if (lane < a.k) {
-        w.ids[(int64_t)t * a.k + lane] = (int)my_id;
+        w.ids[(int64_t)t * a.k + lane] = my_id;
         w.g[(int64_t)t * a.k + lane] = mine / den;
+        if (s_ids) s_ids[t * a.k + lane] = my_id;
     }
+}
+
+// Inclusive scan over the 1024 threads of the block (every thread calls it).
+template <typename T>
+__device__ __forceinline__ T block_scan(T v, T* s_wave, T* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+        const T n = __shfl_up(v, o);
+        if (lane >= o) v += n;
+    }
+    __syncthreads();
+    if (lane == 63) s_wave[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        T x = lane < kWaves ? s_wave[lane] : T(0);
+        for (int o = 1; o < kWaves; o <<= 1) {
+            const T n = __shfl_up(x, o);
+            if (lane >= o) x += n;
+        }
+        if (lane < kWaves) s_wave[lane] = x;
+    }
+    __syncthreads();
+    *total = s_wave[kWaves - 1];
+    return v + (wave > 0 ? s_wave[wave - 1] : T(0));
+}
+
+// Offsets, bit-ordered active list, and pair positions. cnt_of(e) gives the
+// count of expert e, rank_of(p) the rank of pair p.
+template <class CntF, class RankF, class IdF>
+__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, const int32_t* bits,
+                                         CntF cnt_of, RankF rank_of, IdF id_of) {
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_wave_i[kWaves];
+    __shared__ long long s_wave_l[kWaves];
+    const int tid = threadIdx.x;
+    const int c = tid < E ? cnt_of(tid) : 0;
+    int tot;
+    const int inc = block_scan<int>(c, s_wave_i, &tot);
+    if (tid < E) {
+        s_off[tid] = inc - c;
+        w.off[tid] = inc - c;
+    }
+    if (tid == 0) w.off[E] = tot;
+    // classes: 0 = 8-bit, 1 = 4-bit, 2 = 3-bit; 21-bit counters per class
+    const int b = tid < E ? bits[tid] : 0;
+    const int cls = b == 8 ? 0 : (b == 4 ? 1 : 2);
+    const long long flag = (tid < E && c > 0) ? (1ll << (21 * cls)) : 0ll;
+    long long ltot;
+    const long long linc = block_scan<long long>(flag, s_wave_l, &ltot);
+    const int n8 = (int)(ltot & 0x1fffff), n4 = (int)((ltot >> 21) & 0x1fffff),
+              n3 = (int)((ltot >> 42) & 0x1fffff);
+    if (flag) {
+        const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
+        const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
+        w.act[base + before] = tid;
+    }
+    if (tid == 0) w.n_act[0] = n8 + n4 + n3;
+    __syncthreads();
+    const int P = T * k;
+    for (int p = tid; p < P; p += kBlock) {
+        const int e = id_of(p);
+        const int pos = s_off[e] + rank_of(p);
+        w.pos[p] = pos;
+        w.sorted[pos] = p;
+    }
+}
+
+// ---- small batches: one workgroup ----
+__global__ __launch_bounds__(kBlock) void route_small_kernel(RouteArgs a, FwdWork w,
+                                                             const int32_t* bits) {
+    __shared__ int s_ids[kFusedMaxPairs];
+    __shared__ int s_rank[kFusedMaxPairs];
+    __shared__ int s_cnt[kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < a.T; t += kWaves) route_token(a, w, t, s_ids);
+    __syncthreads();
+    // stable rank: wave handles experts wave, wave + 16, ...; lanes = tokens
+    for (int e = wave; e < a.E; e += kWaves) {
+        int running = 0;
+        for (int t0 = 0; t0 < a.T; t0 += 64) {
+            const int t = t0 + lane;
+            int slot = -1;
+            if (t < a.T)
+                for (int j = 0; j < a.k; ++j)
+                    if (s_ids[t * a.k + j] == e) slot = j;
+            const uint64_t m = __ballot(slot >= 0);
+            if (slot >= 0) s_rank[t * a.k + slot] = running + __popcll(m & ((1ull << lane) - 1ull));
+            running += __popcll(m);
+        }
+        if (lane == 0) {
+            s_cnt[e] = running;
+            w.cnt[e] = running;
+        }
+    }
+    __syncthreads();
+    finalize(a.T, a.E, a.k, w, bits, [&](int e) { return s_cnt[e]; },
+             [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
+}
+
+// ---- large batches: route, rank, finalize ----
+// grid ceil(T / 4), 256 threads: wave w of block b handles token 4b + w.
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < a.T) route_token(a, w, t, nullptr);
 }
 
 // grid E, 256 threads: rank of expert e's pairs in token order.
@@ -104,52 +209,26 @@ __global__ __launch_bounds__(256) void rank_kernel(int T, int k, FwdWork w) {
     if (threadIdx.x == 0) w.cnt[e] = running;
 }
 
-// one block of 1024 threads
-__global__ __launch_bounds__(1024) void finalize_kernel(int T, int E, int k, FwdWork w) {
-    __shared__ int sc[kMaxExperts];
-    __shared__ int sa[kMaxExperts];
-    const int tid = threadIdx.x;
-    const int c = tid < E ? w.cnt[tid] : 0;
-    sc[tid] = c;
-    sa[tid] = (tid < E && c > 0) ? 1 : 0;
-    __syncthreads();
-    // Hillis-Steele inclusive scans of counts and of the active flags
-    for (int o = 1; o < kMaxExperts; o <<= 1) {
-        const int x = tid >= o ? sc[tid - o] : 0;
-        const int y = tid >= o ? sa[tid - o] : 0;
-        __syncthreads();
-        sc[tid] += x;
-        sa[tid] += y;
-        __syncthreads();
-    }
-    if (tid < E) {
-        w.off[tid] = sc[tid] - c;
-        if (c > 0) w.act[sa[tid] - 1] = tid;
-    }
-    if (tid == 0) {
-        w.off[E] = sc[E - 1];
-        w.n_act[0] = sa[E - 1];
-    }
-    __syncthreads();
-    const int P = T * k;
-    for (int p = tid; p < P; p += 1024) {
-        const int e = w.ids[p];
-        const int pos = (sc[e] - w.cnt[e]) + w.rank[p];
-        w.pos[p] = pos;
-        w.sorted[pos] = p;
-    }
+__global__ __launch_bounds__(kBlock) void finalize_kernel(int T, int E, int k, FwdWork w,
+                                                          const int32_t* bits) {
+    finalize(T, E, k, w, bits, [&](int e) { return w.cnt[e]; },
+             [&](int p) { return w.rank[p]; }, [&](int p) { return w.ids[p]; });
 }
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, hipStream_t s) {
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s) {
+    if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxPairs) {
+        route_small_kernel<<<1, kBlock, 0, s>>>(a, w, bits);
+        return hipGetLastError();
+    }
     route_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a, w);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     rank_kernel<<<a.E, 256, 0, s>>>(a.T, a.k, w);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    finalize_kernel<<<1, 1024, 0, s>>>(a.T, a.E, a.k, w);
+    finalize_kernel<<<1, kBlock, 0, s>>>(a.T, a.E, a.k, w, bits);
     return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ constexpr int kMaxTopK = 32;
 constexpr int kRowAlign = 128;         // codes per row are a multiple of this
 constexpr int kPageAlign = 256;        // page offsets and sizes
 constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
+constexpr int kFusedMaxT = 256;        // batches routed by a single workgroup
+constexpr int kFusedMaxPairs = 4096;
 
 // supported bit-widths, in loss-table order
 __host__ __device__ constexpr int bits_of_index(int i) { return i == 0 ? 3 : i == 1 ? 4 : 8; }
@@ -41,7 +43,7 @@ struct FwdWork {
     int32_t* act;      // [E] experts with cnt > 0, ascending
     int32_t* n_act;    // [1]
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
-    float* O;          // [P, d] down-projection output per sorted pair (scaled by s_e)
+    float* O;          // [nsplit, P, d] down-projection partials per sorted pair (scaled by s_e)
 };
 
 struct Layout {
@@ -50,7 +52,7 @@ struct Layout {
     uint64_t total;
 };
 
-Layout workspace_layout(int E, int d, int F, int k, int max_tokens);
+Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit);
 
 // ---- launchers (kernels_*.hip) ----
 hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16, int E,
@@ -66,15 +68,16 @@ struct RouteArgs {
     const float* logits;
     int T, E, k, renorm;
 };
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s);
 
 struct FfnPlan {
-    int wr, wk;       // waves along rows x waves along K (wr * wk = 4)
-    int kc;           // K codes staged in LDS per chunk
-    int nt_alloc;     // token rows staged in LDS
+    int nt_alloc;     // token rows the LDS is sized for
+    int nsplit;       // workgroups along K (down product only)
     size_t lds;       // dynamic LDS bytes
 };
-FfnPlan plan_ffn(int K, int T, int rows);
+FfnPlan plan_ffn(int K, int T, int nsplit);
+// K-splits of the down product for a layer (partials summed by the combine)
+int down_splits(int F, int64_t max_pairs);
 
 struct FfnArgs {
     const uint8_t* pool;
@@ -82,10 +85,12 @@ struct FfnArgs {
     FwdWork w;
     const uint16_t* x;   // bf16 [T, d]
     int d, F, k, max_act;
+    int P;               // pair stride of the split partial outputs O[split][P][d]
 };
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
-hipError_t launch_combine(const FwdWork& w, int T, int d, int k, float* y, hipStream_t s);
+hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,
+                          hipStream_t s);
 
 // ---- host allocator (alloc.cpp) ----
 pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,

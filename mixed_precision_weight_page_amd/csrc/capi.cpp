@@ -290,7 +290,7 @@ pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s) {
                               hipMemcpyHostToDevice, s));
     HIP_TRY(c, hipEventRecord(c->upload_done, s));
     const int f16 = c->desc.master_dtype == PW_MASTER_F16;
-    HIP_TRY(c, launch_pack(c->w1, c->w3, c->w2, f16, c->M, dev_table(c, next), dev_list(c, next),
+    HIP_TRY(c, launch_pack(c->w1, c->w3, c->w2, f16, c->d, c->F, dev_table(c, next), dev_list(c, next),
                            (int)list.size(), c->pool, s));
     c->table = nt;
     c->cur = next;

@@ -2,9 +2,10 @@
 // Paging": the routed experts' pages are dequantized on the fly; Eq. 2 gives
 // the dequantized weight s_e * q). SwiGLU: h = silu(W1 x) * (W3 x), o = W2 h.
 //
-// One workgroup = one 64-row tile of one active expert, all of the expert's
-// tokens; each of its four waves streams 16 rows over the full K. Codes
-// stream from the page with one 4B-byte load per lane per 128-code step
+// One workgroup = 64 rows of one active expert, all of the expert's tokens;
+// each of its four waves streams one 16-row block, whose tiles (16 rows x
+// 128 codes) are contiguous in the page, so every load instruction of a
+// wave reads one contiguous run. One 4B-byte load per lane per tile
 // (B = bits), prefetched several steps ahead; they are masked into fp16
 // subnormals u * 2^-24 (exact) in registers and multiplied on the
 // matrix cores (v_mfma_f32_16x16x32_f16: 16 weight rows x 16 token columns,
@@ -41,20 +42,35 @@ struct Codes {
     uint32_t w[B];   // 32 consecutive codes of one row, LSB-first
 };
 
+// byte offset of lane l's run inside a 16-row x 128-code tile (the 8-bit
+// run's second half lies 1024 bytes further)
+template <int B>
+__device__ __forceinline__ constexpr int lane_offset(int l) { return (B == 3 ? 12 : 16) * l; }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Codes are read once per forward: non-temporal loads keep them from
+// displacing the activations and partial outputs in the caches.
+__device__ __forceinline__ u32x4 stream_load16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <int B>
 __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
     Codes<B> c;
     if constexpr (B == 4) {
-        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const u32x4 u = stream_load16(p);
         c.w[0] = u.x; c.w[1] = u.y; c.w[2] = u.z; c.w[3] = u.w;
     } else if constexpr (B == 8) {
-        const uint4 u = *reinterpret_cast<const uint4*>(p);
-        const uint4 v = *reinterpret_cast<const uint4*>(p + 16);
+        const u32x4 u = stream_load16(p);
+        const u32x4 v = stream_load16(p + 1024);
         c.w[0] = u.x; c.w[1] = u.y; c.w[2] = u.z; c.w[3] = u.w;
         c.w[4] = v.x; c.w[5] = v.y; c.w[6] = v.z; c.w[7] = v.w;
     } else {
         const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-        c.w[0] = q[0]; c.w[1] = q[1]; c.w[2] = q[2];
+        c.w[0] = __builtin_nontemporal_load(q);
+        c.w[1] = __builtin_nontemporal_load(q + 1);
+        c.w[2] = __builtin_nontemporal_load(q + 2);
     }
     return c;
 }
@@ -235,10 +251,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                                          float* rsum) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
     constexpr int PD = prefetch_depth<B>();
-    constexpr int SB = kStep * B / 8;   // bytes of one step of one row
+    constexpr int SB = 16 * kStep * B / 8;   // bytes of one tile: 16 rows x 128 codes
     const int K = MODE == 0 ? a.d : a.F;
     const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
-    const int64_t row_bytes = (int64_t)K * B / 8;
     const uint8_t* page = a.pool + a.tab.off[e];
     const float s = a.tab.scale[e];
     const int Te = a.w.cnt[e];
@@ -246,11 +261,12 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
+    // this wave's 16-row block is one contiguous run of K/128 tiles
     const uint8_t* ap[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-        ap[m] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)(row0 + r) * row_bytes +
-                (int64_t)ks0 * SB + 4 * B * g;
+        ap[m] = page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * (K / kStep) + ks0) * SB +
+                lane_offset<B>(lane);
 
     for (int tb = 0; tb < Te; tb += 16) {
         const int nt = min(16, Te - tb);
@@ -266,17 +282,19 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
             if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
         }
         __syncthreads();
+        // first codes in flight before the token rows are staged, so the
+        // staging's wait overlaps their latency
+        Codes<B> buf[NMAT][PD];
+#pragma unroll
+        for (int j = 0; j < PD; ++j)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
         stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
         __syncthreads();
         add_row_sums(xs, stride, nt, min(spc, nsteps) * kStep, rsum);
         f32x4 acc[NMAT];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Codes<B> buf[NMAT][PD];
-#pragma unroll
-        for (int j = 0; j < PD; ++j)
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
         // B-fragment row of this lane's token (columns past nt repeat a real row)
         const _Float16* bp0 = xs + min(r, nt - 1) * stride + 32 * g;
         int s0 = 0;

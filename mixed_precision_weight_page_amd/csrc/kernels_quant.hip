@@ -3,9 +3,12 @@
 // and the pack of codes into the expert's page.
 //
 // Weight space of expert e: its W1 block (M = F*d weights), then W3, then W2,
-// each row-major. Because every row holds a multiple of 128 codes, the page
-// of an expert is exactly the LSB-first bitstream of the 3*M codes u = q +
-// 2^(b-1) in that order: code i occupies bits [b*i, b*i + b) of the page.
+// each row-major. A page holds the codes u = q + 2^(b-1) of W1, W3, W2, each
+// matrix in tiles of 16 rows x 128 codes: tiles in (row block, K step)
+// order; in a tile, lane l = 16 g + r holds the LSB-first run of codes
+// 32g..32g+31 of row r (4b bytes), split into pieces of at most 16 bytes,
+// piece p of all 64 lanes stored together. A wave of the forward kernels
+// then reads each tile as contiguous 16-byte (12-byte) lane loads.
 #include <hip/hip_runtime.h>
 
 #include "pw_internal.h"
@@ -175,59 +178,68 @@ __global__ __launch_bounds__(kThreads) void loss_final_kernel(const double* part
     }
 }
 
-// One wave turns 256 consecutive weights into 8*B packed dwords: lane l
-// quantizes weights 4l..4l+3 into a 4B-bit chunk, then lane j < 8B gathers
-// the chunks that overlap bits [32j, 32j+32) of the wave's bitstream.
+// One wave packs one tile of 16 rows x 128 codes. Lane l = 16 g + r
+// quantizes codes 32g..32g+31 of row r into a 32B-bit LSB-first run and
+// stores it in the tile: 4-bit 16 bytes at 16 l; 8-bit 16 bytes at 16 l and
+// 16 bytes at 1024 + 16 l; 3-bit 12 bytes at 12 l.
 template <int B>
-__device__ __forceinline__ void pack_wave(const void* base, int64_t idx, int f16, float s,
-                                          uint32_t* out) {
+__device__ __forceinline__ void pack_lane(const void* base, int64_t src, int f16, float s,
+                                          uint8_t* tile) {
     const int lane = threadIdx.x & 63;
-    float v[4];
-    load4(base, idx + 4 * lane, f16, v);
     const float qm = (float)qmax_of(B);
-    uint32_t chunk = 0;
+    uint32_t w[B];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = (int)code_of(v[j], s, qm);
-        chunk |= (uint32_t)(q + (1 << (B - 1))) << (B * j);
-    }
-    constexpr int CB = 4 * B;                 // chunk bits
-    const int j = lane;                       // output dword of this lane
-    const int l0 = (32 * j) / CB;             // first chunk overlapping it
-    uint32_t word = 0;
+    for (int i = 0; i < B; ++i) w[i] = 0;
 #pragma unroll
-    for (int i = 0; i < (32 + CB - 1) / CB + 1; ++i) {
-        const int l = min(l0 + i, 63);
-        const uint32_t c = (uint32_t)__shfl((int)chunk, l);
-        const int shift = CB * (l0 + i) - 32 * j;   // chunk start relative to the dword
-        if (l0 + i < 64 && shift < 32 && shift > -CB)
-            word |= shift >= 0 ? (c << shift) : (c >> (-shift));
+    for (int i = 0; i < 8; ++i) {
+        float v[4];
+        load4(base, src + 4 * i, f16, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t u = (uint32_t)((int)code_of(v[j], s, qm) + (1 << (B - 1)));
+            const int bit = B * (4 * i + j);          // compile-time after unrolling
+            w[bit / 32] |= u << (bit % 32);
+            if (bit % 32 + B > 32) w[bit / 32 + 1] |= u >> (32 - bit % 32);
+        }
     }
-    if (j < 8 * B) out[j] = word;
+    if constexpr (B == 4) {
+        *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (B == 8) {
+        *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(tile + 1024 + 16 * lane) = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+        uint32_t* o = reinterpret_cast<uint32_t*>(tile + 12 * lane);
+        o[0] = w[0]; o[1] = w[1]; o[2] = w[2];
+    }
 }
 
-// grid (3*M / kStatChunk, nlist): pack the listed experts into their pages.
+// grid (3*M / 8192, nlist), 4 waves: wave w of block x packs tile 4x + w of
+// the listed expert (tiles of W1, then W3, then W2; in each matrix in
+// (16-row block, 128-code step) order).
 __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const void* w3,
-                                                        const void* w2, int f16, int64_t M,
+                                                        const void* w2, int f16, int d, int F,
                                                         DevTable tab, const int32_t* list,
                                                         uint8_t* pool) {
     const int e = list[blockIdx.y];
     const int b = tab.bits[e];
     const float s = tab.scale[e];
-    const int64_t start = (int64_t)blockIdx.x * kStatChunk;
-    const int mtx = (int)(start / M);
+    const int64_t M = (int64_t)F * d;
+    const int64_t tpm = M / 2048;                         // tiles per matrix
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int mtx = (int)(t / tpm);
+    const int64_t tt = t - mtx * tpm;
+    const int K = mtx == 2 ? F : d;
+    const int steps = K / 128;
+    const int64_t rb = tt / steps;
+    const int st = (int)(tt - rb * steps);
+    const int lane = threadIdx.x & 63;
+    const int64_t row = rb * 16 + (lane & 15);
+    const int64_t src = (int64_t)e * M + row * K + st * 128 + 32 * (lane >> 4);
     const void* base = matrix_base(w1, w3, w2, mtx);
-    const int64_t src = (int64_t)e * M + (start - (int64_t)mtx * M);
-    uint8_t* page = pool + tab.off[e];
-    const int wave = threadIdx.x >> 6;
-    for (int it = wave; it < kStatChunk / 256; it += kThreads / 64) {
-        const int64_t code0 = start + (int64_t)it * 256;       // index in the expert's 3M codes
-        uint32_t* out = reinterpret_cast<uint32_t*>(page + code0 * b / 8);
-        const int64_t idx = src + (int64_t)it * 256;
-        if (b == 3) pack_wave<3>(base, idx, f16, s, out);
-        else if (b == 4) pack_wave<4>(base, idx, f16, s, out);
-        else pack_wave<8>(base, idx, f16, s, out);
-    }
+    uint8_t* tile = pool + tab.off[e] + mtx * (M * b / 8) + tt * (256 * b);
+    if (b == 3) pack_lane<3>(base, src, f16, s, tile);
+    else if (b == 4) pack_lane<4>(base, src, f16, s, tile);
+    else pack_lane<8>(base, src, f16, s, tile);
 }
 
 }  // namespace
@@ -250,12 +262,13 @@ hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, 
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int64_t M,
+hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int d, int F,
                        DevTable tab, const int32_t* list, int nlist, uint8_t* pool,
                        hipStream_t s) {
     if (nlist == 0) return hipSuccess;
-    dim3 grid((unsigned)(3 * M / kStatChunk), (unsigned)nlist);
-    pack_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, M, tab, list, pool);
+    const int64_t M = (int64_t)F * d;
+    dim3 grid((unsigned)(3 * M / 8192), (unsigned)nlist);
+    pack_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, d, F, tab, list, pool);
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16
 hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, int E,
                        int64_t M, const uint32_t* absmax, double* partial, double* loss,
                        hipStream_t s);
-hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int64_t M,
+hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int d, int F,
                        DevTable tab, const int32_t* list, int nlist, uint8_t* pool,
                        hipStream_t s);
 

@@ -85,17 +85,33 @@ def check_pages(layer, pool: torch.Tensor, masters, bits, experts=None, rows_per
             off = 0
             for mat in (w1[e], w3[e], w2[e]):
                 rows, K = mat.shape
-                rb = K * b // 8
+                nb = rows * K * b // 8
                 for r in rng.choice(rows, size=min(rows, rows_per_matrix), replace=False):
                     want = quant.pack_rows(quant.stored(quant.codes(mat[r:r + 1], s, b), b), b)[0]
-                    got = page[off + r * rb: off + (r + 1) * rb]
+                    got = torch.tensor(list(tiled_row(page[off:off + nb], K, b, int(r))), dtype=torch.uint8)
                     assert torch.equal(got, want), (e, b, int(r))
-                off += rows * rb
+                off += nb
     # placement invariants: aligned, inside the pool, no overlap
     spans = sorted((t["offset"], t["offset"] + t["nbytes"]) for t in table)
     for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
         assert a1 <= b0
     assert spans[-1][1] <= pool.numel()
+
+
+def tiled_row(matrix: torch.Tensor, K: int, b: int, r: int) -> bytes:
+    """Bytes of row r's bitstream read back from a tiled matrix (tile =
+    16 rows x 128 codes; lane 16 g + r holds codes 32g..32g+31 of row r in
+    pieces of min(16, 4b) bytes, piece p of all 64 lanes together)."""
+    steps = K // 128
+    piece = min(16, 4 * b)
+    idx = []
+    for s in range(steps):
+        tile = ((r // 16) * steps + s) * (16 * 128 * b // 8)
+        for g in range(4):
+            for p in range(4 * b // piece):
+                at = tile + p * 64 * piece + (16 * g + r % 16) * piece
+                idx.extend(range(at, at + piece))
+    return bytes(matrix[torch.tensor(idx)].tolist())
 
 
 def oracle_bits(wl, masters, B, L=None):

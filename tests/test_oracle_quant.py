@@ -156,6 +156,33 @@ def test_pack_against_bigint_unpacker(b, K):
     assert torch.equal(quant.unpack_rows(packed, b, K), u)
 
 
+def tiled_row(matrix_bytes: bytes, rows: int, K: int, b: int, r: int) -> bytes:
+    """Independent address formula of the tile layout: gather row r's
+    bitstream back, piece by piece."""
+    steps = K // 128
+    lane_bytes = 4 * b
+    piece = min(16, lane_bytes)
+    out = bytearray()
+    for s in range(steps):
+        tile = ((r // 16) * steps + s) * (16 * 128 * b // 8)
+        for g in range(4):
+            for p in range(lane_bytes // piece):
+                at = tile + p * 64 * piece + (16 * g + r % 16) * piece
+                out += matrix_bytes[at:at + piece]
+    return bytes(out)
+
+
+@pytest.mark.parametrize("b", quant.BITS)
+def test_tile_layout_against_address_formula(b):
+    rows, K = 48, 384
+    g = torch.Generator().manual_seed(40 + b)
+    u = torch.randint(0, 2 ** b, (rows, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    tiled = bytes(quant.tile_matrix(quant.pack_rows(u, b), b).tolist())
+    assert len(tiled) == rows * K * b // 8
+    for r in range(rows):
+        assert bigint_unpack(tiled_row(tiled, rows, K, b, r), b, K) == u[r].tolist(), r
+
+
 def test_page_layout_and_size():
     E, d, F = 1, 128, 256
     g = torch.Generator().manual_seed(5)
@@ -171,18 +198,17 @@ def test_page_layout_and_size():
         assert page.numel() == 3 * d * F * b // 8       # 128-multiples: no padding
         pb = bytes(page.tolist())
         # W3 block starts after the F rows of W1; W2 after both
-        row_w1 = d * b // 8
-        row_w2 = F * b // 8
-        r = 17
-        q3 = bigint_unpack(pb[F * row_w1 + r * row_w1: F * row_w1 + (r + 1) * row_w1], b, d)
-        want3 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
-                 for v in w3[r].tolist()]
-        assert q3 == want3
-        off2 = 2 * F * row_w1
-        q2 = bigint_unpack(pb[off2 + r * row_w2: off2 + (r + 1) * row_w2], b, F)
-        want2 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
-                 for v in w2[r].tolist()]
-        assert q2 == want2
+        m1 = F * d * b // 8
+        for r in (0, 17, F - 1):
+            q3 = bigint_unpack(tiled_row(pb[m1:2 * m1], F, d, b, r), b, d)
+            want3 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
+                     for v in w3[r].tolist()]
+            assert q3 == want3
+        for r in (0, 17, d - 1):
+            q2 = bigint_unpack(tiled_row(pb[2 * m1:], d, F, b, r), b, F)
+            want2 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
+                     for v in w2[r].tolist()]
+            assert q2 == want2
 
 
 def test_loss_closed_forms():

@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without the per-kernel events (no roofline)")
     return ap.parse_args()
 
 
@@ -119,7 +121,7 @@ class Bench:
         dn = sum(wl.d * wl.F * self.bits[e] // 8 for e in active)
         return gu, dn, len(active)
 
-    def run(self, T, steps, warmup, profile=True):
+    def run(self, T, steps, warmup, profile=2):
         torch = self.torch
         nb = 8
         batches = self.batches(T, nb)
@@ -147,7 +149,7 @@ class Bench:
         if profile:
             for layer in self.layers:
                 p = layer.profile_read()
-                layer.profile(False)
+                layer.profile(0)
                 for k in prof:
                     prof[k] += p[k]
         tot_gu = sum(bytes_gu[i % nb] for i in range(steps))
@@ -204,11 +206,13 @@ def main():
     max_tokens = max([T] + sweep_T)
     npools = args.pools if args.workload != "prefill" else 2
     b = Bench(wl, max_tokens, npools, log)
-    r = b.run(T, args.steps, args.warmup)
+    # timed region: events only on the gate/up kernel (the roofline kernel);
+    # a second pass of the same steps times every kernel for the breakdown
+    r = b.run(T, args.steps, args.warmup, profile=0 if args.no_profile else 2)
+    r_all = b.run(T, args.steps, 0, profile=15) if not args.no_profile else None
     tokens_per_s = T * r["steps"] / r["elapsed"]
     ms = 1e3 * r["elapsed"] / r["steps"]
     gu_ms = r["prof"]["gate_up_ms"] / r["steps"]
-    dn_ms = r["prof"]["down_ms"] / r["steps"]
     gu_gbps = r["bytes_gu"] / r["steps"] / (gu_ms * 1e-3) / 1e9 if gu_ms > 0 else None
     fwd_gbps = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
     traffic = traffic_from_profiles(args.workload, T)
@@ -245,15 +249,17 @@ def main():
                    "bits": b.bits, "pools_rotated": npools},
         "packed_weight_GBps": fwd_gbps,
         "packed_weight_frac_of_hbm": fwd_gbps / HBM_PEAK_GBPS,
-        "kernels_ms_per_step": {k: v / r["steps"] for k, v in r["prof"].items()},
-        "down_GBps": r["bytes_dn"] / r["steps"] / (dn_ms * 1e-3) / 1e9 if dn_ms > 0 else None,
+        "kernels_ms_per_step": ({k: v / r_all["steps"] for k, v in r_all["prof"].items()}
+                                if r_all else None),
+        "down_GBps": (r_all["bytes_dn"] / r_all["steps"] / (r_all["prof"]["down_ms"] / r_all["steps"] * 1e-3) / 1e9
+                      if r_all and r_all["prof"]["down_ms"] > 0 else None),
         "mean_active_experts": r["mean_active"],
         "roofline": roof,
     }
     if not args.no_sweep and sweep_T:
         sw = {}
         for t in sweep_T:
-            rs = b.run(t, args.steps, args.warmup)
+            rs = b.run(t, args.steps, args.warmup, profile=0 if args.no_profile else 2)
             g = rs["prof"]["gate_up_ms"] / rs["steps"]
             sw[f"T={t}"] = {"tokens_per_s": t * rs["steps"] / rs["elapsed"],
                             "ms_per_step": 1e3 * rs["elapsed"] / rs["steps"],

@@ -155,10 +155,13 @@ pw_status pw_get_loss_table(pw_ctx* ctx, double* out, void* stream);
 pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, const double* L,
                               uint64_t budget_bits, uint8_t* bits_out);
 
-/* Timing of the forward kernels with HIP events on the forward's stream.
- * enable = 1 starts (and clears) collection, 0 stops it. pw_profile_read
- * waits for the recorded events and returns the sums. */
-pw_status pw_profile(pw_ctx* ctx, int32_t enable);
+/* Timing of the forward kernels on the forward's stream: each timed kernel
+ * is launched with start/stop HIP events stamped by its own dispatch
+ * (hipExtLaunchKernel). mask selects the kernels: bit 0 router/grouping,
+ * bit 1 gate/up, bit 2 down, bit 3 combine; a nonzero mask starts (and
+ * clears) collection, 0 stops it. pw_profile_read waits for the recorded
+ * events and returns the per-class sums over the timed forwards. */
+pw_status pw_profile(pw_ctx* ctx, int32_t mask);
 pw_status pw_profile_read(pw_ctx* ctx, pw_profile_data* out);
 
 const char* pw_last_error(const pw_ctx* ctx);

@@ -56,8 +56,9 @@ struct pw_ctx {
     int cur = 0;                // active device table
 
     // profiling
-    bool profiling = false;
+    int profile_mask = 0;      // bit 0 route, 1 gate/up, 2 down, 3 combine
     std::vector<hipEvent_t> ev_pool;
+    std::vector<int> ev_kind;   // kernel class of each (start, stop) pair in use
     size_t ev_used = 0;
     int64_t forwards_timed = 0;
 
@@ -542,15 +543,18 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const FwdWork w = fwd_work(c);
-    hipEvent_t ev[5] = {};
-    if (c->profiling) {
-        for (auto& e : ev)
-            if (!(e = next_event(c))) return fail(c, PW_ERR_HIP, "hipEventCreate failed");
-        HIP_TRY(c, hipEventRecord(ev[0], s));
+    KTimer tm[4];
+    if (c->profile_mask) {
+        for (int j = 0; j < 4; ++j) {
+            if (!((c->profile_mask >> j) & 1)) continue;
+            tm[j].start = next_event(c);
+            tm[j].stop = next_event(c);
+            if (!tm[j].start || !tm[j].stop) return fail(c, PW_ERR_HIP, "hipEventCreate failed");
+            c->ev_kind.push_back(j);
+        }
     }
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s));
-    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[1], s));
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
     FfnArgs fa;
     fa.pool = c->pool;
     fa.tab = dev_table(c, c->cur);
@@ -561,15 +565,10 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     fa.k = c->k;
     fa.max_act = std::min<int64_t>(c->E, (int64_t)T * c->k);
     fa.P = c->desc.max_tokens * c->k;
-    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s));
-    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[2], s));
-    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s));
-    if (c->profiling) HIP_TRY(c, hipEventRecord(ev[3], s));
-    HIP_TRY(c, launch_combine(w, T, c->d, c->k, fa.P, c->nsplit, y, s));
-    if (c->profiling) {
-        HIP_TRY(c, hipEventRecord(ev[4], s));
-        c->forwards_timed++;
-    }
+    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
+    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s, tm[2]));
+    HIP_TRY(c, launch_combine(w, T, c->d, c->k, fa.P, c->nsplit, y, s, tm[3]));
+    if (c->profile_mask) c->forwards_timed++;
     return PW_OK;
 }
 
@@ -594,11 +593,13 @@ pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, con
     return solve_allocation(E, W, p, L, budget_bits, bits_out, nullptr);
 }
 
-pw_status pw_profile(pw_ctx* c, int32_t enable) {
+pw_status pw_profile(pw_ctx* c, int32_t mask) {
     if (!c) return PW_ERR_INVALID_ARG;
-    c->profiling = enable != 0;
-    if (enable) {
+    if (mask < 0 || mask > 15) return fail(c, PW_ERR_INVALID_ARG, "profile mask must be in [0, 15]");
+    c->profile_mask = mask;
+    if (mask) {
         c->ev_used = 0;
+        c->ev_kind.clear();
         c->forwards_timed = 0;
     }
     return PW_OK;
@@ -609,12 +610,11 @@ pw_status pw_profile_read(pw_ctx* c, pw_profile_data* out) {
     std::memset(out, 0, sizeof *out);
     if (c->ev_used) HIP_TRY(c, hipEventSynchronize(c->ev_pool[c->ev_used - 1]));
     double* slot[4] = {&out->route_ms, &out->gate_up_ms, &out->down_ms, &out->combine_ms};
-    for (size_t i = 0; i + 5 <= c->ev_used; i += 5)
-        for (int j = 0; j < 4; ++j) {
-            float ms = 0.f;
-            HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_pool[i + j], c->ev_pool[i + j + 1]));
-            *slot[j] += ms;
-        }
+    for (size_t i = 0; i < c->ev_kind.size(); ++i) {
+        float ms = 0.f;
+        HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_pool[2 * i], c->ev_pool[2 * i + 1]));
+        *slot[c->ev_kind[i]] += ms;
+    }
     out->forwards = c->forwards_timed;
     return PW_OK;
 }

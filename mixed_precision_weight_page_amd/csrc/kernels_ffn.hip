@@ -394,12 +394,12 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, int lds_bytes,
 }
 
 template <int MODE>
-hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
     const int rows = MODE == 0 ? a.F : a.d;
     const int tiles = rows / 64;
     const dim3 grid((unsigned)(a.max_act * tiles * p.nsplit));
-    ffn_kernel<MODE><<<grid, kThreads, p.lds, s>>>(a, (int)p.lds, tiles, p.nsplit);
-    return hipGetLastError();
+    return launch_timed(ffn_kernel<MODE>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
+                        (int)p.lds, tiles, p.nsplit);
 }
 
 // y[t] = sum_j g[t,j] * (sum_s O[s][pos(t,j)]) in slot and split order;
@@ -454,18 +454,18 @@ int down_splits(int F, int64_t max_pairs) {
     return 1;
 }
 
-hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
-    return launch_ffn<0>(a, p, s);
+hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
+    return launch_ffn<0>(a, p, s, t);
 }
-hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
-    return launch_ffn<1>(a, p, s);
+hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
+    return launch_ffn<1>(a, p, s, t);
 }
 
 hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,
-                          hipStream_t s) {
+                          hipStream_t s, KTimer t) {
     dim3 grid((unsigned)((d + 4 * kThreads - 1) / (4 * kThreads)), (unsigned)T);
-    combine_kernel<<<grid, kThreads, 0, s>>>(w, d, k, P, nsplit, y);
-    return hipGetLastError();
+    return launch_timed(combine_kernel, grid, dim3(kThreads), 0, s, t.start, t.stop, w, d, k, P,
+                        nsplit, y);
 }
 
 }  // namespace pw

@@ -217,19 +217,18 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(int T, int E, int k, F
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s) {
-    if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxPairs) {
-        route_small_kernel<<<1, kBlock, 0, s>>>(a, w, bits);
-        return hipGetLastError();
-    }
-    route_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a, w);
-    hipError_t err = hipGetLastError();
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
+                        KTimer t) {
+    if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxPairs)
+        return launch_timed(route_small_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
+    hipError_t err = launch_timed(route_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, t.start,
+                                  (hipEvent_t) nullptr, a, w);
     if (err != hipSuccess) return err;
-    rank_kernel<<<a.E, 256, 0, s>>>(a.T, a.k, w);
-    err = hipGetLastError();
+    err = launch_timed(rank_kernel, dim3(a.E), dim3(256), 0, s, (hipEvent_t) nullptr,
+                       (hipEvent_t) nullptr, a.T, a.k, w);
     if (err != hipSuccess) return err;
-    finalize_kernel<<<1, kBlock, 0, s>>>(a.T, a.E, a.k, w, bits);
-    return hipGetLastError();
+    return launch_timed(finalize_kernel, dim3(1), dim3(kBlock), 0, s, (hipEvent_t) nullptr, t.stop,
+                        a.T, a.E, a.k, w, bits);
 }
 
 }  // namespace pw

@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI host code and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,6 +55,22 @@ struct Layout {
 
 Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit);
 
+// Optional timing of a launch: the events are stamped by the kernel's own
+// dispatch (hipExtLaunchKernel), so timing adds no packets between kernels.
+struct KTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename Kern, typename... Args>
+inline hipError_t launch_timed(Kern kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                               hipEvent_t start, hipEvent_t stop, Args... args) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0u, args...);
+    else
+        kernel<<<grid, block, lds, s>>>(args...);
+    return hipGetLastError();
+}
+
 // ---- launchers (kernels_*.hip) ----
 hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16, int E,
                          int64_t M, uint32_t* absmax, uint32_t* flags, hipStream_t s);
@@ -68,7 +85,8 @@ struct RouteArgs {
     const float* logits;
     int T, E, k, renorm;
 };
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
+                        KTimer t = {});
 
 struct FfnPlan {
     int nt_alloc;     // token rows the LDS is sized for
@@ -87,10 +105,10 @@ struct FfnArgs {
     int d, F, k, max_act;
     int P;               // pair stride of the split partial outputs O[split][P][d]
 };
-hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
-hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
+hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,
-                          hipStream_t s);
+                          hipStream_t s, KTimer t = {});
 
 // ---- host allocator (alloc.cpp) ----
 pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,

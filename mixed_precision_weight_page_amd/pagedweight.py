@@ -230,8 +230,11 @@ class PagedMoELayer:
         _check(lib().pw_get_loss_table(self._ctx, out.ctypes.data, _stream(stream)), self._ctx)
         return out.reshape(self.E, 3)
 
-    def profile(self, enable: bool):
-        _check(lib().pw_profile(self._ctx, 1 if enable else 0), self._ctx)
+    def profile(self, mask):
+        """Per-kernel timing: mask bits 0 router, 1 gate/up, 2 down, 3 combine
+        (True = all, False/0 = off)."""
+        m = 15 if mask is True else (0 if mask is False else int(mask))
+        _check(lib().pw_profile(self._ctx, m), self._ctx)
 
     def profile_read(self) -> dict:
         d = ProfileData()

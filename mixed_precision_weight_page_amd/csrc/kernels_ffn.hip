@@ -6,21 +6,21 @@
 // each of its four waves streams one 16-row block, whose tiles (16 rows x
 // 128 codes) are contiguous in the page, so every load instruction of a
 // wave reads one contiguous run. One 4B-byte load per lane per tile
-// (B = bits), prefetched several steps ahead; they are masked into fp16
-// subnormals u * 2^-24 (exact) in registers and multiplied on the
+// (B = bits), prefetched several steps ahead; they are turned into exact
+// fp16 integers q in registers (magic-exponent OR, then one packed fp16
+// subtract) and multiplied on the
 // matrix cores (v_mfma_f32_16x16x32_f16: 16 weight rows x 16 token columns,
 // K = 32), accumulating in fp32. Token rows are staged once per K chunk in
 // LDS as fp16, permuted so that each lane's 8 K-slots line up with the
-// order in which its codes unpack. The per-expert scale, the 2^24 and the
-// code offset are applied in the epilogue, so every product is exact and
-// only fp32 accumulation rounds.
+// order in which its codes unpack. The per-expert scale is applied in the
+// epilogue, so every product is exact and only fp32 accumulation rounds.
 //
 // Why matrix cores for a memory-bound skinny product: with T_e tokens per
 // expert a VALU dot product costs T_e/2 instructions per weight (packed
 // dot2), which exceeds the VALU issue budget at HBM speed (about 2.5
 // lane-instructions per 4-bit weight at 8 TB/s) as soon as T_e > 2. The
 // MFMA does the multiply-adds for up to 16 tokens at once and leaves the
-// VALU only the unpack (under one instruction per 4-bit weight).
+// VALU only the unpack (about 1.4 instructions per 4-bit weight).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -35,7 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kStep = 128;   // codes per wave per step (4 K-groups x 32)
-constexpr float kTwo24 = 16777216.0f;      // codes enter the MFMA as u * 2^-24
+constexpr uint32_t kMagic = 0x64006400u;   // two fp16 1024.0
 
 template <int B>
 struct Codes {
@@ -75,35 +75,38 @@ __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
     return c;
 }
 
-// Four dwords, each holding two codes u in its 16-bit halves, read as eight
-// fp16 values: a half with bits u (u < 1024, exponent field 0) is the
-// subnormal u * 2^-24, exact. The MFMA then sums u * x; the epilogue scales
-// by 2^24 and removes the offset 2^(B-1) * sum(x) of u = q + 2^(B-1).
-__device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+// Four dwords, each holding two fp16 values 1024 + u (the code u ORed into
+// the mantissa of 1024), minus 1024 + 2^(B-1): the exact signed code q in
+// fp16 (one packed subtract per pair). Exact q keeps the MFMA sums free of
+// the offset 2^(B-1) sum(x), which would otherwise dominate them when most
+// codes are 0 (weights far below an expert's largest weight).
+__device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                           _Float16 bias) {
     union {
         uint32_t u[4];
         half8_t h;
     } x;
     x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
-    return x.h;
+    return x.h - bias;
 }
 
-// The 16 code pairs (one code per 16-bit half) of a 3-bit group of 32 codes
-// held in three dwords; pair p = (slot 2p, slot 2p+1) of the staging
-// permutation.
+// The 16 fp16 pairs (each "1024 + code") of a 3-bit group of 32 codes held
+// in three dwords; pair p = (slot 2p, slot 2p+1) of the staging permutation.
 __device__ __forceinline__ void pairs3(const uint32_t* w, uint32_t p[16]) {
     const uint32_t M3 = 0x00070007u;
     const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
     const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
     const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
 #pragma unroll
-    for (int j = 0; j < 5; ++j) p[j] = (v01 >> (3 * j)) & M3;                                 // (j, j+16)
-    p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u);   // (5, 21)
+    for (int j = 0; j < 5; ++j) p[j] = ((v01 >> (3 * j)) & M3) | kMagic;          // (j, j+16)
+    p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u) |
+           kMagic;                                                                 // (5, 21)
 #pragma unroll
-    for (int j = 6; j < 10; ++j) p[j] = (v02 >> (3 * j - 16)) & M3;                           // (j+16, j)
-    p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u);    // (10, 26)
+    for (int j = 6; j < 10; ++j) p[j] = ((v02 >> (3 * j - 16)) & M3) | kMagic;    // (j+16, j)
+    p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u) |
+            kMagic;                                                                // (10, 26)
 #pragma unroll
-    for (int j = 11; j < 16; ++j) p[j] = (v12 >> (3 * j - 32)) & M3;                          // (j, j+16)
+    for (int j = 11; j < 16; ++j) p[j] = ((v12 >> (3 * j - 32)) & M3) | kMagic;   // (j, j+16)
 }
 
 // Code (within a 32-code group) whose activation goes to LDS slot s.
@@ -181,12 +184,14 @@ template <int B>
 __device__ __forceinline__ half8_t frag(const Codes<B>& c, int i) {
     if constexpr (B == 4) {
         const uint32_t w = c.w[i];
-        return to_frag(w & 0x000f000fu, (w >> 4) & 0x000f000fu, (w >> 8) & 0x000f000fu,
-                       (w >> 12) & 0x000f000fu);
+        return to_frag((w & 0x000f000fu) | kMagic, ((w >> 4) & 0x000f000fu) | kMagic,
+                       ((w >> 8) & 0x000f000fu) | kMagic, ((w >> 12) & 0x000f000fu) | kMagic,
+                       (_Float16)1032.0f);
     } else {
         const uint32_t w0 = c.w[2 * i], w1 = c.w[2 * i + 1];
-        return to_frag(w0 & 0x00ff00ffu, (w0 >> 8) & 0x00ff00ffu, w1 & 0x00ff00ffu,
-                       (w1 >> 8) & 0x00ff00ffu);
+        return to_frag((w0 & 0x00ff00ffu) | kMagic, ((w0 >> 8) & 0x00ff00ffu) | kMagic,
+                       (w1 & 0x00ff00ffu) | kMagic, ((w1 >> 8) & 0x00ff00ffu) | kMagic,
+                       (_Float16)1152.0f);
     }
 }
 
@@ -205,7 +210,8 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    to_frag(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]),
+                    to_frag(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3],
+                            (_Float16)1028.0f),
                     bfr, acc[m], 0, 0, 0);
         }
     } else {
@@ -226,29 +232,9 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
 // of them. Codes are prefetched PD steps ahead in a register ring; the main
 // loop issues its loads unconditionally so the ring stays full, and LDS
 // chunks of the token rows are staged before the first load when K fits.
-// Add the staged chunk's per-row sums to rsum: wave w sums rows w, w+4, ...
-// (fixed order: strided lane sums, then a butterfly), so results repeat
-// bit for bit.
-__device__ __forceinline__ void add_row_sums(const _Float16* xs, int stride, int nt, int kc,
-                                             float* rsum) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int n = wave; n < nt; n += kThreads / 64) {
-        const half8_t* row = reinterpret_cast<const half8_t*>(xs + n * stride);
-        float acc = 0.0f;
-        for (int i = lane; i < kc / 8; i += 64) {
-            const half8_t v = row[i];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc += (float)v[j];
-        }
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if (lane == 0) rsum[n] += acc;
-    }
-}
-
 template <int MODE, int B>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e, int rt, int sp,
-                                         int ks0, int nsteps, _Float16* xs, int* tok,
-                                         float* rsum) {
+                                         int ks0, int nsteps, _Float16* xs, int* tok) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
     constexpr int PD = prefetch_depth<B>();
     constexpr int SB = 16 * kStep * B / 8;   // bytes of one tile: 16 rows x 128 codes
@@ -276,8 +262,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
         if (nt * (nsteps * kStep + 8) * 2 > lds_bytes)
             spc = ((lds_bytes / (2 * nt) - 8) / (kStep * PD)) * PD;
         const int stride = spc * kStep + 8;
-        __syncthreads();   // previous token block done with tok, rsum and xs
-        if (threadIdx.x < 16) rsum[threadIdx.x] = 0.0f;
+        __syncthreads();   // previous token block done with tok and xs
         if constexpr (MODE == 0) {
             if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
         }
@@ -291,7 +276,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
             for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
         stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
         __syncthreads();
-        add_row_sums(xs, stride, nt, min(spc, nsteps) * kStep, rsum);
         f32x4 acc[NMAT];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -304,7 +288,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                 stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
-                add_row_sums(xs, stride, nt, min(spc, nsteps - s0) * kStep, rsum);
             }
             const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
@@ -324,7 +307,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                 stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
-                add_row_sums(xs, stride, nt, min(spc, nsteps - s0) * kStep, rsum);
             }
             const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
@@ -341,13 +323,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                 }
             }
         }
-        __syncthreads();   // rsum complete
-        // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n.
-        // sum_k x q = 2^24 acc - 2^(B-1) sum_k x
+        // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n
         if (r < nt) {
             const int pos = base + tb + r;
             const int orow = row0 + 4 * g;
-            const float off = (float)(1 << (B - 1)) * rsum[r];
             if constexpr (MODE == 0) {
                 union {
                     uint2 u;
@@ -355,17 +334,17 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                 } hv;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float av = s * fmaf(acc[0][v], kTwo24, -off);
-                    const float cv = s * fmaf(acc[1][v], kTwo24, -off);
+                    const float av = s * acc[0][v];
+                    const float cv = s * acc[1][v];
                     hv.h[v] = (_Float16)(av / (1.0f + expf(-av)) * cv);
                 }
                 *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + orow) = hv.u;
             } else {
                 float4 o;
-                o.x = s * fmaf(acc[0][0], kTwo24, -off);
-                o.y = s * fmaf(acc[0][1], kTwo24, -off);
-                o.z = s * fmaf(acc[0][2], kTwo24, -off);
-                o.w = s * fmaf(acc[0][3], kTwo24, -off);
+                o.x = s * acc[0][0];
+                o.y = s * acc[0][1];
+                o.z = s * acc[0][2];
+                o.w = s * acc[0][3];
                 *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + pos) * a.d + orow) = o;
             }
         }
@@ -378,7 +357,6 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     __shared__ int tok[16];
-    __shared__ float rsum[16];
     const int per_expert = tiles * nsplit;
     const int ai = blockIdx.x / per_expert;
     if (ai >= a.w.n_act[0]) return;
@@ -388,9 +366,9 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, int lds_bytes,
     const int b = a.tab.bits[e];
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
-    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
-    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
-    else ffn_tile<MODE, 3>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok, rsum);
+    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
+    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
+    else ffn_tile<MODE, 3>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
 }
 
 template <int MODE>

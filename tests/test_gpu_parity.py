@@ -216,3 +216,20 @@ def test_zero_expert_and_lossless_grid():
     x, logits = synth.tokens(wl)
     y = layer.moe_forward(x.cuda(), logits.cuda())
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), "grid")
+
+
+def test_mostly_zero_codes_keep_precision():
+    """Outliers x1000 make nearly every 3- and 4-bit code 0, so the true
+    products sum only a few terms; the kernel must not let the code offset
+    2^(b-1) sum(x) swamp them (long K = 4096 makes that visible)."""
+    wl = synth.WORKLOADS["decode_fine"].scaled(name="sparse_codes", E=8, d=4096, F=256, k=2,
+                                               T=16, outlier_rate=0.0005, outlier_mult=1000.0,
+                                               bits=(3, 3, 3, 4, 4, 8, 3, 4))
+    masters = synth.expert_weights(wl)
+    x, logits = synth.tokens(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    ref = oracle_y(x, logits, wl, masters, wl.bits)
+    norm_err, _ = compare_y(y, ref, "mostly-zero codes")
+    assert norm_err < 1e-3

@@ -336,6 +336,8 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
         at = align_up(at + bytes, kAlign);
         return o;
     };
+    const uint64_t scratch = at;
+    // forward scratch
     L.ids = take(4 * P);
     L.g = take(4 * P);
     L.rank = take(4 * P);
@@ -348,10 +350,10 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.H = take(2 * P * (uint64_t)F);
     L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
     L.fwd_end = at;
-    // the loss pass reuses the same memory (calls on one stream are ordered)
+    // the loss pass reuses the forward scratch (calls on one stream are ordered)
     const uint64_t nblk = 3 * (uint64_t)F * d / kStatChunk;
-    L.partial = 0;
-    L.stats_end = align_up(8 * 3 * nblk * (uint64_t)E, kAlign);
+    L.partial = scratch;
+    L.stats_end = scratch + align_up(8 * 3 * nblk * (uint64_t)E, kAlign);
     L.total = std::max(L.fwd_end, L.stats_end);
     return L;
 }

@@ -9,9 +9,12 @@
 // active experts is ordered 8-bit pages first, then 4-bit, then 3-bit (each
 // by expert id), so the longest tiles are dispatched first.
 //
-// Small batches (T <= kFusedMaxT) run everything in one workgroup; larger
-// ones use three kernels (route, per-expert rank, finalize). No host
-// synchronisation: later kernels read the counts from device memory.
+// Up to 16 tokens: one workgroup does everything. Up to kFusedMaxPairs
+// pairs: a router kernel (one wave per token, many workgroups), then one
+// workgroup ranks and offsets. Larger batches: router, per-expert rank,
+// finalize. Kernel boundaries carry the results between workgroups (a
+// device-scope handshake inside one kernel would have to write back and
+// invalidate the per-XCD L2 caches). No host synchronisation.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -30,16 +33,17 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
 }
 
 // One wave routes token t: writes ids/g (and the ids to s_ids if given).
-__device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t,
-                                            int* s_ids) {
+// PER = logits held per lane (ceil(E / 64)).
+template <int PER>
+__device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork& w, int t,
+                                              int* s_ids) {
     const int lane = threadIdx.x & 63;
     const float* row = a.logits + (int64_t)t * a.E;
-    const int per = (a.E + 63) / 64;
-    float v[kMaxPerLane];
+    float v[PER];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        v[i] = (i < per && e < a.E) ? row[e] : -INFINITY;
+        v[i] = e < a.E ? row[e] : -INFINITY;
     }
     int my_id = 0;
     float my_val = -INFINITY, top = -INFINITY;
@@ -48,9 +52,9 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w
         float bv = -INFINITY;
         int be = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
+        for (int i = 0; i < PER; ++i) {
             const int e = lane + 64 * i;
-            if (i < per && e < a.E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
+            if (e < a.E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
                 bv = v[i];
                 be = e;
             }
@@ -66,9 +70,9 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w
     }
     float sum_all = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        if (i < per && e < a.E) sum_all += expf(v[i] - top);
+        if (e < a.E) sum_all += expf(v[i] - top);
     }
     const float mine = lane < a.k ? expf(my_val - top) : 0.0f;
     float den = a.renorm ? mine : sum_all;
@@ -78,6 +82,15 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w
         w.g[(int64_t)t * a.k + lane] = mine / den;
         if (s_ids) s_ids[t * a.k + lane] = my_id;
     }
+}
+
+__device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t, int* s_ids) {
+    const int per = (a.E + 63) / 64;
+    if (per == 1) route_token_t<1>(a, w, t, s_ids);
+    else if (per == 2) route_token_t<2>(a, w, t, s_ids);
+    else if (per <= 4) route_token_t<4>(a, w, t, s_ids);
+    else if (per <= 8) route_token_t<8>(a, w, t, s_ids);
+    else route_token_t<16>(a, w, t, s_ids);
 }
 
 // Inclusive scan over the 1024 threads of the block (every thread calls it).
@@ -145,26 +158,21 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
     }
 }
 
-// ---- small batches: one workgroup ----
-__global__ __launch_bounds__(kBlock) void route_small_kernel(RouteArgs a, FwdWork w,
-                                                             const int32_t* bits) {
-    __shared__ int s_ids[kFusedMaxPairs];
-    __shared__ int s_rank[kFusedMaxPairs];
-    __shared__ int s_cnt[kMaxExperts];
+// Stable rank of every pair from ids in LDS: wave handles experts wave,
+// wave + 16, ...; lanes = tokens. Writes s_rank, s_cnt and w.cnt.
+__device__ __forceinline__ void rank_small(int T, int E, int k, const int* s_ids, int* s_rank,
+                                           int* s_cnt, const FwdWork& w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < a.T; t += kWaves) route_token(a, w, t, s_ids);
-    __syncthreads();
-    // stable rank: wave handles experts wave, wave + 16, ...; lanes = tokens
-    for (int e = wave; e < a.E; e += kWaves) {
+    for (int e = wave; e < E; e += kWaves) {
         int running = 0;
-        for (int t0 = 0; t0 < a.T; t0 += 64) {
-            const int t = t0 + lane;
+        for (int t0 = 0; t0 < T; t0 += 64) {
+            const int tt = t0 + lane;
             int slot = -1;
-            if (t < a.T)
-                for (int j = 0; j < a.k; ++j)
-                    if (s_ids[t * a.k + j] == e) slot = j;
+            if (tt < T)
+                for (int j = 0; j < k; ++j)
+                    if (s_ids[tt * k + j] == e) slot = j;
             const uint64_t m = __ballot(slot >= 0);
-            if (slot >= 0) s_rank[t * a.k + slot] = running + __popcll(m & ((1ull << lane) - 1ull));
+            if (slot >= 0) s_rank[tt * k + slot] = running + __popcll(m & ((1ull << lane) - 1ull));
             running += __popcll(m);
         }
         if (lane == 0) {
@@ -172,8 +180,35 @@ __global__ __launch_bounds__(kBlock) void route_small_kernel(RouteArgs a, FwdWor
             w.cnt[e] = running;
         }
     }
+}
+
+// ---- tiny batches (T <= 16): everything in one workgroup ----
+__global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWork w,
+                                                             const int32_t* bits) {
+    __shared__ int s_ids[kFusedMaxPairs];
+    __shared__ int s_rank[kFusedMaxPairs];
+    __shared__ int s_cnt[kMaxExperts];
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < a.T; t += kWaves) route_token(a, w, t, s_ids);
+    __syncthreads();
+    rank_small(a.T, a.E, a.k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
     finalize(a.T, a.E, a.k, w, bits, [&](int e) { return s_cnt[e]; },
+             [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
+}
+
+// ---- small batches: ranking and offsets of routed pairs in one workgroup ----
+__global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k, FwdWork w,
+                                                             const int32_t* bits) {
+    __shared__ int s_ids[kFusedMaxPairs];
+    __shared__ int s_rank[kFusedMaxPairs];
+    __shared__ int s_cnt[kMaxExperts];
+    const int P = T * k;
+    for (int p = threadIdx.x; p < P; p += kBlock) s_ids[p] = w.ids[p];
+    __syncthreads();
+    rank_small(T, E, k, s_ids, s_rank, s_cnt, w);
+    __syncthreads();
+    finalize(T, E, k, w, bits, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
@@ -219,16 +254,17 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(int T, int E, int k, F
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
                         KTimer t) {
-    if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxPairs)
-        return launch_timed(route_small_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
-    hipError_t err = launch_timed(route_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, t.start,
-                                  (hipEvent_t) nullptr, a, w);
+    const hipEvent_t none = nullptr;
+    if (a.T <= kWaves && a.T * a.k <= kFusedMaxPairs)
+        return launch_timed(route_fused_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
+    hipError_t err = launch_timed(route_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, t.start, none, a, w);
     if (err != hipSuccess) return err;
-    err = launch_timed(rank_kernel, dim3(a.E), dim3(256), 0, s, (hipEvent_t) nullptr,
-                       (hipEvent_t) nullptr, a.T, a.k, w);
+    if (a.T * a.k <= kFusedMaxPairs)
+        return launch_timed(group_small_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k,
+                            w, bits);
+    err = launch_timed(rank_kernel, dim3(a.E), dim3(256), 0, s, none, none, a.T, a.k, w);
     if (err != hipSuccess) return err;
-    return launch_timed(finalize_kernel, dim3(1), dim3(kBlock), 0, s, (hipEvent_t) nullptr, t.stop,
-                        a.T, a.E, a.k, w, bits);
+    return launch_timed(finalize_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k, w, bits);
 }
 
 }  // namespace pw

@@ -17,8 +17,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kRowAlign = 128;         // codes per row are a multiple of this
 constexpr int kPageAlign = 256;        // page offsets and sizes
 constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
-constexpr int kFusedMaxT = 256;        // batches routed by a single workgroup
-constexpr int kFusedMaxPairs = 4096;
+constexpr int kFusedMaxPairs = 4096;   // (token, slot) pairs ranked by one workgroup
 
 // supported bit-widths, in loss-table order
 __host__ __device__ constexpr int bits_of_index(int i) { return i == 0 ? 3 : i == 1 ? 4 : 8; }

@@ -43,7 +43,10 @@ def test_tiny_pages_and_forward():
 
 
 def test_router_matches_oracle():
-    for wl, T in ((TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300)):
+    # one-workgroup path (T <= 16), router + one-workgroup grouping, and the
+    # three-kernel path (more than 4096 pairs)
+    for wl, T in ((TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300),
+                  (SMALL_FINE, 700)):
         masters = tuple(torch.zeros(1) for _ in range(3))
         from mixed_precision_weight_page_amd import PagedMoELayer
         layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=T)

@@ -145,6 +145,7 @@ FwdWork fwd_work(pw_ctx* c) {
     w.off = reinterpret_cast<int32_t*>(b + c->lay.off);
     w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
     w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
+    w.tt_off = reinterpret_cast<int32_t*>(b + c->lay.tt_off);
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
     w.O = reinterpret_cast<float*>(b + c->lay.O);
     return w;
@@ -347,6 +348,7 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.off = take(4 * (uint64_t)(E + 1));
     L.act = take(4 * (uint64_t)E);
     L.n_act = take(4);
+    L.tt_off = take(4 * (uint64_t)(E + 1));
     L.H = take(2 * P * (uint64_t)F);
     L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
     L.fwd_end = at;
@@ -557,19 +559,40 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     }
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
     HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
-    FfnArgs fa;
-    fa.pool = c->pool;
-    fa.tab = dev_table(c, c->cur);
-    fa.w = w;
-    fa.x = static_cast<const uint16_t*>(x);
-    fa.d = c->d;
-    fa.F = c->F;
-    fa.k = c->k;
-    fa.max_act = std::min<int64_t>(c->E, (int64_t)T * c->k);
-    fa.P = c->desc.max_tokens * c->k;
-    HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
-    HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s, tm[2]));
-    HIP_TRY(c, launch_combine(w, T, c->d, c->k, fa.P, c->nsplit, y, s, tm[3]));
+    const int64_t pairs = (int64_t)T * c->k;
+    const int max_act = (int)std::min<int64_t>(c->E, pairs);
+    const int P = c->desc.max_tokens * c->k;
+    // many tokens per expert: dense tiles on the matrix cores (weights read
+    // once per 128 tokens); few: the streaming kernels (weights read once)
+    if (gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act) {
+        GemmArgs ga;
+        ga.pool = c->pool;
+        ga.tab = dev_table(c, c->cur);
+        ga.w = w;
+        ga.x = static_cast<const uint16_t*>(x);
+        ga.d = c->d;
+        ga.F = c->F;
+        ga.k = c->k;
+        ga.max_act = max_act;
+        ga.P_used = pairs;
+        HIP_TRY(c, launch_gate_up_gemm(ga, s, tm[1]));
+        HIP_TRY(c, launch_down_gemm(ga, s, tm[2]));
+        HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, 1, y, s, tm[3]));
+    } else {
+        FfnArgs fa;
+        fa.pool = c->pool;
+        fa.tab = dev_table(c, c->cur);
+        fa.w = w;
+        fa.x = static_cast<const uint16_t*>(x);
+        fa.d = c->d;
+        fa.F = c->F;
+        fa.k = c->k;
+        fa.max_act = max_act;
+        fa.P = P;
+        HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
+        HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s, tm[2]));
+        HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, c->nsplit, y, s, tm[3]));
+    }
     if (c->profile_mask) c->forwards_timed++;
     return PW_OK;
 }

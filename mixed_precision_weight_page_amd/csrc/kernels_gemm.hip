@@ -1,0 +1,394 @@
+// Expert FFN for large batches (prefill): per active expert, a dense
+// product of its T_e routed tokens with its dequantized weights on the
+// matrix cores (PagedWeight page, section "Dynamic Paging": pages are
+// dequantized on the fly; Eq. 2: W = s_e q). SwiGLU as in the decode path:
+// h = silu(W1 x) * (W3 x) (MODE 0), o = W2 h (MODE 1).
+//
+// Workgroup tile: 128 weight rows (of W1 and W3 for MODE 0) x 128 tokens of
+// one expert. Each of the four waves owns 32 rows (two 16-row blocks of the
+// page's tiles) for all 128 tokens and streams its codes straight from the
+// page into registers, prefetched several 128-code steps ahead, turning them
+// into exact fp16 integers q in registers (no LDS for weights, each code read
+// once per workgroup). The 128 token rows go through double-buffered LDS, one
+// 128-code step at a time, as fp16 in the same per-32 K permutation as the
+// codes unpack, so each MFMA operand of a lane is one 16-byte read.
+// Per step and wave: 4 K-groups x (2 blocks x matrices) x 8 token blocks of
+// v_mfma_f32_16x16x32_f16, fp32 accumulate.
+//
+// Tile order: expert (in the active list, 8-bit first), token tile, row
+// tile; workgroup b runs tile (b % 8) * N/8 + b / 8, so each XCD (which
+// receives every eighth workgroup) walks one contiguous range: the workgroups
+// resident on an XCD share token rows and weight tiles through its L2.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "pw_internal.h"
+
+namespace pw {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 128;          // weight rows per tile (per matrix)
+constexpr int BN = kGemmTokens;  // tokens per tile
+constexpr uint32_t kMagic = 0x64006400u;
+
+template <int B>
+struct Run {
+    uint32_t w[B];   // 32 consecutive codes of one row, LSB-first
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One 32-code run at p (lane offset applied): 16 bytes (4-bit), 16 + 16
+// bytes 1 KB apart (8-bit), 12 bytes (3-bit). Non-temporal: codes are read
+// once per workgroup.
+template <int B>
+__device__ __forceinline__ Run<B> load_run_at(const uint8_t* p) {
+    Run<B> r;
+    if constexpr (B == 4) {
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+    } else if constexpr (B == 8) {
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 1024));
+        r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+        r.w[4] = v.x; r.w[5] = v.y; r.w[6] = v.z; r.w[7] = v.w;
+    } else {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        r.w[0] = __builtin_nontemporal_load(q);
+        r.w[1] = __builtin_nontemporal_load(q + 1);
+        r.w[2] = __builtin_nontemporal_load(q + 2);
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint4 sub_bias(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                          _Float16 bias) {
+    union {
+        uint32_t u[4];
+        half8_t h;
+        uint4 v;
+    } x;
+    x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
+    x.h = x.h - bias;
+    return x.v;
+}
+
+// The 32 codes of a run as exact fp16 q, in the K-slot order of the staging
+// permutation (4 x 16 bytes).
+template <int B>
+__device__ __forceinline__ void run_to_f16(const Run<B>& r, uint4 out[4]) {
+    if constexpr (B == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = r.w[i];
+            out[i] = sub_bias((w & 0x000f000fu) | kMagic, ((w >> 4) & 0x000f000fu) | kMagic,
+                              ((w >> 8) & 0x000f000fu) | kMagic, ((w >> 12) & 0x000f000fu) | kMagic,
+                              (_Float16)1032.0f);
+        }
+    } else if constexpr (B == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w0 = r.w[2 * i], w1 = r.w[2 * i + 1];
+            out[i] = sub_bias((w0 & 0x00ff00ffu) | kMagic, ((w0 >> 8) & 0x00ff00ffu) | kMagic,
+                              (w1 & 0x00ff00ffu) | kMagic, ((w1 >> 8) & 0x00ff00ffu) | kMagic,
+                              (_Float16)1152.0f);
+        }
+    } else {
+        const uint32_t* w = r.w;
+        const uint32_t M3 = 0x00070007u;
+        const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
+        const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
+        const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
+        uint32_t p[16];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) p[j] = ((v01 >> (3 * j)) & M3) | kMagic;
+        p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u) | kMagic;
+#pragma unroll
+        for (int j = 6; j < 10; ++j) p[j] = ((v02 >> (3 * j - 16)) & M3) | kMagic;
+        p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u) | kMagic;
+#pragma unroll
+        for (int j = 11; j < 16; ++j) p[j] = ((v12 >> (3 * j - 32)) & M3) | kMagic;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[i] = sub_bias(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3], (_Float16)1028.0f);
+    }
+}
+
+// Code (within a 32-code run) whose activation goes to K-slot s.
+template <int B>
+__device__ __forceinline__ constexpr int perm_slot(int s) {
+    if constexpr (B == 4) {
+        constexpr int p[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        return (s & ~7) + p[s & 7];
+    } else if constexpr (B == 8) {
+        constexpr int p[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        return (s & ~7) + p[s & 7];
+    } else {
+        constexpr int p[32] = {0, 16, 1, 17, 2, 18, 3, 19, 4, 20, 5, 21, 22, 6, 23, 7,
+                               24, 8, 25, 9, 10, 26, 11, 27, 12, 28, 13, 29, 14, 30, 15, 31};
+        return p[s];
+    }
+}
+
+// 32 consecutive activations (bf16 for MODE 0, fp16 for MODE 1) as fp16 in
+// K-slot order.
+template <int MODE, int B>
+__device__ __forceinline__ void act_to_f16(const uint4 (&in)[4], uint4 out[4]) {
+    _Float16 v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t ww[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            if constexpr (MODE == 0) {
+                v[8 * q + 2 * h] = (_Float16)__uint_as_float((ww[h] & 0xffffu) << 16);
+                v[8 * q + 2 * h + 1] = (_Float16)__uint_as_float(ww[h] & 0xffff0000u);
+            } else {
+                union {
+                    uint32_t u;
+                    _Float16 f[2];
+                } t;
+                t.u = ww[h];
+                v[8 * q + 2 * h] = t.f[0];
+                v[8 * q + 2 * h + 1] = t.f[1];
+            }
+        }
+    }
+    union {
+        uint4 u[4];
+        _Float16 h[32];
+    } o;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) o.h[s] = v[perm_slot<B>(s)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = o.u[q];
+}
+
+constexpr int SK = 128;            // K codes per step (one page tile)
+constexpr int LDX = SK + 8;        // padded LDS row of staged tokens (halves)
+
+// Steps of codes in flight per wave.
+template <int B>
+__device__ __forceinline__ constexpr int gemm_depth() { return B == 8 ? 2 : 4; }  // even
+
+template <int B>
+__device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i) {
+    union {
+        uint4 v[4];
+        half8_t h[4];
+    } o;
+    run_to_f16<B>(r, o.v);   // the compiler keeps only fragment i alive
+    return o.h[i];
+}
+
+// Token rows of one step: thread t stages token t / 2, codes 64 (t % 2) ..
+// +64 of the step (two 32-code runs).
+template <int MODE>
+__device__ __forceinline__ void load_act(uint4 (&xr)[8], const uint8_t* act_row, int step, int tid) {
+    const uint4* src = reinterpret_cast<const uint4*>(act_row + (int64_t)(step * SK + 64 * (tid & 1)) * 2);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xr[q] = src[q];
+}
+
+template <int MODE, int B>
+__device__ __forceinline__ void store_act(const uint4 (&xr)[8], _Float16* xs, int tid) {
+    uint4* dst = reinterpret_cast<uint4*>(xs + (tid >> 1) * LDX + 64 * (tid & 1));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4 in[4] = {xr[4 * h], xr[4 * h + 1], xr[4 * h + 2], xr[4 * h + 3]};
+        uint4 o[4];
+        act_to_f16<MODE, B>(in, o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[4 * h + q] = o[q];
+    }
+}
+
+template <int MODE, int B>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
+                                          int* tok) {
+    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    constexpr int PD = gemm_depth<B>();
+    constexpr int TB = 256 * B;                  // bytes of one 16-row x 128-code tile
+    const int K = MODE == 0 ? a.d : a.F;
+    const int S = K / SK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int Te = a.w.cnt[e];
+    const int base = a.w.off[e];
+    const int t0 = tt * BN;
+    const int nt = min(BN, Te - t0);
+    const float s = a.tab.scale[e];
+    const uint8_t* page = a.pool + a.tab.off[e];
+    const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
+    const int loff = (B == 3 ? 12 : 16) * lane;
+    // this wave's code streams: matrix m, row block rb0 + blk, all K steps
+    const int rb0 = rt * (BM / 16) + 2 * wave;
+    const uint8_t* ap[NMAT][2];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            ap[m][blk] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)(rb0 + blk) * S * TB + loff;
+
+    if (tid < BN) {
+        const int n = tid < nt ? tid : 0;   // past nt: repeat the first row, outputs dropped
+        tok[tid] = MODE == 0 ? a.w.sorted[base + t0 + n] / a.k : base + t0 + n;
+    }
+    __syncthreads();
+    const int my_tok = tok[tid >> 1];
+    const uint8_t* act_row = MODE == 0
+        ? reinterpret_cast<const uint8_t*>(a.x + (int64_t)my_tok * a.d)
+        : reinterpret_cast<const uint8_t*>(a.w.H + (int64_t)my_tok * a.F);
+    _Float16* xs[2] = {smem, smem + BN * LDX};
+
+    // prologue: codes for steps 0..PD-1 in flight, token rows of step 0 staged
+    Run<B> ring[PD][NMAT][2];
+#pragma unroll
+    for (int j = 0; j < PD; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+                ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(j, S - 1) * TB);
+    // token rows travel two steps ahead: xr[p] holds the step that goes to
+    // LDS at the end of the current step
+    uint4 xr[2][8];
+    load_act<MODE>(xr[0], act_row, 0, tid);
+    store_act<MODE, B>(xr[0], xs[0], tid);
+    load_act<MODE>(xr[1], act_row, min(1, S - 1), tid);
+    __syncthreads();
+
+    f32x4 acc[NMAT][2][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = 0; s0 < S; s0 += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) {
+            const int st = s0 + j;
+            if (st < S) {
+                // token rows two steps ahead and codes PD steps ahead, unconditionally
+                load_act<MODE>(xr[j & 1], act_row, min(st + 2, S - 1), tid);
+                Run<B> cur[NMAT][2];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int blk = 0; blk < 2; ++blk) {
+                        cur[m][blk] = ring[j][m][blk];
+                        ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
+                    }
+                // lane (r, g): its run holds codes 32g..32g+31 of the step and
+                // MFMA kc uses codes 32g + 8kc..+8, so the token fragment is the
+                // same 8 K-slots of token row 16 jt + r
+                const _Float16* xb = xs[st & 1] + r * LDX + 32 * g;
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    half8_t af[NMAT][2];
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(cur[m][blk], kc);
+#pragma unroll
+                    for (int jt = 0; jt < 8; ++jt) {
+                        const half8_t bf = *reinterpret_cast<const half8_t*>(xb + 16 * jt * LDX + 8 * kc);
+#pragma unroll
+                        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                            for (int blk = 0; blk < 2; ++blk)
+                                acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bf,
+                                                                                         acc[m][blk][jt], 0, 0, 0);
+                    }
+                }
+                if (st + 1 < S) store_act<MODE, B>(xr[(j & 1) ^ 1], xs[(st + 1) & 1], tid);
+                __syncthreads();
+            }
+        }
+    }
+    // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+        const int n = 16 * jt + r;
+        if (n >= nt) continue;
+        const int pos = base + t0 + n;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int row = rt * BM + 32 * wave + 16 * blk + 4 * g;
+            if constexpr (MODE == 0) {
+                union {
+                    uint2 u;
+                    _Float16 h[4];
+                } hv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float av = s * acc[0][blk][jt][v];
+                    const float cv = s * acc[1][blk][jt][v];
+                    hv.h[v] = (_Float16)(av / (1.0f + expf(-av)) * cv);
+                }
+                *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + row) = hv.u;
+            } else {
+                float4 o;
+                o.x = s * acc[0][blk][jt][0];
+                o.y = s * acc[0][blk][jt][1];
+                o.z = s * acc[0][blk][jt][2];
+                o.w = s * acc[0][blk][jt][3];
+                *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + row) = o;
+            }
+        }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, int row_tiles, int ntiles) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
+    __shared__ int tok[BN];
+    // XCD swizzle: the eighth of the tile range that this workgroup's XCD walks
+    const int L = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+    const int tg = L / row_tiles;                  // token tile, over all experts
+    const int rt = L - tg * row_tiles;
+    const int na = a.w.n_act[0];
+    if (tg >= a.w.tt_off[na]) return;
+    int lo = 0, hi = na;                           // expert slot: tt_off[lo] <= tg < tt_off[lo + 1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.w.tt_off[mid] <= tg) lo = mid; else hi = mid;
+    }
+    const int e = a.w.act[lo];
+    const int tt = tg - a.w.tt_off[lo];
+    const int b = a.tab.bits[e];
+    if (b == 4) gemm_tile<MODE, 4>(a, e, tt, rt, smem, tok);
+    else if (b == 8) gemm_tile<MODE, 8>(a, e, tt, rt, smem, tok);
+    else gemm_tile<MODE, 3>(a, e, tt, rt, smem, tok);
+}
+
+template <int MODE>
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
+    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    const int rows = MODE == 0 ? a.F : a.d;
+    const int row_tiles = rows / BM;
+    // token tiles over all experts: at most ceil(P / BN) + (active experts)
+    const int64_t tt_max = (a.P_used + BN - 1) / BN + a.max_act;
+    int64_t ntiles = tt_max * row_tiles;
+    ntiles = (ntiles + 7) / 8 * 8;
+    const size_t lds = 2 * (size_t)BN * LDX * 2;
+    return launch_timed(gemm_kernel<MODE>, dim3((unsigned)ntiles), dim3(kThreads), lds, s, t.start,
+                        t.stop, a, row_tiles, (int)ntiles);
+}
+
+}  // namespace
+
+bool gemm_supported(int d, int F) { return d % BM == 0 && F % BM == 0; }
+
+hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<0>(a, s, t); }
+hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<1>(a, s, t); }
+
+}  // namespace pw

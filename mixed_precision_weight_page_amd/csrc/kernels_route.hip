@@ -148,6 +148,20 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
         w.act[base + before] = tid;
     }
     if (tid == 0) w.n_act[0] = n8 + n4 + n3;
+    // token tiles of the large-batch kernels, in active-list order
+    __shared__ int s_slot_cnt[kMaxExperts];
+    if (flag) {
+        const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
+        const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
+        s_slot_cnt[base + before] = c;
+    }
+    __syncthreads();
+    const int na = n8 + n4 + n3;
+    const int ntt = tid < na ? (s_slot_cnt[tid] + kGemmTokens - 1) / kGemmTokens : 0;
+    int ttot;
+    const int tinc = block_scan<int>(ntt, s_wave_i, &ttot);
+    if (tid < na) w.tt_off[tid] = tinc - ntt;
+    if (tid == 0) w.tt_off[na] = ttot;
     __syncthreads();
     const int P = T * k;
     for (int p = tid; p < P; p += kBlock) {

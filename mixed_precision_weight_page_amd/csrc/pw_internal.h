@@ -18,6 +18,8 @@ constexpr int kRowAlign = 128;         // codes per row are a multiple of this
 constexpr int kPageAlign = 256;        // page offsets and sizes
 constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
 constexpr int kFusedMaxPairs = 4096;   // (token, slot) pairs ranked by one workgroup
+constexpr int kGemmTokens = 128;       // tokens per tile of the large-batch kernels
+constexpr int kGemmMinTokens = 64;     // mean tokens per active expert for those kernels
 
 // supported bit-widths, in loss-table order
 __host__ __device__ constexpr int bits_of_index(int i) { return i == 0 ? 3 : i == 1 ? 4 : 8; }
@@ -42,12 +44,13 @@ struct FwdWork {
     int32_t* off;      // [E+1] exclusive prefix of cnt
     int32_t* act;      // [E] experts with cnt > 0, ascending
     int32_t* n_act;    // [1]
+    int32_t* tt_off;   // [E+1] prefix over the active list of ceil(cnt / kGemmTokens)
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
     float* O;          // [nsplit, P, d] down-projection partials per sorted pair (scaled by s_e)
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, H, O, fwd_end;
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, H, O, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };
@@ -108,6 +111,18 @@ hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTi
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,
                           hipStream_t s, KTimer t = {});
+
+struct GemmArgs {
+    const uint8_t* pool;
+    DevTable tab;
+    FwdWork w;
+    const uint16_t* x;   // bf16 [T, d]
+    int d, F, k, max_act;
+    int64_t P_used;      // T * k of this call
+};
+bool gemm_supported(int d, int F);
+hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
+hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 
 // ---- host allocator (alloc.cpp) ----
 pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,

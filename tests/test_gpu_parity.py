@@ -236,3 +236,19 @@ def test_mostly_zero_codes_keep_precision():
     ref = oracle_y(x, logits, wl, masters, wl.bits)
     norm_err, _ = compare_y(y, ref, "mostly-zero codes")
     assert norm_err < 1e-3
+
+
+@pytest.mark.parametrize("T", [600, 257])
+def test_large_batch_matrix_core_path(T):
+    """Batches with many tokens per expert take the tiled matrix-core
+    kernels (128 tokens x 128 rows per workgroup): ragged last token tile,
+    3/4/8-bit experts, and an expert left without tokens."""
+    wl = synth.WORKLOADS["tiny"].scaled(name="gemm_path", E=8, d=512, F=384, k=2, T=T,
+                                        bits=(8, 3, 4, 4, 3, 8, 4, 3))
+    masters = synth.expert_weights(wl)
+    x, logits = synth.tokens(wl)
+    logits[:, 6] = -50.0     # expert 6 gets no tokens
+    layer, pool = make_layer(wl, masters, max_tokens=T)
+    layer.quantize_experts(wl.bits)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")

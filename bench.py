@@ -49,15 +49,17 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-kernel events (no roofline)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources of the decode gate/up kernel (the roofline kernel)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in ("kernels_ffn.hip", "pw_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -198,6 +200,15 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
     wl = synth.WORKLOADS[args.workload]
     if args.workload == "dynamic":
         return bench_dynamic(args, wl, log)

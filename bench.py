@@ -230,9 +230,9 @@ def main():
     if args.workload == "prefill":
         pairs = T * wl.k
         flops = 2.0 * pairs * 2 * wl.d * wl.F          # gate/up: 2 flops per weight per pair
-        achieved = flops / (gu_ms * 1e-3) / 1e12
+        achieved = flops / (gu_ms * 1e-3) / 1e12 if gu_ms > 0 else None
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
+                "unit": "TFLOP/s", "frac": (achieved or 0) / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "gate_up (fused dequant + W1/W3 + SwiGLU)"}
     else:
         roof = {"bound": "hbm", "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

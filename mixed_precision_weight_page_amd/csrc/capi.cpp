@@ -351,6 +351,7 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.tt_off = take(4 * (uint64_t)(E + 1));
     L.H = take(2 * P * (uint64_t)F);
     L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
+    L.xp = take(2 * 3 * (uint64_t)max_tokens * (uint64_t)d);
     L.fwd_end = at;
     // the loss pass reuses the forward scratch (calls on one stream are ordered)
     const uint64_t nblk = 3 * (uint64_t)F * d / kStatChunk;
@@ -575,7 +576,14 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         ga.k = c->k;
         ga.max_act = max_act;
         ga.P_used = pairs;
+        ga.T = T;
+        ga.xp = reinterpret_cast<const _Float16*>(c->ws + c->lay.xp);
+        ga.xp_plane = (int64_t)c->desc.max_tokens * c->d;
+        ga.bits_mask = 0;
+        for (int e = 0; e < c->E; ++e) ga.bits_mask |= 1 << bits_index(c->table[e].bits);
+        HIP_TRY(c, launch_prep_x(ga, s));
         HIP_TRY(c, launch_gate_up_gemm(ga, s, tm[1]));
+        HIP_TRY(c, launch_prep_h(ga, s));
         HIP_TRY(c, launch_down_gemm(ga, s, tm[2]));
         HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, 1, y, s, tm[3]));
     } else {

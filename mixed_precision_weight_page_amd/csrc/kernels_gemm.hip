@@ -135,17 +135,17 @@ __device__ __forceinline__ constexpr int perm_slot(int s) {
     }
 }
 
-// 32 consecutive activations (bf16 for MODE 0, fp16 for MODE 1) as fp16 in
-// K-slot order.
-template <int MODE, int B>
-__device__ __forceinline__ void act_to_f16(const uint4 (&in)[4], uint4 out[4]) {
+// 32 consecutive activations (bf16 when SRC_BF16, else fp16) as fp16 in the
+// K-slot order of B-bit codes.
+template <bool SRC_BF16, int B>
+__device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4]) {
     _Float16 v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t ww[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            if constexpr (MODE == 0) {
+            if constexpr (SRC_BF16) {
                 v[8 * q + 2 * h] = (_Float16)__uint_as_float((ww[h] & 0xffffu) << 16);
                 v[8 * q + 2 * h + 1] = (_Float16)__uint_as_float(ww[h] & 0xffff0000u);
             } else {
@@ -169,8 +169,56 @@ __device__ __forceinline__ void act_to_f16(const uint4 (&in)[4], uint4 out[4]) {
     for (int q = 0; q < 4; ++q) out[q] = o.u[q];
 }
 
+// Token rows for the gate/up tiles, once per forward: xp[i][t] = x[t] as
+// fp16 in the K order of the codes of bit-width kBits[i], for each
+// bit-width some expert uses (bit i of mask). grid (T, 3).
+__global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int d, int mask,
+                                                          _Float16* xp, int64_t plane) {
+    const int i = blockIdx.y;
+    if (!((mask >> i) & 1)) return;
+    const int64_t t = blockIdx.x;
+    for (int grp = threadIdx.x; grp < d / 32; grp += kThreads) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + t * d + 32 * grp);
+        uint4 in[4] = {src[0], src[1], src[2], src[3]};
+        uint4 o[4];
+        if (i == 0) permute32<true, 3>(in, o);
+        else if (i == 1) permute32<true, 4>(in, o);
+        else permute32<true, 8>(in, o);
+        uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + t * d + 32 * grp);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = o[q];
+    }
+}
+
+// SwiGLU rows for the down tiles: H[pos] permuted in place into the K order
+// of its expert's codes. grid (active slot, row blocks of 64 pairs).
+__global__ __launch_bounds__(kThreads) void prep_h_kernel(FwdWork w, DevTable tab, int F) {
+    const int ai = blockIdx.x;
+    if (ai >= w.n_act[0]) return;
+    const int e = w.act[ai];
+    const int b = tab.bits[e];
+    const int cnt = w.cnt[e], base = w.off[e];
+    const int ngrp = F / 32;
+    // each (row, group) is owned by one thread: read, permute, write back
+    for (int idx = blockIdx.y * kThreads + threadIdx.x; idx < cnt * ngrp; idx += gridDim.y * kThreads) {
+        const int row = idx / ngrp, grp = idx - row * ngrp;
+        uint4* p = reinterpret_cast<uint4*>(w.H + (int64_t)(base + row) * F + 32 * grp);
+        uint4 in[4] = {p[0], p[1], p[2], p[3]};
+        uint4 o[4];
+        if (b == 3) permute32<false, 3>(in, o);
+        else if (b == 4) permute32<false, 4>(in, o);
+        else permute32<false, 8>(in, o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = o[q];
+    }
+}
+
 constexpr int SK = 128;            // K codes per step (one page tile)
-constexpr int LDX = SK + 8;        // padded LDS row of staged tokens (halves)
+constexpr int LDX = SK;            // LDS row of staged tokens (halves): 256 B, no padding
+// 16-byte chunk c of token row n lives at chunk position c ^ (n % 16) of its
+// row, so the 16 lanes reading one chunk of 16 consecutive rows hit 16
+// different bank groups.
+__device__ __forceinline__ int swz(int n, int c) { return n * (LDX / 8) + (c ^ (n & 15)); }
 
 // Steps of codes in flight per wave.
 template <int B>
@@ -186,26 +234,19 @@ __device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i) {
     return o.h[i];
 }
 
-// Token rows of one step: thread t stages token t / 2, codes 64 (t % 2) ..
-// +64 of the step (two 32-code runs).
-template <int MODE>
-__device__ __forceinline__ void load_act(uint4 (&xr)[8], const uint8_t* act_row, int step, int tid) {
-    const uint4* src = reinterpret_cast<const uint4*>(act_row + (int64_t)(step * SK + 64 * (tid & 1)) * 2);
+// Token rows of one step (already fp16 in the codes' K order): thread t
+// copies token t / 2, chunks 8 (t % 2) .. +8 (64 codes) of the step.
+__device__ __forceinline__ void load_act(u32x4 (&xr)[8], const _Float16* act_row, int step, int tid) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(act_row + step * SK + 64 * (tid & 1));
 #pragma unroll
     for (int q = 0; q < 8; ++q) xr[q] = src[q];
 }
 
-template <int MODE, int B>
-__device__ __forceinline__ void store_act(const uint4 (&xr)[8], _Float16* xs, int tid) {
-    uint4* dst = reinterpret_cast<uint4*>(xs + (tid >> 1) * LDX + 64 * (tid & 1));
+__device__ __forceinline__ void store_act(const u32x4 (&xr)[8], _Float16* xs, int tid) {
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
+    const int n = tid >> 1;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint4 in[4] = {xr[4 * h], xr[4 * h + 1], xr[4 * h + 2], xr[4 * h + 3]};
-        uint4 o[4];
-        act_to_f16<MODE, B>(in, o);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[4 * h + q] = o[q];
-    }
+    for (int q = 0; q < 8; ++q) dst[swz(n, 8 * (tid & 1) + q)] = xr[q];
 }
 
 template <int MODE, int B>
@@ -242,9 +283,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     }
     __syncthreads();
     const int my_tok = tok[tid >> 1];
-    const uint8_t* act_row = MODE == 0
-        ? reinterpret_cast<const uint8_t*>(a.x + (int64_t)my_tok * a.d)
-        : reinterpret_cast<const uint8_t*>(a.w.H + (int64_t)my_tok * a.F);
+    const _Float16* act_row = MODE == 0 ? a.xp + (int64_t)bits_index(B) * a.xp_plane + (int64_t)my_tok * a.d
+                                        : a.w.H + (int64_t)my_tok * a.F;
     _Float16* xs[2] = {smem, smem + BN * LDX};
 
     // prologue: codes for steps 0..PD-1 in flight, token rows of step 0 staged
@@ -256,12 +296,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
                 ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(j, S - 1) * TB);
-    // token rows travel two steps ahead: xr[p] holds the step that goes to
-    // LDS at the end of the current step
-    uint4 xr[2][8];
-    load_act<MODE>(xr[0], act_row, 0, tid);
-    store_act<MODE, B>(xr[0], xs[0], tid);
-    load_act<MODE>(xr[1], act_row, min(1, S - 1), tid);
+    // token rows travel two steps ahead: xa holds even steps and xb odd
+    // ones; each goes to LDS at the end of the step before its own
+    u32x4 xa[8], xb[8];
+    load_act(xa, act_row, 0, tid);
+    store_act(xa, xs[0], tid);
+    load_act(xb, act_row, min(1, S - 1), tid);
     __syncthreads();
 
     f32x4 acc[NMAT][2][8];
@@ -272,46 +312,50 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = 0; s0 < S; s0 += PD) {
+    // one step: token rows of step st + 2 into `fill` (which held step st),
+    // codes of step st + PD into ring slot j, then the MFMAs of step st and
+    // the token rows of step st + 1 (`next`) into the other LDS buffer
+    auto step = [&](int st, auto& ring_j, u32x4 (&fill)[8], const u32x4 (&next)[8]) {
+        load_act(fill, act_row, min(st + 2, S - 1), tid);
+        Run<B> cur[NMAT][2];
 #pragma unroll
-        for (int j = 0; j < PD; ++j) {
-            const int st = s0 + j;
-            if (st < S) {
-                // token rows two steps ahead and codes PD steps ahead, unconditionally
-                load_act<MODE>(xr[j & 1], act_row, min(st + 2, S - 1), tid);
-                Run<B> cur[NMAT][2];
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                cur[m][blk] = ring_j[m][blk];
+                ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
+            }
+        // lane (r, g): its run holds codes 32g..32g+31 of the step and MFMA
+        // kc uses codes 32g + 8kc..+8, so the token fragment is the same 8
+        // K-slots of token row 16 jt + r
+        const uint4* xb_lds = reinterpret_cast<const uint4*>(xs[st & 1]);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            half8_t af[NMAT][2];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(cur[m][blk], kc);
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt) {
+                const half8_t bf = *reinterpret_cast<const half8_t*>(xb_lds + swz(16 * jt + r, 4 * g + kc));
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int blk = 0; blk < 2; ++blk) {
-                        cur[m][blk] = ring[j][m][blk];
-                        ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
-                    }
-                // lane (r, g): its run holds codes 32g..32g+31 of the step and
-                // MFMA kc uses codes 32g + 8kc..+8, so the token fragment is the
-                // same 8 K-slots of token row 16 jt + r
-                const _Float16* xb = xs[st & 1] + r * LDX + 32 * g;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    half8_t af[NMAT][2];
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(cur[m][blk], kc);
-#pragma unroll
-                    for (int jt = 0; jt < 8; ++jt) {
-                        const half8_t bf = *reinterpret_cast<const half8_t*>(xb + 16 * jt * LDX + 8 * kc);
-#pragma unroll
-                        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                            for (int blk = 0; blk < 2; ++blk)
-                                acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bf,
-                                                                                         acc[m][blk][jt], 0, 0, 0);
-                    }
-                }
-                if (st + 1 < S) store_act<MODE, B>(xr[(j & 1) ^ 1], xs[(st + 1) & 1], tid);
-                __syncthreads();
+                    for (int blk = 0; blk < 2; ++blk)
+                        acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bf,
+                                                                                 acc[m][blk][jt], 0, 0, 0);
             }
+        }
+        if (st + 1 < S) store_act(next, xs[(st + 1) & 1], tid);
+        __syncthreads();
+    };
+
+    for (int s0 = 0; s0 < S; s0 += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; j += 2) {
+            if (s0 + j < S) step(s0 + j, ring[j], xa, xb);
+            if (s0 + j + 1 < S) step(s0 + j + 1, ring[j + 1], xb, xa);
         }
     }
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
@@ -388,6 +432,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
 
 bool gemm_supported(int d, int F) { return d % BM == 0 && F % BM == 0; }
 
+hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
+    return launch_timed(prep_x_kernel, dim3((unsigned)a.T, 3), dim3(kThreads), 0, s, (hipEvent_t) nullptr,
+                        (hipEvent_t) nullptr, a.x, a.d, a.bits_mask, const_cast<_Float16*>(a.xp), a.xp_plane);
+}
+hipError_t launch_prep_h(const GemmArgs& a, hipStream_t s) {
+    const int blocks_per_expert = (int)((a.P_used / (a.max_act > 0 ? a.max_act : 1) * (a.F / 32) + kThreads - 1) / kThreads);
+    const unsigned gy = (unsigned)(blocks_per_expert < 1 ? 1 : (blocks_per_expert > 64 ? 64 : blocks_per_expert));
+    return launch_timed(prep_h_kernel, dim3((unsigned)a.max_act, gy), dim3(kThreads), 0, s, (hipEvent_t) nullptr,
+                        (hipEvent_t) nullptr, a.w, a.tab, a.F);
+}
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<0>(a, s, t); }
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<1>(a, s, t); }
 

@@ -50,7 +50,7 @@ struct FwdWork {
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, H, O, fwd_end;
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, H, O, xp, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };
@@ -117,10 +117,15 @@ struct GemmArgs {
     DevTable tab;
     FwdWork w;
     const uint16_t* x;   // bf16 [T, d]
-    int d, F, k, max_act;
+    const _Float16* xp;  // [3][max_tokens][d] x as fp16 in the K order of 3-, 4-, 8-bit codes
+    int64_t xp_plane;    // elements per plane of xp
+    int bits_mask;       // bit i: some expert uses bit-width (3, 4, 8)[i]
+    int T, d, F, k, max_act;
     int64_t P_used;      // T * k of this call
 };
 bool gemm_supported(int d, int F);
+hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s);
+hipError_t launch_prep_h(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 

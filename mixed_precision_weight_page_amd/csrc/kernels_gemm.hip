@@ -34,6 +34,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int BM = 128;          // weight rows per tile (per matrix)
 constexpr int BN = kGemmTokens;  // tokens per tile
+constexpr int NJ = BN / 16;      // 16-token blocks per tile
 constexpr uint32_t kMagic = 0x64006400u;
 
 template <int B>
@@ -44,24 +45,25 @@ struct Run {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // One 32-code run at p (lane offset applied): 16 bytes (4-bit), 16 + 16
-// bytes 1 KB apart (8-bit), 12 bytes (3-bit). Non-temporal: codes are read
-// once per workgroup.
+// bytes 1 KB apart (8-bit), 12 bytes (3-bit). Plain loads: the workgroups of
+// the expert's other token tiles read the same runs at about the same time,
+// and those hits in L2 are what keeps the matrix cores fed.
 template <int B>
 __device__ __forceinline__ Run<B> load_run_at(const uint8_t* p) {
     Run<B> r;
     if constexpr (B == 4) {
-        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
         r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
     } else if constexpr (B == 8) {
-        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 1024));
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p + 1024);
         r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
         r.w[4] = v.x; r.w[5] = v.y; r.w[6] = v.z; r.w[7] = v.w;
     } else {
         const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-        r.w[0] = __builtin_nontemporal_load(q);
-        r.w[1] = __builtin_nontemporal_load(q + 1);
-        r.w[2] = __builtin_nontemporal_load(q + 2);
+        r.w[0] = q[0];
+        r.w[1] = q[1];
+        r.w[2] = q[2];
     }
     return r;
 }
@@ -222,7 +224,7 @@ __device__ __forceinline__ int swz(int n, int c) { return n * (LDX / 8) + (c ^ (
 
 // Steps of codes in flight per wave.
 template <int B>
-__device__ __forceinline__ constexpr int gemm_depth() { return B == 8 ? 2 : 4; }  // even
+__device__ __forceinline__ constexpr int gemm_depth() { return 2; }  // even
 
 template <int B>
 __device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i) {
@@ -235,18 +237,20 @@ __device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i) {
 }
 
 // Token rows of one step (already fp16 in the codes' K order): thread t
-// copies token t / 2, chunks 8 (t % 2) .. +8 (64 codes) of the step.
-__device__ __forceinline__ void load_act(u32x4 (&xr)[8], const _Float16* act_row, int step, int tid) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(act_row + step * SK + 64 * (tid & 1));
+// copies chunks 4 (t % 4) .. +4 (32 codes) of token t / 4.
+constexpr int XR = BN * SK * 2 / 16 / kThreads;   // 16-byte chunks per thread and step
+static_assert(XR == 4, "staging assumes 4 chunks per thread");
+__device__ __forceinline__ void load_act(u32x4 (&xr)[XR], const _Float16* act_row, int step, int tid) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(act_row + step * SK + 32 * (tid & 3));
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xr[q] = src[q];
+    for (int q = 0; q < XR; ++q) xr[q] = src[q];
 }
 
-__device__ __forceinline__ void store_act(const u32x4 (&xr)[8], _Float16* xs, int tid) {
+__device__ __forceinline__ void store_act(const u32x4 (&xr)[XR], _Float16* xs, int tid) {
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
-    const int n = tid >> 1;
+    const int n = tid >> 2;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dst[swz(n, 8 * (tid & 1) + q)] = xr[q];
+    for (int q = 0; q < XR; ++q) dst[swz(n, 4 * (tid & 3) + q)] = xr[q];
 }
 
 template <int MODE, int B>
@@ -282,7 +286,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         tok[tid] = MODE == 0 ? a.w.sorted[base + t0 + n] / a.k : base + t0 + n;
     }
     __syncthreads();
-    const int my_tok = tok[tid >> 1];
+    const int my_tok = tok[tid >> 2];
     const _Float16* act_row = MODE == 0 ? a.xp + (int64_t)bits_index(B) * a.xp_plane + (int64_t)my_tok * a.d
                                         : a.w.H + (int64_t)my_tok * a.F;
     _Float16* xs[2] = {smem, smem + BN * LDX};
@@ -298,24 +302,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                 ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(j, S - 1) * TB);
     // token rows travel two steps ahead: xa holds even steps and xb odd
     // ones; each goes to LDS at the end of the step before its own
-    u32x4 xa[8], xb[8];
+    u32x4 xa[XR], xb[XR];
     load_act(xa, act_row, 0, tid);
     store_act(xa, xs[0], tid);
     load_act(xb, act_row, min(1, S - 1), tid);
     __syncthreads();
 
-    f32x4 acc[NMAT][2][8];
+    f32x4 acc[NMAT][2][NJ];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one step: token rows of step st + 2 into `fill` (which held step st),
     // codes of step st + PD into ring slot j, then the MFMAs of step st and
     // the token rows of step st + 1 (`next`) into the other LDS buffer
-    auto step = [&](int st, auto& ring_j, u32x4 (&fill)[8], const u32x4 (&next)[8]) {
+    auto step = [&](int st, auto& ring_j, u32x4 (&fill)[XR], const u32x4 (&next)[XR]) {
         load_act(fill, act_row, min(st + 2, S - 1), tid);
         Run<B> cur[NMAT][2];
 #pragma unroll
@@ -328,7 +332,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         // lane (r, g): its run holds codes 32g..32g+31 of the step and MFMA
         // kc uses codes 32g + 8kc..+8, so the token fragment is the same 8
         // K-slots of token row 16 jt + r
-        const uint4* xb_lds = reinterpret_cast<const uint4*>(xs[st & 1]);
+        const u32x4* xb_lds = reinterpret_cast<const u32x4*>(xs[st & 1]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             half8_t af[NMAT][2];
@@ -337,8 +341,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(cur[m][blk], kc);
 #pragma unroll
-            for (int jt = 0; jt < 8; ++jt) {
-                const half8_t bf = *reinterpret_cast<const half8_t*>(xb_lds + swz(16 * jt + r, 4 * g + kc));
+            for (int jt = 0; jt < NJ; ++jt) {
+                const half8_t bf = __builtin_bit_cast(half8_t, xb_lds[swz(16 * jt + r, 4 * g + kc)]);
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -351,16 +355,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         __syncthreads();
     };
 
-    for (int s0 = 0; s0 < S; s0 += PD) {
+    // whole ring cycles without guards (the prefetch stays in flight across
+    // iterations), then the last S % PD steps
+    int s0 = 0;
+    for (; s0 + PD <= S; s0 += PD) {
 #pragma unroll
         for (int j = 0; j < PD; j += 2) {
-            if (s0 + j < S) step(s0 + j, ring[j], xa, xb);
-            if (s0 + j + 1 < S) step(s0 + j + 1, ring[j + 1], xb, xa);
+            step(s0 + j, ring[j], xa, xb);
+            step(s0 + j + 1, ring[j + 1], xb, xa);
         }
+    }
+#pragma unroll
+    for (int j = 0; j < PD; j += 2) {
+        if (s0 + j < S) step(s0 + j, ring[j], xa, xb);
+        if (s0 + j + 1 < S) step(s0 + j + 1, ring[j + 1], xb, xa);
     }
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
+    for (int jt = 0; jt < NJ; ++jt) {
         const int n = 16 * jt + r;
         if (n >= nt) continue;
         const int pos = base + t0 + n;
@@ -392,7 +404,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, int row_tiles, int ntiles) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_tiles, int ntiles) {
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
     __shared__ int tok[BN];
     // XCD swizzle: the eighth of the tile range that this workgroup's XCD walks

@@ -18,7 +18,7 @@ constexpr int kRowAlign = 128;         // codes per row are a multiple of this
 constexpr int kPageAlign = 256;        // page offsets and sizes
 constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
 constexpr int kFusedMaxPairs = 4096;   // (token, slot) pairs ranked by one workgroup
-constexpr int kGemmTokens = 128;       // tokens per tile of the large-batch kernels
+constexpr int kGemmTokens = 64;        // tokens per tile of the large-batch kernels
 constexpr int kGemmMinTokens = 64;     // mean tokens per active expert for those kernels
 
 // supported bit-widths, in loss-table order

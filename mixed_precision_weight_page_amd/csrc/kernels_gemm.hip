@@ -317,18 +317,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
             for (int j = 0; j < NJ; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one step: token rows of step st + 2 into `fill` (which held step st),
-    // codes of step st + PD into ring slot j, then the MFMAs of step st and
-    // the token rows of step st + 1 (`next`) into the other LDS buffer
+    // the MFMAs of step st from ring slot j, whose codes are reloaded with
+    // step st + PD as soon as their last fragment is in registers (old and
+    // new never live together, so the slot keeps its registers across the
+    // loop and nothing waits on the load), then the token rows of step
+    // st + 1 (`next`) into the other LDS buffer
     auto step = [&](int st, auto& ring_j, u32x4 (&fill)[XR], const u32x4 (&next)[XR]) {
         load_act(fill, act_row, min(st + 2, S - 1), tid);
-        Run<B> cur[NMAT][2];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                cur[m][blk] = ring_j[m][blk];
-                ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
-            }
         // lane (r, g): its run holds codes 32g..32g+31 of the step and MFMA
         // kc uses codes 32g + 8kc..+8, so the token fragment is the same 8
         // K-slots of token row 16 jt + r
@@ -339,7 +334,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(cur[m][blk], kc);
+                for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(ring_j[m][blk], kc);
+            if (kc == 3) {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int blk = 0; blk < 2; ++blk)
+                        ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
+            }
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt) {
                 const half8_t bf = __builtin_bit_cast(half8_t, xb_lds[swz(16 * jt + r, 4 * g + kc)]);

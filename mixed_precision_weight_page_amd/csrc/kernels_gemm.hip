@@ -80,25 +80,48 @@ __device__ __forceinline__ uint4 sub_bias(uint32_t a, uint32_t b, uint32_t c, ui
     return x.v;
 }
 
+// A 32-bit constant held in a VGPR. A VOP3 instruction on this target can
+// read at most one SGPR or literal, so with the masks and the exponent
+// pattern in VGPRs each (w & mask) | magic is one v_and_or_b32 instead of a
+// v_and plus a v_or.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+struct DeqConst {
+    uint32_t magic;   // 0x64006400: fp16 1024 in both halves
+    uint32_t m4;      // 0x000f000f
+    uint32_t e8;      // 0x64646464: exponent byte for v_perm_b32
+};
+
+__device__ __forceinline__ DeqConst deq_const() {
+    return DeqConst{vgpr_const(kMagic), vgpr_const(0x000f000fu), vgpr_const(0x64646464u)};
+}
+
 // The 32 codes of a run as exact fp16 q, in the K-slot order of the staging
 // permutation (4 x 16 bytes).
 template <int B>
-__device__ __forceinline__ void run_to_f16(const Run<B>& r, uint4 out[4]) {
+__device__ __forceinline__ void run_to_f16(const Run<B>& r, uint4 out[4], const DeqConst& c) {
     if constexpr (B == 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t w = r.w[i];
-            out[i] = sub_bias((w & 0x000f000fu) | kMagic, ((w >> 4) & 0x000f000fu) | kMagic,
-                              ((w >> 8) & 0x000f000fu) | kMagic, ((w >> 12) & 0x000f000fu) | kMagic,
+            out[i] = sub_bias((w & c.m4) | c.magic, ((w >> 4) & c.m4) | c.magic,
+                              ((w >> 8) & c.m4) | c.magic, ((w >> 12) & c.m4) | c.magic,
                               (_Float16)1032.0f);
         }
     } else if constexpr (B == 8) {
+        // bytes (b0, 0x64, b2, 0x64) and (b1, 0x64, b3, 0x64) of each word:
+        // selector bytes 0-3 pick from the word, 4 from the exponent pattern
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t w0 = r.w[2 * i], w1 = r.w[2 * i + 1];
-            out[i] = sub_bias((w0 & 0x00ff00ffu) | kMagic, ((w0 >> 8) & 0x00ff00ffu) | kMagic,
-                              (w1 & 0x00ff00ffu) | kMagic, ((w1 >> 8) & 0x00ff00ffu) | kMagic,
-                              (_Float16)1152.0f);
+            out[i] = sub_bias(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u),
+                              __builtin_amdgcn_perm(c.e8, w0, 0x04030401u),
+                              __builtin_amdgcn_perm(c.e8, w1, 0x04020400u),
+                              __builtin_amdgcn_perm(c.e8, w1, 0x04030401u), (_Float16)1152.0f);
         }
     } else {
         const uint32_t* w = r.w;
@@ -227,12 +250,12 @@ template <int B>
 __device__ __forceinline__ constexpr int gemm_depth() { return 2; }  // even
 
 template <int B>
-__device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i) {
+__device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i, const DeqConst& c) {
     union {
         uint4 v[4];
         half8_t h[4];
     } o;
-    run_to_f16<B>(r, o.v);   // the compiler keeps only fragment i alive
+    run_to_f16<B>(r, o.v, c);   // the compiler keeps only fragment i alive
     return o.h[i];
 }
 
@@ -290,6 +313,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     const _Float16* act_row = MODE == 0 ? a.xp + (int64_t)bits_index(B) * a.xp_plane + (int64_t)my_tok * a.d
                                         : a.w.H + (int64_t)my_tok * a.F;
     _Float16* xs[2] = {smem, smem + BN * LDX};
+    const DeqConst dc = deq_const();
 
     // prologue: codes for steps 0..PD-1 in flight, token rows of step 0 staged
     Run<B> ring[PD][NMAT][2];
@@ -300,12 +324,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
                 ring[j][m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(j, S - 1) * TB);
-    // token rows travel two steps ahead: xa holds even steps and xb odd
-    // ones; each goes to LDS at the end of the step before its own
-    u32x4 xa[XR], xb[XR];
-    load_act(xa, act_row, 0, tid);
-    store_act(xa, xs[0], tid);
-    load_act(xb, act_row, min(1, S - 1), tid);
+    // token rows travel one step ahead through registers
+    u32x4 xr[XR];
+    load_act(xr, act_row, 0, tid);
+    store_act(xr, xs[0], tid);
     __syncthreads();
 
     f32x4 acc[NMAT][2][NJ];
@@ -316,62 +338,69 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // one step: token rows of step st + 2 into `fill` (which held step st),
-    // the MFMAs of step st from ring slot j, whose codes are reloaded with
+    // one step: token rows of step st + 1 into registers; the MFMAs of step
+    // st, with the token fragments of K-group kc + 1 read from LDS while
+    // those of kc are in use, and the codes of ring slot j, reloaded with
     // step st + PD as soon as their last fragment is in registers (old and
     // new never live together, so the slot keeps its registers across the
-    // loop and nothing waits on the load), then the token rows of step
-    // st + 1 (`next`) into the other LDS buffer
-    auto step = [&](int st, auto& ring_j, u32x4 (&fill)[XR], const u32x4 (&next)[XR]) {
-        load_act(fill, act_row, min(st + 2, S - 1), tid);
+    // loop and nothing waits on the load); then the token rows of step
+    // st + 1 into the other LDS buffer
+    auto step = [&](int st, auto& ring_j, const _Float16* cur, _Float16* nxt) {
+        load_act(xr, act_row, min(st + 1, S - 1), tid);
+        // keep the loads here: the scheduler would otherwise sink them to
+        // their LDS stores at the end of the step and expose their latency
+        __builtin_amdgcn_sched_barrier(0);
         // lane (r, g): its run holds codes 32g..32g+31 of the step and MFMA
         // kc uses codes 32g + 8kc..+8, so the token fragment is the same 8
         // K-slots of token row 16 jt + r
-        const u32x4* xb_lds = reinterpret_cast<const u32x4*>(xs[st & 1]);
+        const u32x4* xl = reinterpret_cast<const u32x4*>(cur);
+        half8_t bq[2][NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) bq[0][jt] = __builtin_bit_cast(half8_t, xl[swz(16 * jt + r, 4 * g)]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
+            if (kc < 3) {
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    bq[(kc + 1) & 1][jt] = __builtin_bit_cast(half8_t, xl[swz(16 * jt + r, 4 * g + kc + 1)]);
+            }
             half8_t af[NMAT][2];
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(ring_j[m][blk], kc);
+                for (int blk = 0; blk < 2; ++blk) af[m][blk] = frag_of<B>(ring_j[m][blk], kc, dc);
             if (kc == 3) {
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                     for (int blk = 0; blk < 2; ++blk)
                         ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
-                const half8_t bf = __builtin_bit_cast(half8_t, xb_lds[swz(16 * jt + r, 4 * g + kc)]);
+            for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                     for (int blk = 0; blk < 2; ++blk)
-                        acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bf,
+                        acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bq[kc & 1][jt],
                                                                                  acc[m][blk][jt], 0, 0, 0);
-            }
         }
-        if (st + 1 < S) store_act(next, xs[(st + 1) & 1], tid);
+        if (st + 1 < S) store_act(xr, nxt, tid);
         __syncthreads();
     };
 
     // whole ring cycles without guards (the prefetch stays in flight across
-    // iterations), then the last S % PD steps
+    // iterations), then the last S % PD steps; PD is even, so step s0 + j
+    // reads LDS buffer j % 2
     int s0 = 0;
     for (; s0 + PD <= S; s0 += PD) {
 #pragma unroll
-        for (int j = 0; j < PD; j += 2) {
-            step(s0 + j, ring[j], xa, xb);
-            step(s0 + j + 1, ring[j + 1], xb, xa);
-        }
+        for (int j = 0; j < PD; ++j) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     }
 #pragma unroll
-    for (int j = 0; j < PD; j += 2) {
-        if (s0 + j < S) step(s0 + j, ring[j], xa, xb);
-        if (s0 + j + 1 < S) step(s0 + j + 1, ring[j + 1], xb, xa);
-    }
+    for (int j = 0; j < PD; ++j)
+        if (s0 + j < S) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {

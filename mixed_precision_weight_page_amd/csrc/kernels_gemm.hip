@@ -32,7 +32,11 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 128;          // weight rows per tile (per matrix)
+// Weight rows per tile: 128 of W1 and of W3 (MODE 0), 256 of W2 (MODE 1).
+// Either way a wave streams four 16-row blocks, so each token fragment read
+// from LDS feeds four MFMAs.
+template <int MODE>
+constexpr int tile_rows() { return MODE == 0 ? 128 : 256; }
 constexpr int BN = kGemmTokens;  // tokens per tile
 constexpr int NJ = BN / 16;      // 16-token blocks per tile
 constexpr uint32_t kMagic = 0x64006400u;
@@ -279,7 +283,7 @@ __device__ __forceinline__ void store_act(const u32x4 (&xr)[XR], _Float16* xs, i
 template <int MODE, int B>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
                                           int* tok) {
-    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    constexpr int NMAT = 2;   // stream pairs: W1 / W3 (MODE 0), two 32-row halves of W2 (MODE 1)
     constexpr int PD = gemm_depth<B>();
     constexpr int TB = 256 * B;                  // bytes of one 16-row x 128-code tile
     const int K = MODE == 0 ? a.d : a.F;
@@ -295,14 +299,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     const uint8_t* page = a.pool + a.tab.off[e];
     const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
     const int loff = (B == 3 ? 12 : 16) * lane;
-    // this wave's code streams: matrix m, row block rb0 + blk, all K steps
-    const int rb0 = rt * (BM / 16) + 2 * wave;
+    // this wave's four code streams (m, blk), all K steps: row block
+    // 8 rt + 2 wave + blk of matrix m (W1, W3), or row block
+    // 16 rt + 4 wave + 2 m + blk of W2
     const uint8_t* ap[NMAT][2];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-            ap[m][blk] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)(rb0 + blk) * S * TB + loff;
+        for (int blk = 0; blk < 2; ++blk) {
+            const int rb = MODE == 0 ? 8 * rt + 2 * wave + blk : 16 * rt + 4 * wave + 2 * m + blk;
+            ap[m][blk] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)rb * S * TB + loff;
+        }
 
     if (tid < BN) {
         const int n = tid < nt ? tid : 0;   // past nt: repeat the first row, outputs dropped
@@ -409,8 +416,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         const int pos = base + t0 + n;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const int row = rt * BM + 32 * wave + 16 * blk + 4 * g;
             if constexpr (MODE == 0) {
+                const int row = rt * tile_rows<0>() + 32 * wave + 16 * blk + 4 * g;
                 union {
                     uint2 u;
                     _Float16 h[4];
@@ -423,12 +430,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                 }
                 *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + row) = hv.u;
             } else {
-                float4 o;
-                o.x = s * acc[0][blk][jt][0];
-                o.y = s * acc[0][blk][jt][1];
-                o.z = s * acc[0][blk][jt][2];
-                o.w = s * acc[0][blk][jt][3];
-                *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + row) = o;
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const int row = rt * tile_rows<1>() + 64 * wave + 32 * m + 16 * blk + 4 * g;
+                    float4 o;
+                    o.x = s * acc[m][blk][jt][0];
+                    o.y = s * acc[m][blk][jt][1];
+                    o.z = s * acc[m][blk][jt][2];
+                    o.w = s * acc[m][blk][jt][3];
+                    *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + row) = o;
+                }
             }
         }
     }
@@ -459,9 +470,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
 
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
-    constexpr int NMAT = MODE == 0 ? 2 : 1;
     const int rows = MODE == 0 ? a.F : a.d;
-    const int row_tiles = rows / BM;
+    const int row_tiles = rows / tile_rows<MODE>();
     // token tiles over all experts: at most ceil(P / BN) + (active experts)
     const int64_t tt_max = (a.P_used + BN - 1) / BN + a.max_act;
     int64_t ntiles = tt_max * row_tiles;
@@ -473,7 +483,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
 
 }  // namespace
 
-bool gemm_supported(int d, int F) { return d % BM == 0 && F % BM == 0; }
+bool gemm_supported(int d, int F) { return d % tile_rows<1>() == 0 && F % tile_rows<0>() == 0; }
 
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
     return launch_timed(prep_x_kernel, dim3((unsigned)a.T, 3), dim3(kThreads), 0, s, (hipEvent_t) nullptr,

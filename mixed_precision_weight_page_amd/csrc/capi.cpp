@@ -583,7 +583,6 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         for (int e = 0; e < c->E; ++e) ga.bits_mask |= 1 << bits_index(c->table[e].bits);
         HIP_TRY(c, launch_prep_x(ga, s));
         HIP_TRY(c, launch_gate_up_gemm(ga, s, tm[1]));
-        HIP_TRY(c, launch_prep_h(ga, s));
         HIP_TRY(c, launch_down_gemm(ga, s, tm[2]));
         HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, 1, y, s, tm[3]));
     } else {

@@ -164,6 +164,17 @@ __device__ __forceinline__ constexpr int perm_slot(int s) {
     }
 }
 
+// K-slot that code c (within a 32-code run) takes in the K order of B-bit
+// codes: the inverse of perm_slot.
+template <int B>
+__device__ __forceinline__ int slot_of(int c) {
+    int slot = 0;
+#pragma unroll
+    for (int s = 0; s < 32; ++s)
+        if (perm_slot<B>(s) == c) slot = s;
+    return slot;
+}
+
 // 32 consecutive activations (bf16 when SRC_BF16, else fp16) as fp16 in the
 // K-slot order of B-bit codes.
 template <bool SRC_BF16, int B>
@@ -216,29 +227,6 @@ __global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int
         uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + t * d + 32 * grp);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = o[q];
-    }
-}
-
-// SwiGLU rows for the down tiles: H[pos] permuted in place into the K order
-// of its expert's codes. grid (active slot, row blocks of 64 pairs).
-__global__ __launch_bounds__(kThreads) void prep_h_kernel(FwdWork w, DevTable tab, int F) {
-    const int ai = blockIdx.x;
-    if (ai >= w.n_act[0]) return;
-    const int e = w.act[ai];
-    const int b = tab.bits[e];
-    const int cnt = w.cnt[e], base = w.off[e];
-    const int ngrp = F / 32;
-    // each (row, group) is owned by one thread: read, permute, write back
-    for (int idx = blockIdx.y * kThreads + threadIdx.x; idx < cnt * ngrp; idx += gridDim.y * kThreads) {
-        const int row = idx / ngrp, grp = idx - row * ngrp;
-        uint4* p = reinterpret_cast<uint4*>(w.H + (int64_t)(base + row) * F + 32 * grp);
-        uint4 in[4] = {p[0], p[1], p[2], p[3]};
-        uint4 o[4];
-        if (b == 3) permute32<false, 3>(in, o);
-        else if (b == 4) permute32<false, 4>(in, o);
-        else permute32<false, 8>(in, o);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) p[q] = o[q];
     }
 }
 
@@ -417,18 +405,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             if constexpr (MODE == 0) {
-                const int row = rt * tile_rows<0>() + 32 * wave + 16 * blk + 4 * g;
-                union {
-                    uint2 u;
-                    _Float16 h[4];
-                } hv;
+                // rows 32 c0 + 16 blk + 4 g + v of H, stored at the K-slots
+                // the down projection's B-bit codes expect
+                const int c0 = (rt * tile_rows<0>() + 32 * wave) / 32;
+                _Float16* hrow = a.w.H + (int64_t)pos * a.F + 32 * c0;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float av = s * acc[0][blk][jt][v];
                     const float cv = s * acc[1][blk][jt][v];
-                    hv.h[v] = (_Float16)(av / (1.0f + expf(-av)) * cv);
+                    hrow[slot_of<B>(16 * blk + 4 * g + v)] = (_Float16)(av / (1.0f + expf(-av)) * cv);
                 }
-                *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + row) = hv.u;
             } else {
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
@@ -488,12 +474,6 @@ bool gemm_supported(int d, int F) { return d % tile_rows<1>() == 0 && F % tile_r
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
     return launch_timed(prep_x_kernel, dim3((unsigned)a.T, 3), dim3(kThreads), 0, s, (hipEvent_t) nullptr,
                         (hipEvent_t) nullptr, a.x, a.d, a.bits_mask, const_cast<_Float16*>(a.xp), a.xp_plane);
-}
-hipError_t launch_prep_h(const GemmArgs& a, hipStream_t s) {
-    const int blocks_per_expert = (int)((a.P_used / (a.max_act > 0 ? a.max_act : 1) * (a.F / 32) + kThreads - 1) / kThreads);
-    const unsigned gy = (unsigned)(blocks_per_expert < 1 ? 1 : (blocks_per_expert > 64 ? 64 : blocks_per_expert));
-    return launch_timed(prep_h_kernel, dim3((unsigned)a.max_act, gy), dim3(kThreads), 0, s, (hipEvent_t) nullptr,
-                        (hipEvent_t) nullptr, a.w, a.tab, a.F);
 }
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<0>(a, s, t); }
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<1>(a, s, t); }

@@ -125,7 +125,6 @@ struct GemmArgs {
 };
 bool gemm_supported(int d, int F);
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s);
-hipError_t launch_prep_h(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 

@@ -146,6 +146,8 @@ FwdWork fwd_work(pw_ctx* c) {
     w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
     w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
     w.tt_off = reinterpret_cast<int32_t*>(b + c->lay.tt_off);
+    w.ccnt = reinterpret_cast<int32_t*>(b + c->lay.ccnt);
+    w.cpre = reinterpret_cast<int32_t*>(b + c->lay.cpre);
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
     w.O = reinterpret_cast<float*>(b + c->lay.O);
     return w;
@@ -349,6 +351,9 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.act = take(4 * (uint64_t)E);
     L.n_act = take(4);
     L.tt_off = take(4 * (uint64_t)(E + 1));
+    const uint64_t chunks = ((uint64_t)max_tokens + kRankChunk - 1) / kRankChunk;
+    L.ccnt = take(4 * (uint64_t)E * chunks);
+    L.cpre = take(4 * (uint64_t)E * chunks);
     L.H = take(2 * P * (uint64_t)F);
     L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
     L.xp = take(2 * 3 * (uint64_t)max_tokens * (uint64_t)d);

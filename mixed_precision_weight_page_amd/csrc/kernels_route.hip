@@ -11,8 +11,9 @@
 //
 // Up to 16 tokens: one workgroup does everything. Up to kFusedMaxPairs
 // pairs: a router kernel (one wave per token, many workgroups), then one
-// workgroup ranks and offsets. Larger batches: router, per-expert rank,
-// finalize. Kernel boundaries carry the results between workgroups (a
+// workgroup ranks and offsets. Larger batches: router; ranks per expert and
+// chunk of kRankChunk tokens; counts, chunk prefixes and offsets in one
+// workgroup; pair positions over many workgroups. Kernel boundaries carry the results between workgroups (a
 // device-scope handshake inside one kernel would have to write back and
 // invalidate the per-XCD L2 caches). No host synchronisation.
 #include <hip/hip_runtime.h>
@@ -117,12 +118,11 @@ __device__ __forceinline__ T block_scan(T v, T* s_wave, T* total) {
     return v + (wave > 0 ? s_wave[wave - 1] : T(0));
 }
 
-// Offsets, bit-ordered active list, and pair positions. cnt_of(e) gives the
-// count of expert e, rank_of(p) the rank of pair p.
-template <class CntF, class RankF, class IdF>
-__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, const int32_t* bits,
-                                         CntF cnt_of, RankF rank_of, IdF id_of) {
-    __shared__ int s_off[kMaxExperts];
+// Offsets, bit-ordered active list and token tiles; cnt_of(e) gives the
+// count of expert e. Leaves the offsets in s_off.
+template <class CntF>
+__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const int32_t* bits,
+                                                 CntF cnt_of, int* s_off) {
     __shared__ int s_wave_i[kWaves];
     __shared__ long long s_wave_l[kWaves];
     const int tid = threadIdx.x;
@@ -142,19 +142,15 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
     const long long linc = block_scan<long long>(flag, s_wave_l, &ltot);
     const int n8 = (int)(ltot & 0x1fffff), n4 = (int)((ltot >> 21) & 0x1fffff),
               n3 = (int)((ltot >> 42) & 0x1fffff);
-    if (flag) {
-        const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
-        const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
-        w.act[base + before] = tid;
-    }
-    if (tid == 0) w.n_act[0] = n8 + n4 + n3;
     // token tiles of the large-batch kernels, in active-list order
     __shared__ int s_slot_cnt[kMaxExperts];
     if (flag) {
         const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
         const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
+        w.act[base + before] = tid;
         s_slot_cnt[base + before] = c;
     }
+    if (tid == 0) w.n_act[0] = n8 + n4 + n3;
     __syncthreads();
     const int na = n8 + n4 + n3;
     const int ntt = tid < na ? (s_slot_cnt[tid] + kGemmTokens - 1) / kGemmTokens : 0;
@@ -163,8 +159,17 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
     if (tid < na) w.tt_off[tid] = tinc - ntt;
     if (tid == 0) w.tt_off[na] = ttot;
     __syncthreads();
+}
+
+// Offsets and pair positions in one workgroup; rank_of(p) gives the rank of
+// pair p, id_of(p) its expert.
+template <class CntF, class RankF, class IdF>
+__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, const int32_t* bits,
+                                         CntF cnt_of, RankF rank_of, IdF id_of) {
+    __shared__ int s_off[kMaxExperts];
+    finalize_offsets(E, w, bits, cnt_of, s_off);
     const int P = T * k;
-    for (int p = tid; p < P; p += kBlock) {
+    for (int p = threadIdx.x; p < P; p += kBlock) {
         const int e = id_of(p);
         const int pos = s_off[e] + rank_of(p);
         w.pos[p] = pos;
@@ -233,16 +238,18 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
     if (t < a.T) route_token(a, w, t, nullptr);
 }
 
-// grid E, 256 threads: rank of expert e's pairs in token order.
-__global__ __launch_bounds__(256) void rank_kernel(int T, int k, FwdWork w) {
-    const int e = blockIdx.x;
+// grid (E, C), 256 threads: rank of expert e's pairs in token order among
+// the tokens of chunk c, and their count.
+__global__ __launch_bounds__(256) void rank_kernel(int T, int k, int C, FwdWork w) {
+    const int e = blockIdx.x, c = blockIdx.y;
     __shared__ int wave_tot[4];
     int running = 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t0 = 0; t0 < T; t0 += 256) {
+    const int t_end = min(T, (c + 1) * kRankChunk);
+    for (int t0 = c * kRankChunk; t0 < t_end; t0 += 256) {
         const int t = t0 + threadIdx.x;
         int slot = -1;
-        if (t < T)
+        if (t < t_end)
             for (int j = 0; j < k; ++j)
                 if (w.ids[(int64_t)t * k + j] == e) slot = j;
         const uint64_t m = __ballot(slot >= 0);
@@ -255,13 +262,36 @@ __global__ __launch_bounds__(256) void rank_kernel(int T, int k, FwdWork w) {
         if (slot >= 0) w.rank[(int64_t)t * k + slot] = base + before;
         running += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
     }
-    if (threadIdx.x == 0) w.cnt[e] = running;
+    if (threadIdx.x == 0) w.ccnt[e * C + c] = running;
 }
 
-__global__ __launch_bounds__(kBlock) void finalize_kernel(int T, int E, int k, FwdWork w,
-                                                          const int32_t* bits) {
-    finalize(T, E, k, w, bits, [&](int e) { return w.cnt[e]; },
-             [&](int p) { return w.rank[p]; }, [&](int p) { return w.ids[p]; });
+// One workgroup: per-expert counts and chunk prefixes, then offsets, the
+// active list and the token tiles.
+__global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, FwdWork w, const int32_t* bits) {
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += kBlock) {
+        int run = 0;
+        for (int c = 0; c < C; ++c) {
+            w.cpre[e * C + c] = run;
+            run += w.ccnt[e * C + c];
+        }
+        s_cnt[e] = run;
+        w.cnt[e] = run;
+    }
+    __syncthreads();
+    finalize_offsets(E, w, bits, [&](int e) { return s_cnt[e]; }, s_off);
+}
+
+// grid ceil(P / 256): position of every pair in expert-sorted order.
+__global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWork w) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= P) return;
+    const int e = w.ids[p];
+    const int c = (p / k) / kRankChunk;
+    const int pos = w.off[e] + w.cpre[e * C + c] + w.rank[p];
+    w.pos[p] = pos;
+    w.sorted[pos] = p;
 }
 
 }  // namespace
@@ -276,9 +306,13 @@ hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bit
     if (a.T * a.k <= kFusedMaxPairs)
         return launch_timed(group_small_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k,
                             w, bits);
-    err = launch_timed(rank_kernel, dim3(a.E), dim3(256), 0, s, none, none, a.T, a.k, w);
+    const int C = (a.T + kRankChunk - 1) / kRankChunk;
+    err = launch_timed(rank_kernel, dim3(a.E, C), dim3(256), 0, s, none, none, a.T, a.k, C, w);
     if (err != hipSuccess) return err;
-    return launch_timed(finalize_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k, w, bits);
+    err = launch_timed(offsets_kernel, dim3(1), dim3(kBlock), 0, s, none, none, a.E, C, w, bits);
+    if (err != hipSuccess) return err;
+    const int P = a.T * a.k;
+    return launch_timed(scatter_kernel, dim3((P + 255) / 256), dim3(256), 0, s, none, t.stop, P, a.k, C, w);
 }
 
 }  // namespace pw

@@ -18,6 +18,7 @@ constexpr int kRowAlign = 128;         // codes per row are a multiple of this
 constexpr int kPageAlign = 256;        // page offsets and sizes
 constexpr int64_t kStatChunk = 16384;  // weights per block in the stats kernels
 constexpr int kFusedMaxPairs = 4096;   // (token, slot) pairs ranked by one workgroup
+constexpr int kRankChunk = 1024;      // tokens per ranking workgroup of the large-batch router
 constexpr int kGemmTokens = 64;        // tokens per tile of the large-batch kernels
 constexpr int kGemmMinTokens = 64;     // mean tokens per active expert for those kernels
 
@@ -45,12 +46,14 @@ struct FwdWork {
     int32_t* act;      // [E] experts with cnt > 0, ascending
     int32_t* n_act;    // [1]
     int32_t* tt_off;   // [E+1] prefix over the active list of ceil(cnt / kGemmTokens)
+    int32_t* ccnt;     // [E, C] pairs of expert e among the tokens of chunk c (kRankChunk tokens)
+    int32_t* cpre;     // [E, C] exclusive prefix of ccnt over the chunks
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
     float* O;          // [nsplit, P, d] down-projection partials per sorted pair (scaled by s_e)
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, H, O, xp, fwd_end;
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, ccnt, cpre, H, O, xp, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };

@@ -44,9 +44,10 @@ def test_tiny_pages_and_forward():
 
 def test_router_matches_oracle():
     # one-workgroup path (T <= 16), router + one-workgroup grouping, and the
-    # three-kernel path (more than 4096 pairs)
+    # multi-workgroup path (more than 4096 pairs; 2500 tokens = three ranking
+    # chunks of 1024, the last one ragged)
     for wl, T in ((TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300),
-                  (SMALL_FINE, 700)):
+                  (SMALL_FINE, 700), (SMALL_FINE, 2500)):
         masters = tuple(torch.zeros(1) for _ in range(3))
         from mixed_precision_weight_page_amd import PagedMoELayer
         layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=T)
@@ -238,11 +239,12 @@ def test_mostly_zero_codes_keep_precision():
     assert norm_err < 1e-3
 
 
-@pytest.mark.parametrize("T", [600, 257])
+@pytest.mark.parametrize("T", [600, 257, 2100])
 def test_large_batch_matrix_core_path(T):
     """Batches with many tokens per expert take the tiled matrix-core
-    kernels (128 tokens x 128 rows per workgroup): ragged last token tile,
-    3/4/8-bit experts, and an expert left without tokens."""
+    kernels (64 tokens x 128 or 256 rows per workgroup): ragged last token
+    tile, 3/4/8-bit experts, an expert left without tokens, and (2100 tokens)
+    a router that ranks pairs over several chunks of 1024 tokens."""
     wl = synth.WORKLOADS["tiny"].scaled(name="gemm_path", E=8, d=512, F=384, k=2, T=T,
                                         bits=(8, 3, 4, 4, 3, 8, 4, 3))
     masters = synth.expert_weights(wl)

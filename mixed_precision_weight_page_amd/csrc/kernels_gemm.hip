@@ -268,6 +268,21 @@ __device__ __forceinline__ void store_act(const u32x4 (&xr)[XR], _Float16* xs, i
     for (int q = 0; q < XR; ++q) dst[swz(n, 4 * (tid & 3) + q)] = xr[q];
 }
 
+// Scheduling groups for one step (64 MFMAs, 16 LDS reads, 16 fragments of
+// dequantization): masks 0x8 MFMA, 0x2 VALU, 0x100 LDS read.
+template <int B>
+__device__ __forceinline__ void sched_step() {
+    constexpr int kValuPerMfma = B == 8 ? 2 : 3;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x2, B == 8 ? 32 : 44, 0);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x2, kValuPerMfma, 0);
+        if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
+
 template <int MODE, int B>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
                                           int* tok) {
@@ -370,7 +385,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 #pragma unroll
                     for (int blk = 0; blk < 2; ++blk)
                         ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
-                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
@@ -381,6 +395,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                         acc[m][blk][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m][blk], bq[kc & 1][jt],
                                                                                  acc[m][blk][jt], 0, 0, 0);
         }
+        // issue order for the step: the first K group's token fragments and
+        // codes, then each MFMA followed by a few VALU instructions (the next
+        // groups' dequantization) and, every fourth MFMA, one LDS read
+        sched_step<B>();
         if (st + 1 < S) store_act(xr, nxt, tid);
         __syncthreads();
     };

@@ -54,11 +54,14 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources of the decode gate/up kernel (the roofline kernel)."""
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources of the workload's gate/up kernel (the roofline
+    kernel): the matrix-core kernels for prefill, the streaming kernels for
+    the decode workloads."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
-    for f in ("kernels_ffn.hip", "pw_internal.h"):
+    src = "kernels_gemm.hip" if workload == "prefill" else "kernels_ffn.hip"
+    for f in (src, "pw_internal.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -72,7 +75,7 @@ def traffic_from_profiles(workload: str, T: int):
     text = open(path).read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    if not m or not t or m.group(1) != kernel_source_hash(workload):
         return None
     return float(t.group(1))
 

@@ -4,21 +4,24 @@
 // dequantized on the fly; Eq. 2: W = s_e q). SwiGLU as in the decode path:
 // h = silu(W1 x) * (W3 x) (MODE 0), o = W2 h (MODE 1).
 //
-// Workgroup tile: 128 weight rows (of W1 and W3 for MODE 0) x 128 tokens of
-// one expert. Each of the four waves owns 32 rows (two 16-row blocks of the
-// page's tiles) for all 128 tokens and streams its codes straight from the
-// page into registers, prefetched several 128-code steps ahead, turning them
-// into exact fp16 integers q in registers (no LDS for weights, each code read
-// once per workgroup). The 128 token rows go through double-buffered LDS, one
-// 128-code step at a time, as fp16 in the same per-32 K permutation as the
-// codes unpack, so each MFMA operand of a lane is one 16-byte read.
-// Per step and wave: 4 K-groups x (2 blocks x matrices) x 8 token blocks of
+// Workgroup tile: 64 tokens of one expert x 128 rows of W1 and of W3
+// (MODE 0) or 256 rows of W2 (MODE 1); two workgroups per CU, so each SIMD
+// interleaves two waves. Each of the four waves streams four 16-row blocks
+// of the page's tiles straight from the page into registers (a two-step
+// ring, each slot reloaded as soon as its last fragment is dequantized) and
+// turns them into exact fp16 integers q in registers: no LDS for weights,
+// each code read once per workgroup. The token rows (fp16, in the same
+// per-32 K permutation as the codes unpack, prepared once per forward) go
+// through double-buffered LDS one 128-code step at a time, one step ahead
+// in registers; each lane's MFMA operand is one 16-byte LDS read, and the
+// next K group's operands are read while the current ones are in use.
+// Per step and wave: 4 K groups x 4 code streams x 4 token blocks of
 // v_mfma_f32_16x16x32_f16, fp32 accumulate.
 //
-// Tile order: expert (in the active list, 8-bit first), token tile, row
+// Tile order: expert (in the active list, 8-bit first), row tile, token
 // tile; workgroup b runs tile (b % 8) * N/8 + b / 8, so each XCD (which
 // receives every eighth workgroup) walks one contiguous range: the workgroups
-// resident on an XCD share token rows and weight tiles through its L2.
+// resident on an XCD share weight tiles and token rows through its L2.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -455,8 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     __shared__ int tok[BN];
     // XCD swizzle: the eighth of the tile range that this workgroup's XCD walks
     const int L = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
-    const int tg = L / row_tiles;                  // token tile, over all experts
-    const int rt = L - tg * row_tiles;
+    const int tg = L / row_tiles;                  // L lies in the range of token tile tg's expert
     const int na = a.w.n_act[0];
     if (tg >= a.w.tt_off[na]) return;
     int lo = 0, hi = na;                           // expert slot: tt_off[lo] <= tg < tt_off[lo + 1]
@@ -465,7 +467,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
         if (a.w.tt_off[mid] <= tg) lo = mid; else hi = mid;
     }
     const int e = a.w.act[lo];
-    const int tt = tg - a.w.tt_off[lo];
+    // within the expert's range, row tile major and token tile minor: the
+    // workgroups that stream the same codes are neighbours in dispatch order
+    // and run side by side on one XCD, so the codes come from its L2
+    const int ntt = a.w.tt_off[lo + 1] - a.w.tt_off[lo];
+    const int l = L - a.w.tt_off[lo] * row_tiles;
+    const int rt = l / ntt;
+    const int tt = l - rt * ntt;
     const int b = a.tab.bits[e];
     if (b == 4) gemm_tile<MODE, 4>(a, e, tt, rt, smem, tok);
     else if (b == 8) gemm_tile<MODE, 8>(a, e, tt, rt, smem, tok);

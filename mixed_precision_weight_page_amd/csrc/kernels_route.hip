@@ -9,13 +9,15 @@
 // active experts is ordered 8-bit pages first, then 4-bit, then 3-bit (each
 // by expert id), so the longest tiles are dispatched first.
 //
-// Up to 16 tokens: one workgroup does everything. Up to kFusedMaxPairs
-// pairs: a router kernel (one wave per token, many workgroups), then one
+// Top-k per token: with at most 256 experts a row of 16 lanes routes one
+// token (DPP reductions within the row), else a wave (shuffles). Up to 16
+// tokens: one workgroup does everything. Up to kFusedMaxPairs pairs: a router kernel over many workgroups, then one
 // workgroup ranks and offsets. Larger batches: router; ranks per expert and
 // chunk of kRankChunk tokens; counts, chunk prefixes and offsets in one
-// workgroup; pair positions over many workgroups. Kernel boundaries carry the results between workgroups (a
-// device-scope handshake inside one kernel would have to write back and
-// invalidate the per-XCD L2 caches). No host synchronisation.
+// workgroup; pair positions over many workgroups. Kernel boundaries carry
+// the results between workgroups (a device-scope handshake inside one kernel
+// would have to write back and invalidate the per-XCD L2 caches). No host
+// synchronisation.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -28,6 +30,11 @@ namespace {
 constexpr int kMaxPerLane = kMaxExperts / 64;  // 16 logits per lane
 constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / 64;
+constexpr int kRowMaxExperts = 256;             // 16 lanes per token up to this many experts
+// One workgroup routes and groups up to this many tokens; beyond, the top-k
+// (VALU-bound) is spread over many workgroups and only the grouping stays in
+// one.
+constexpr int kFusedMaxTokens = 16;
 
 __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
     return v > v2 || (v == v2 && e < e2);
@@ -85,6 +92,108 @@ __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork&
     }
 }
 
+// ---- 16 lanes per token (E <= 256) ----
+// A row of 16 lanes routes one token; lane i of the row holds the logits of
+// experts i, i + 16, ... . Reductions across the row use DPP (quad
+// permutations, then the half-row and row mirrors), which leaves the row's
+// result in every lane of the row without a trip through LDS.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+constexpr int kQuadXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& be) {
+    const float ov = dpp_f<CTRL>(bv);
+    const int oe = dpp_i<CTRL>(be);
+    if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+}
+__device__ __forceinline__ void row_argmax(float& bv, int& be) {
+    argmax_step<kQuadXor1>(bv, be);
+    argmax_step<kQuadXor2>(bv, be);
+    argmax_step<kRowHalfMirror>(bv, be);
+    argmax_step<kRowMirror>(bv, be);
+}
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_f<kQuadXor1>(x);
+    x += dpp_f<kQuadXor2>(x);
+    x += dpp_f<kRowHalfMirror>(x);
+    x += dpp_f<kRowMirror>(x);
+    return x;
+}
+
+// The row of 16 lanes containing this thread routes token t (all lanes of
+// the row call it with the same t; `valid` false for a row past the batch).
+template <int PER>
+__device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w, int t, bool valid,
+                                            int* s_ids) {
+    const int l16 = threadIdx.x & 15;
+    const float* row = a.logits + (int64_t)t * a.E;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = l16 + 16 * i;
+        v[i] = (valid && e < a.E) ? row[e] : -INFINITY;
+    }
+    int id0 = 0, id1 = 0;
+    float val0 = -INFINITY, val1 = -INFINITY, top = -INFINITY;
+    uint32_t taken = 0;   // bit i: v[i] already chosen
+    for (int j = 0; j < a.k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = l16 + 16 * i;
+            if (e < a.E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
+                bv = v[i];
+                be = e;
+            }
+        }
+        row_argmax(bv, be);
+        if ((be & 15) == l16) taken |= 1u << (be >> 4);
+        if (j == 0) top = bv;
+        if (j == l16) { id0 = be; val0 = bv; }
+        if (j == l16 + 16) { id1 = be; val1 = bv; }
+    }
+    float sum_all = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = l16 + 16 * i;
+        if (e < a.E) sum_all += expf(v[i] - top);
+    }
+    const float m0 = l16 < a.k ? expf(val0 - top) : 0.0f;
+    const float m1 = l16 + 16 < a.k ? expf(val1 - top) : 0.0f;
+    const float den = row_sum(a.renorm ? m0 + m1 : sum_all);
+    if (!valid) return;
+    if (l16 < a.k) {
+        w.ids[(int64_t)t * a.k + l16] = id0;
+        w.g[(int64_t)t * a.k + l16] = m0 / den;
+        if (s_ids) s_ids[t * a.k + l16] = id0;
+    }
+    if (l16 + 16 < a.k) {
+        w.ids[(int64_t)t * a.k + l16 + 16] = id1;
+        w.g[(int64_t)t * a.k + l16 + 16] = m1 / den;
+        if (s_ids) s_ids[t * a.k + l16 + 16] = id1;
+    }
+}
+
+__device__ __forceinline__ void route_row(const RouteArgs& a, const FwdWork& w, int t, bool valid, int* s_ids) {
+    const int per = (a.E + 15) / 16;
+    if (per == 1) route_row_t<1>(a, w, t, valid, s_ids);
+    else if (per == 2) route_row_t<2>(a, w, t, valid, s_ids);
+    else if (per <= 4) route_row_t<4>(a, w, t, valid, s_ids);
+    else if (per <= 8) route_row_t<8>(a, w, t, valid, s_ids);
+    else route_row_t<16>(a, w, t, valid, s_ids);
+}
+
 __device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t, int* s_ids) {
     const int per = (a.E + 63) / 64;
     if (per == 1) route_token_t<1>(a, w, t, s_ids);
@@ -121,8 +230,8 @@ __device__ __forceinline__ T block_scan(T v, T* s_wave, T* total) {
 // Offsets, bit-ordered active list and token tiles; cnt_of(e) gives the
 // count of expert e. Leaves the offsets in s_off.
 template <class CntF>
-__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const int32_t* bits,
-                                                 CntF cnt_of, int* s_off) {
+__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my_bits, CntF cnt_of,
+                                                 int* s_off) {
     __shared__ int s_wave_i[kWaves];
     __shared__ long long s_wave_l[kWaves];
     const int tid = threadIdx.x;
@@ -135,7 +244,7 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const 
     }
     if (tid == 0) w.off[E] = tot;
     // classes: 0 = 8-bit, 1 = 4-bit, 2 = 3-bit; 21-bit counters per class
-    const int b = tid < E ? bits[tid] : 0;
+    const int b = my_bits;   // bit-width of expert tid (loaded by the caller at kernel entry)
     const int cls = b == 8 ? 0 : (b == 4 ? 1 : 2);
     const long long flag = (tid < E && c > 0) ? (1ll << (21 * cls)) : 0ll;
     long long ltot;
@@ -164,10 +273,10 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const 
 // Offsets and pair positions in one workgroup; rank_of(p) gives the rank of
 // pair p, id_of(p) its expert.
 template <class CntF, class RankF, class IdF>
-__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, const int32_t* bits,
+__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, int my_bits,
                                          CntF cnt_of, RankF rank_of, IdF id_of) {
     __shared__ int s_off[kMaxExperts];
-    finalize_offsets(E, w, bits, cnt_of, s_off);
+    finalize_offsets(E, w, my_bits, cnt_of, s_off);
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) {
         const int e = id_of(p);
@@ -177,42 +286,64 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
     }
 }
 
-// Stable rank of every pair from ids in LDS: wave handles experts wave,
-// wave + 16, ...; lanes = tokens. Writes s_rank, s_cnt and w.cnt.
-__device__ __forceinline__ void rank_small(int T, int E, int k, const int* s_ids, int* s_rank,
-                                           int* s_cnt, const FwdWork& w) {
+// Stable rank of every pair from ids in LDS: for each chunk of 64 tokens,
+// lane = token, holding its KMAX (>= k) expert ids in registers; wave w
+// handles experts w, w + 16, ... and keeps their running counts in s_cnt.
+// Writes s_rank, s_cnt and w.cnt.
+template <int KMAX>
+__device__ __forceinline__ void rank_small_t(int T, int E, int k, const int* s_ids, int* s_rank, int* s_cnt,
+                                             const FwdWork& w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int e = wave; e < E; e += kWaves) {
-        int running = 0;
-        for (int t0 = 0; t0 < T; t0 += 64) {
-            const int tt = t0 + lane;
+    for (int e = wave; e < E; e += kWaves)
+        if (lane == 0) s_cnt[e] = 0;
+    for (int t0 = 0; t0 < T; t0 += 64) {
+        const int tt = t0 + lane;
+        int my[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) my[j] = (j < k && tt < T) ? s_ids[tt * k + j] : -1;
+        for (int e = wave; e < E; e += kWaves) {
             int slot = -1;
-            if (tt < T)
-                for (int j = 0; j < k; ++j)
-                    if (s_ids[tt * k + j] == e) slot = j;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (my[j] == e) slot = j;
             const uint64_t m = __ballot(slot >= 0);
-            if (slot >= 0) s_rank[tt * k + slot] = running + __popcll(m & ((1ull << lane) - 1ull));
-            running += __popcll(m);
-        }
-        if (lane == 0) {
-            s_cnt[e] = running;
-            w.cnt[e] = running;
+            const int base = s_cnt[e];
+            if (slot >= 0) s_rank[tt * k + slot] = base + __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == 0) s_cnt[e] = base + __popcll(m);
         }
     }
+    for (int e = wave; e < E; e += kWaves)
+        if (lane == 0) w.cnt[e] = s_cnt[e];
 }
 
-// ---- tiny batches (T <= 16): everything in one workgroup ----
+__device__ __forceinline__ void rank_small(int T, int E, int k, const int* s_ids, int* s_rank, int* s_cnt,
+                                           const FwdWork& w) {
+    if (k <= 2) rank_small_t<2>(T, E, k, s_ids, s_rank, s_cnt, w);
+    else if (k <= 4) rank_small_t<4>(T, E, k, s_ids, s_rank, s_cnt, w);
+    else if (k <= 8) rank_small_t<8>(T, E, k, s_ids, s_rank, s_cnt, w);
+    else if (k <= 16) rank_small_t<16>(T, E, k, s_ids, s_rank, s_cnt, w);
+    else rank_small_t<32>(T, E, k, s_ids, s_rank, s_cnt, w);
+}
+
+// ---- small batches (T <= kFusedMaxTokens): everything in one workgroup ----
 __global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWork w,
                                                              const int32_t* bits) {
     __shared__ int s_ids[kFusedMaxPairs];
     __shared__ int s_rank[kFusedMaxPairs];
     __shared__ int s_cnt[kMaxExperts];
-    const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < a.T; t += kWaves) route_token(a, w, t, s_ids);
+    const int my_bits = threadIdx.x < a.E ? bits[threadIdx.x] : 0;
+    if (a.E <= kRowMaxExperts) {
+        const int r16 = threadIdx.x >> 4;          // 64 rows of 16 lanes
+        for (int t0 = 0; t0 < a.T; t0 += kBlock / 16)
+            route_row(a, w, t0 + r16, t0 + r16 < a.T, s_ids);
+    } else {
+        const int wave = threadIdx.x >> 6;
+        for (int t = wave; t < a.T; t += kWaves) route_token(a, w, t, s_ids);
+    }
     __syncthreads();
     rank_small(a.T, a.E, a.k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(a.T, a.E, a.k, w, bits, [&](int e) { return s_cnt[e]; },
+    finalize(a.T, a.E, a.k, w, my_bits, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
@@ -222,20 +353,27 @@ __global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k
     __shared__ int s_ids[kFusedMaxPairs];
     __shared__ int s_rank[kFusedMaxPairs];
     __shared__ int s_cnt[kMaxExperts];
+    const int my_bits = threadIdx.x < E ? bits[threadIdx.x] : 0;
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) s_ids[p] = w.ids[p];
     __syncthreads();
     rank_small(T, E, k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(T, E, k, w, bits, [&](int e) { return s_cnt[e]; },
+    finalize(T, E, k, w, my_bits, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
 // ---- large batches: route, rank, finalize ----
-// grid ceil(T / 4), 256 threads: wave w of block b handles token 4b + w.
+// grid ceil(T / 16) (E <= 256: row r of block b handles token 16b + r) or
+// ceil(T / 4) (wave w of block b handles token 4b + w), 256 threads.
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < a.T) route_token(a, w, t, nullptr);
+    if (a.E <= kRowMaxExperts) {
+        const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+        route_row(a, w, t < a.T ? t : a.T - 1, t < a.T, nullptr);
+    } else {
+        const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (t < a.T) route_token(a, w, t, nullptr);
+    }
 }
 
 // grid (E, C), 256 threads: rank of expert e's pairs in token order among
@@ -270,6 +408,7 @@ __global__ __launch_bounds__(256) void rank_kernel(int T, int k, int C, FwdWork 
 __global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, FwdWork w, const int32_t* bits) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
+    const int my_bits = threadIdx.x < E ? bits[threadIdx.x] : 0;
     for (int e = threadIdx.x; e < E; e += kBlock) {
         int run = 0;
         for (int c = 0; c < C; ++c) {
@@ -280,7 +419,7 @@ __global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, FwdWork w
         w.cnt[e] = run;
     }
     __syncthreads();
-    finalize_offsets(E, w, bits, [&](int e) { return s_cnt[e]; }, s_off);
+    finalize_offsets(E, w, my_bits, [&](int e) { return s_cnt[e]; }, s_off);
 }
 
 // grid ceil(P / 256): position of every pair in expert-sorted order.
@@ -299,9 +438,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWo
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
                         KTimer t) {
     const hipEvent_t none = nullptr;
-    if (a.T <= kWaves && a.T * a.k <= kFusedMaxPairs)
+    if (a.T <= kFusedMaxTokens && a.T * a.k <= kFusedMaxPairs)
         return launch_timed(route_fused_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
-    hipError_t err = launch_timed(route_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, t.start, none, a, w);
+    const int per_block = a.E <= kRowMaxExperts ? 16 : 4;
+    hipError_t err = launch_timed(route_kernel, dim3((a.T + per_block - 1) / per_block), dim3(256), 0, s, t.start,
+                                  none, a, w);
     if (err != hipSuccess) return err;
     if (a.T * a.k <= kFusedMaxPairs)
         return launch_timed(group_small_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k,

@@ -42,28 +42,38 @@ def test_tiny_pages_and_forward():
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), "tiny")
 
 
-def test_router_matches_oracle():
-    # one-workgroup path (T <= 16), router + one-workgroup grouping, and the
-    # multi-workgroup path (more than 4096 pairs; 2500 tokens = three ranking
-    # chunks of 1024, the last one ragged)
-    for wl, T in ((TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300),
-                  (SMALL_FINE, 700), (SMALL_FINE, 2500)):
-        masters = tuple(torch.zeros(1) for _ in range(3))
-        from mixed_precision_weight_page_amd import PagedMoELayer
-        layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=T)
-        layer.alloc_workspace()
-        _, logits = synth.tokens(wl, T=T)
-        # plant exact ties: equal logits must resolve to the lower index
-        logits[0, :] = 0.25
-        logits[1, 3] = logits[1, 5] = logits[1].max() + 1.0
-        ids, g, counts = layer.route(logits.cuda())
-        torch.cuda.synchronize()
-        rid, rg = moe.route(logits, wl.k)
-        assert torch.equal(ids.cpu().long(), rid), wl.name
-        assert torch.allclose(g.cpu().double(), rg, rtol=2e-6, atol=1e-7), wl.name
-        want = torch.bincount(rid.reshape(-1), minlength=wl.E)
-        assert torch.equal(counts.cpu().long(), want)
-        del masters
+ROUTER_CASES = [
+    # (workload, tokens): one-workgroup path with 16-lane rows (E <= 256,
+    # T <= 64), router + one-workgroup grouping, and the multi-workgroup path
+    # (more than 4096 pairs; 2500 tokens = three ranking chunks of 1024, the
+    # last one ragged)
+    (TINY, 16), (SMALL_FINE, 40), (synth.WORKLOADS["decode_fine"], 64),
+    (synth.WORKLOADS["decode_fine"], 65), (synth.WORKLOADS["prefill"].scaled(E=64, d=128, F=128), 300),
+    (SMALL_FINE, 700), (SMALL_FINE, 2500),
+    # 256 experts: 16 logits per lane; k = 20 > 16 slots per row of lanes
+    (TINY.scaled(name="e256", E=256, k=8), 64), (TINY.scaled(name="k20", E=64, k=20), 30),
+    # more than 256 experts: a wave per token (fused up to 16 tokens)
+    (TINY.scaled(name="e300", E=300, k=6), 12), (TINY.scaled(name="e300", E=300, k=6), 40),
+    (TINY.scaled(name="e300", E=300, k=6), 800),
+]
+
+
+@pytest.mark.parametrize("wl,T", ROUTER_CASES, ids=lambda v: str(v) if isinstance(v, int) else v.name)
+def test_router_matches_oracle(wl, T):
+    from mixed_precision_weight_page_amd import PagedMoELayer
+    layer = PagedMoELayer(wl.E, 128, 128, wl.k, max_tokens=T)
+    layer.alloc_workspace()
+    _, logits = synth.tokens(wl, T=T)
+    # plant exact ties: equal logits must resolve to the lower index
+    logits[0, :] = 0.25
+    logits[1, 3] = logits[1, 5] = logits[1].max() + 1.0
+    ids, g, counts = layer.route(logits.cuda())
+    torch.cuda.synchronize()
+    rid, rg = moe.route(logits, wl.k)
+    assert torch.equal(ids.cpu().long(), rid), wl.name
+    assert torch.allclose(g.cpu().double(), rg, rtol=2e-6, atol=1e-7), wl.name
+    want = torch.bincount(rid.reshape(-1), minlength=wl.E)
+    assert torch.equal(counts.cpu().long(), want)
 
 
 def test_router_renorm():

@@ -43,14 +43,16 @@ __device__ __forceinline__ float scale_of(float m, int qm) {
 }
 
 // round-half-to-even of the exact quotient w / s (s > 0), without a
-// double-precision divide: take the rounded fp32 quotient, then test it
-// against the two neighbouring midpoints exactly. fma(-(r +- 1/2), s, w)
-// is w - (r +- 1/2) s rounded once, so its sign (and whether it is zero) is
-// that of the exact difference. Scales below 2^-100 take the fp64 path so
-// that the difference cannot underflow.
-__device__ __forceinline__ float round_quotient(float w, float s) {
+// divide: r = rint(w * (1/s)) is within one of the correctly rounded
+// quotient (the product is off by a few units in the last place of a value
+// of magnitude at most qmax), and the two neighbouring midpoints are then
+// tested exactly: fma(-(r +- 1/2), s, w) is w - (r +- 1/2) s rounded once,
+// so its sign (and whether it is zero) is that of the exact difference.
+// Scales below 2^-100 take the fp64 path so that the difference cannot
+// underflow.
+__device__ __forceinline__ float round_quotient(float w, float s, float inv_s) {
     if (s < 7.8886091e-31f) return (float)rint((double)w / (double)s);
-    float r = rintf(w / s);
+    float r = rintf(w * inv_s);
     const float hi = fmaf(-(r + 0.5f), s, w);   // sign of w/s - (r + 1/2)
     const float lo = fmaf(-(r - 0.5f), s, w);   // sign of w/s - (r - 1/2)
     const bool odd = ((int)r) & 1;
@@ -61,9 +63,9 @@ __device__ __forceinline__ float round_quotient(float w, float s) {
     return r;
 }
 
-__device__ __forceinline__ float code_of(float w, float s, float qm) {
+__device__ __forceinline__ float code_of(float w, float s, float inv_s, float qm) {
     if (s == 0.0f) return 0.0f;
-    const float r = round_quotient(w, s);
+    const float r = round_quotient(w, s, inv_s);
     return fminf(fmaxf(r, -qm), qm);
 }
 
@@ -124,11 +126,12 @@ __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, 
     const void* base = matrix_base(w1, w3, w2, mtx);
     const int64_t off = (int64_t)e * M + (start - (int64_t)mtx * M);
     const float m = __uint_as_float(absmax[e]);
-    float s[3], qm[3];
+    float s[3], inv_s[3], qm[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         qm[i] = (float)qmax_of(bits_of_index(i));
         s[i] = scale_of(m, qmax_of(bits_of_index(i)));
+        inv_s[i] = s[i] > 0.0f ? 1.0f / s[i] : 0.0f;
     }
     double acc[3] = {0.0, 0.0, 0.0};
     for (int i = 0; i < kPerThread / 4; ++i) {
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, 
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int b = 0; b < 3; ++b) {
-                const float q = code_of(v[j], s[b], qm[b]);
+                const float q = code_of(v[j], s[b], inv_s[b], qm[b]);
                 const double err = (double)v[j] - (double)s[b] * (double)q;  // exact
                 acc[b] = fma(err, err, acc[b]);
             }
@@ -178,36 +181,44 @@ __global__ __launch_bounds__(kThreads) void loss_final_kernel(const double* part
     }
 }
 
-// One wave packs one tile of 16 rows x 128 codes. Lane l = 16 g + r
-// quantizes codes 32g..32g+31 of row r into a 32B-bit LSB-first run and
-// stores it in the tile: 4-bit 16 bytes at 16 l; 8-bit 16 bytes at 16 l and
-// 16 bytes at 1024 + 16 l; 3-bit 12 bytes at 12 l.
+// One wave packs one tile of 16 rows x 128 codes of one matrix. Loads are
+// row-contiguous (lanes 0-31 one row, 32-63 the next, four weights each);
+// the codes u = q + 2^(b-1) go through LDS as bytes (rows padded to 144
+// bytes), and lane l = 16 g + r then packs codes 32g..32g+31 of row r into
+// a 32B-bit LSB-first run: 4-bit 16 bytes at 16 l; 8-bit 16 bytes at 16 l
+// and 16 bytes at 1024 + 16 l; 3-bit 12 bytes at 12 l.
+constexpr int kCodeRow = 144;   // LDS bytes per row of codes
+
 template <int B>
-__device__ __forceinline__ void pack_lane(const void* base, int64_t src, int f16, float s,
-                                          uint8_t* tile) {
+__device__ __forceinline__ void pack_run(const uint8_t* codes, uint8_t* tile) {
     const int lane = threadIdx.x & 63;
-    const float qm = (float)qmax_of(B);
-    uint32_t w[B];
+    const int r = lane & 15, g = lane >> 4;
+    const uint4 c0 = *reinterpret_cast<const uint4*>(codes + r * kCodeRow + 32 * g);
+    const uint4 c1 = *reinterpret_cast<const uint4*>(codes + r * kCodeRow + 32 * g + 16);
+    const uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};   // 4 codes per word
+    if constexpr (B == 8) {
+        *reinterpret_cast<uint4*>(tile + 16 * lane) = c0;
+        *reinterpret_cast<uint4*>(tile + 1024 + 16 * lane) = c1;
+    } else if constexpr (B == 4) {
+        uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float v[4];
-        load4(base, src + 4 * i, f16, v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t u = (uint32_t)((int)code_of(v[j], s, qm) + (1 << (B - 1)));
-            const int bit = B * (4 * i + j);          // compile-time after unrolling
-            w[bit / 32] |= u << (bit % 32);
-            if (bit % 32 + B > 32) w[bit / 32 + 1] |= u >> (32 - bit % 32);
+        for (int i = 0; i < 4; ++i) {
+            // codes 8i..8i+7 from words 2i (bytes 0-3) and 2i+1 (bytes 4-7)
+            const uint32_t lo = c[2 * i], hi = c[2 * i + 1];
+            const uint32_t a = (lo & 0x0fu) | ((lo >> 4) & 0xf0u) | ((lo >> 8) & 0xf00u) | ((lo >> 12) & 0xf000u);
+            const uint32_t b = (hi & 0x0fu) | ((hi >> 4) & 0xf0u) | ((hi >> 8) & 0xf00u) | ((hi >> 12) & 0xf000u);
+            w[i] = a | (b << 16);
         }
-    }
-    if constexpr (B == 4) {
         *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else if constexpr (B == 8) {
-        *reinterpret_cast<uint4*>(tile + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(tile + 1024 + 16 * lane) = make_uint4(w[4], w[5], w[6], w[7]);
     } else {
+        uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const uint32_t u = (c[k >> 2] >> (8 * (k & 3))) & 0xffu;
+            const int bit = 3 * k;                    // compile-time after unrolling
+            w[bit / 32] |= u << (bit % 32);
+            if (bit % 32 + 3 > 32) w[bit / 32 + 1] |= u >> (32 - bit % 32);
+        }
         uint32_t* o = reinterpret_cast<uint32_t*>(tile + 12 * lane);
         o[0] = w[0]; o[1] = w[1]; o[2] = w[2];
     }
@@ -220,26 +231,43 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const vo
                                                         const void* w2, int f16, int d, int F,
                                                         DevTable tab, const int32_t* list,
                                                         uint8_t* pool) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[kThreads / 64][16 * kCodeRow];
     const int e = list[blockIdx.y];
     const int b = tab.bits[e];
     const float s = tab.scale[e];
+    const float inv_s = s > 0.0f ? 1.0f / s : 0.0f;
+    const float qm = (float)qmax_of(b);
+    const int bias = 1 << (b - 1);
     const int64_t M = (int64_t)F * d;
     const int64_t tpm = M / 2048;                         // tiles per matrix
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     const int mtx = (int)(t / tpm);
     const int64_t tt = t - mtx * tpm;
     const int K = mtx == 2 ? F : d;
     const int steps = K / 128;
     const int64_t rb = tt / steps;
     const int st = (int)(tt - rb * steps);
-    const int lane = threadIdx.x & 63;
-    const int64_t row = rb * 16 + (lane & 15);
-    const int64_t src = (int64_t)e * M + row * K + st * 128 + 32 * (lane >> 4);
     const void* base = matrix_base(w1, w3, w2, mtx);
+    uint8_t* codes = s_codes[wave];
+    // rows 2i + lane / 32 of the tile, weights 4 (lane % 32) .. +4
+    const int half = lane >> 5, c4 = 4 * (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + half;
+        float v[4];
+        load4(base, (int64_t)e * M + (rb * 16 + row) * K + st * 128 + c4, f16, v);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            packed |= (uint32_t)((int)code_of(v[j], s, inv_s, qm) + bias) << (8 * j);
+        *reinterpret_cast<uint32_t*>(codes + row * kCodeRow + c4) = packed;
+    }
+    __syncthreads();   // (the wave's own rows; a block barrier keeps it simple)
     uint8_t* tile = pool + tab.off[e] + mtx * (M * b / 8) + tt * (256 * b);
-    if (b == 3) pack_lane<3>(base, src, f16, s, tile);
-    else if (b == 4) pack_lane<4>(base, src, f16, s, tile);
-    else pack_lane<8>(base, src, f16, s, tile);
+    if (b == 3) pack_run<3>(codes, tile);
+    else if (b == 4) pack_run<4>(codes, tile);
+    else pack_run<8>(codes, tile);
 }
 
 }  // namespace

@@ -232,6 +232,33 @@ def test_zero_expert_and_lossless_grid():
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), "grid")
 
 
+def test_rounding_ties_and_neighbours():
+    """Eq. 2 rounds half to even. With power-of-two scales (absmax = qmax *
+    2^-j) the quotients w / s of weights (n + 1/2) s are exact ties, and their
+    fp32 neighbours lie just above and below them; every code must match the
+    oracle's exact rounding (bit-exact pages)."""
+    wl = synth.WORKLOADS["tiny"].scaled(name="ties", E=3, d=128, F=128, k=2, T=8, bits=(8, 4, 3))
+    w1, w3, w2 = (m.clone() for m in synth.expert_weights(wl))
+    gen = torch.Generator().manual_seed(7)
+    for e, (b, j) in enumerate(((8, 8), (4, 5), (3, 4))):
+        qm = 2 ** (b - 1) - 1
+        s = 2.0 ** -j
+        for m in (w1, w3, w2):
+            n = torch.randint(-qm, qm, m[e].shape, generator=gen).to(torch.float32)
+            tie = (n + 0.5) * s                                  # exact in fp32
+            kind = torch.randint(0, 4, m[e].shape, generator=gen)
+            up = torch.nextafter(tie, torch.full_like(tie, float("inf")))
+            down = torch.nextafter(tie, torch.full_like(tie, float("-inf")))
+            m[e] = torch.where(kind == 0, up, torch.where(kind == 1, down, tie))
+        w1[e, 0, 0] = qm * s                                     # absmax: s = 2^-j exactly
+    masters = (w1, w3, w2)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    for e, j in enumerate((8, 5, 4)):
+        assert layer.get_page_table()[e]["scale"] == 2.0 ** -j
+    check_pages(layer, pool, masters, wl.bits)
+
+
 def test_mostly_zero_codes_keep_precision():
     """Outliers x1000 make nearly every 3- and 4-bit code 0, so the true
     products sum only a few terms; the kernel must not let the code offset

@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-kernel events (no roofline)")
+    ap.add_argument("--event-every-step", action="store_true",
+                    help="timing events on every forward of the timed region (default: on the forwards of "
+                         "the first rotated pool only, every len(pools)-th step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -126,7 +129,9 @@ class Bench:
         dn = sum(wl.d * wl.F * self.bits[e] // 8 for e in active)
         return gu, dn, len(active)
 
-    def run(self, T, steps, warmup, profile=2):
+    def run(self, T, steps, warmup, profile=2, sample=False):
+        """profile: kernel mask timed with events; sample: events only on the
+        forwards of the first rotated context (every len(layers)-th step)."""
         torch = self.torch
         nb = 8
         batches = self.batches(T, nb)
@@ -142,8 +147,8 @@ class Bench:
             x, lg = batches[i % nb]
             self.layers[i % L].moe_forward(x, lg, ys[i % nb])
         torch.cuda.synchronize()
-        for layer in self.layers:
-            layer.profile(profile)
+        for j, layer in enumerate(self.layers):
+            layer.profile(profile if (j == 0 or not sample) else 0)
         t0 = time.perf_counter()
         for i in range(steps):
             x, lg = batches[i % nb]
@@ -151,15 +156,22 @@ class Bench:
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         prof = {"gate_up_ms": 0.0, "down_ms": 0.0, "route_ms": 0.0, "combine_ms": 0.0}
+        timed = 0
         if profile:
             for layer in self.layers:
                 p = layer.profile_read()
                 layer.profile(0)
+                timed += p["forwards"]
                 for k in prof:
                     prof[k] += p[k]
+        # per-forward kernel times, averaged over the forwards that carried events
+        prof = {k: (v / timed if timed else 0.0) for k, v in prof.items()}
         tot_gu = sum(bytes_gu[i % nb] for i in range(steps))
+        # packed W1+W3 bytes of the forwards that carried events
+        gu_timed = sum(bytes_gu[i % nb] for i in range(steps) if not sample or i % L == 0)
         tot_dn = sum(bytes_dn[i % nb] for i in range(steps))
-        return dict(T=T, steps=steps, elapsed=elapsed, prof=prof, bytes_gu=tot_gu,
+        return dict(T=T, steps=steps, timed_forwards=timed, bytes_gu_timed=gu_timed, elapsed=elapsed, prof=prof,
+                    bytes_gu=tot_gu,
                     bytes_dn=tot_dn, mean_active=sum(n_act[i % nb] for i in range(steps)) / steps)
 
 
@@ -222,12 +234,14 @@ def main():
     b = Bench(wl, max_tokens, npools, log)
     # timed region: events only on the gate/up kernel (the roofline kernel);
     # a second pass of the same steps times every kernel for the breakdown
-    r = b.run(T, args.steps, args.warmup, profile=0 if args.no_profile else 2)
+    sample = not args.event_every_step
+    r = b.run(T, args.steps, args.warmup, profile=0 if args.no_profile else 2, sample=sample)
     r_all = b.run(T, args.steps, 0, profile=15) if not args.no_profile else None
     tokens_per_s = T * r["steps"] / r["elapsed"]
     ms = 1e3 * r["elapsed"] / r["steps"]
-    gu_ms = r["prof"]["gate_up_ms"] / r["steps"]
-    gu_gbps = r["bytes_gu"] / r["steps"] / (gu_ms * 1e-3) / 1e9 if gu_ms > 0 else None
+    gu_ms = r["prof"]["gate_up_ms"]
+    gu_bytes = r["bytes_gu_timed"] / r["timed_forwards"] if r["timed_forwards"] else 0.0
+    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms > 0 else None
     fwd_gbps = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
     traffic = traffic_from_profiles(args.workload, T)
     if args.workload == "prefill":
@@ -241,7 +255,8 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": (gu_gbps or 0) / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "gate_up (fused dequant + W1/W3 + SwiGLU)",
-                "bytes_per_launch": r["bytes_gu"] / r["steps"],
+                "bytes_per_launch": gu_bytes,
+                "launches_timed": r["timed_forwards"],
                 "launch_ms": gu_ms}
     out = {
         "metric": METRIC,
@@ -263,9 +278,9 @@ def main():
                    "bits": b.bits, "pools_rotated": npools},
         "packed_weight_GBps": fwd_gbps,
         "packed_weight_frac_of_hbm": fwd_gbps / HBM_PEAK_GBPS,
-        "kernels_ms_per_step": ({k: v / r_all["steps"] for k, v in r_all["prof"].items()}
+        "kernels_ms_per_step": (dict(r_all["prof"])
                                 if r_all else None),
-        "down_GBps": (r_all["bytes_dn"] / r_all["steps"] / (r_all["prof"]["down_ms"] / r_all["steps"] * 1e-3) / 1e9
+        "down_GBps": (r_all["bytes_dn"] / r_all["steps"] / (r_all["prof"]["down_ms"] * 1e-3) / 1e9
                       if r_all and r_all["prof"]["down_ms"] > 0 else None),
         "mean_active_experts": r["mean_active"],
         "roofline": roof,
@@ -273,12 +288,13 @@ def main():
     if not args.no_sweep and sweep_T:
         sw = {}
         for t in sweep_T:
-            rs = b.run(t, args.steps, args.warmup, profile=0 if args.no_profile else 2)
-            g = rs["prof"]["gate_up_ms"] / rs["steps"]
+            rs = b.run(t, args.steps, args.warmup, profile=0 if args.no_profile else 2, sample=sample)
+            g = rs["prof"]["gate_up_ms"]
             sw[f"T={t}"] = {"tokens_per_s": t * rs["steps"] / rs["elapsed"],
                             "ms_per_step": 1e3 * rs["elapsed"] / rs["steps"],
                             "packed_weight_GBps": (rs["bytes_gu"] + rs["bytes_dn"]) / rs["elapsed"] / 1e9,
-                            "gate_up_GBps": rs["bytes_gu"] / rs["steps"] / (g * 1e-3) / 1e9 if g else None,
+                            "gate_up_GBps": (rs["bytes_gu_timed"] / rs["timed_forwards"] / (g * 1e-3) / 1e9
+                                             if g and rs["timed_forwards"] else None),
                             "mean_active_experts": rs["mean_active"]}
         out["sweep"] = sw
     if not args.no_cpu_baseline:

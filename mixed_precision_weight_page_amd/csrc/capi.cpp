@@ -25,7 +25,7 @@ struct pw_ctx {
     pw_layer_desc desc{};
     int E = 0, d = 0, F = 0, k = 0;
     int64_t M = 0;        // F * d weights per matrix
-    int nsplit = 1;       // K-splits of the down product
+    int nsplit = 1;       // most K-splits of the down product the workspace holds (per pair)
     uint64_t We = 0;      // 3 * M weights per expert
     Layout lay{};
 
@@ -404,7 +404,12 @@ pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out) {
     c->k = d.top_k;
     c->M = (int64_t)d.d_model * d.d_ff;
     c->We = 3 * (uint64_t)c->M;
-    c->nsplit = down_splits(c->F, (int64_t)d.max_tokens * d.top_k);
+    // partial-output buffers for the down product's K splits: room for the
+    // splits a single routed expert would want (the most any forward takes),
+    // unless the batch is large (then the buffer of T k d floats is big
+    // enough on its own and small batches split within it)
+    const int64_t max_pairs = (int64_t)d.max_tokens * d.top_k;
+    c->nsplit = max_pairs > 2048 ? 1 : down_splits(c->F, c->d, 1, 1 << 30);
     c->lay = workspace_layout(c->E, c->d, c->F, c->k, d.max_tokens, c->nsplit);
     c->table.assign(c->E, pw_page_entry{});
     *out = c;
@@ -569,7 +574,7 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
     const int P = c->desc.max_tokens * c->k;
     // many tokens per expert: dense tiles on the matrix cores (weights read
-    // once per 128 tokens); few: the streaming kernels (weights read once)
+    // once per 64 tokens); few: the streaming kernels (weights read once)
     if (gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act) {
         GemmArgs ga;
         ga.pool = c->pool;
@@ -601,9 +606,12 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         fa.k = c->k;
         fa.max_act = max_act;
         fa.P = P;
+        // K splits of the down product for this batch, within the buffer
+        const int64_t cap_pairs = (int64_t)c->nsplit * c->desc.max_tokens * c->k;
+        const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / P, 1 << 30));
         HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
-        HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, c->nsplit), s, tm[2]));
-        HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, c->nsplit, y, s, tm[3]));
+        HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, nsplit), s, tm[2]));
+        HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, nsplit, y, s, tm[3]));
     }
     if (c->profile_mask) c->forwards_timed++;
     return PW_OK;

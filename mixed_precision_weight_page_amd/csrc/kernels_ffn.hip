@@ -415,21 +415,30 @@ FfnPlan plan_ffn(int K, int T, int nsplit) {
     p.nt_alloc = T < 16 ? (T < 1 ? 1 : T) : 16;
     p.nsplit = nsplit;
     const size_t full = (size_t)p.nt_alloc * (K / nsplit + 8) * 2;
-    const size_t cap = 48 * 1024;
+    // at least 8 steps (the deepest prefetch) of 16 token rows, so a chunk of
+    // staged rows always covers whole prefetch groups; 34 KB lets four
+    // workgroups share a CU's LDS
+    const size_t floor_bytes = (size_t)16 * (8 * kStep + 8) * 2;
+    const size_t cap = 34 * 1024 > floor_bytes ? 34 * 1024 : floor_bytes;
     p.lds = full < cap ? full : cap;
     return p;
 }
 
-// Small batches of a layer with a long down-projection K (large d_ff) would
-// leave most CUs idle with one workgroup per 64 output rows: split K so that
-// each workgroup streams at most 16 steps (2048 codes). Large batches keep
-// one split (the partial outputs would cost more traffic than they save).
-int down_splits(int F, int64_t max_pairs) {
+// The down product of a small batch splits K so that the workgroups still
+// fill the GPU: the fewest splits (each workgroup streaming the longest run
+// of K steps) that give at least kFillWorkgroups workgroups for max_act
+// routed experts. Splits divide the d_ff/128 steps; at most max_splits.
+int down_splits(int F, int d, int max_act, int max_splits) {
+    constexpr int kFillWorkgroups = 1024;
     const int nblk = F / kStep;
-    if (max_pairs > 2048) return 1;
-    for (int n = 1; n <= nblk; ++n)
-        if (nblk % n == 0 && nblk / n <= 16) return n;
-    return 1;
+    const int64_t per_split = (int64_t)(max_act > 0 ? max_act : 1) * (d / 64);
+    int best = 1;
+    for (int n = 1; n <= nblk && n <= max_splits; ++n) {
+        if (nblk % n) continue;
+        best = n;
+        if (per_split * n >= kFillWorkgroups) break;
+    }
+    return best;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {

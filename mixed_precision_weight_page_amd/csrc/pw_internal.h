@@ -100,7 +100,7 @@ struct FfnPlan {
 };
 FfnPlan plan_ffn(int K, int T, int nsplit);
 // K-splits of the down product for a layer (partials summed by the combine)
-int down_splits(int F, int64_t max_pairs);
+int down_splits(int F, int d, int max_act, int max_splits);
 
 struct FfnArgs {
     const uint8_t* pool;

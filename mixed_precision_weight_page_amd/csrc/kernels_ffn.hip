@@ -133,44 +133,79 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_floa
 template <int MODE, int B>
 __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a,
                                       const int* tok, int hrow0, int nt, int k0, int kc) {
-    const int ngrp = kc / 32;
-    for (int idx = threadIdx.x; idx < nt * ngrp; idx += kThreads) {
-        const int n = idx / ngrp, grp = idx - n * ngrp;
-        _Float16 v[32];
-        if constexpr (MODE == 0) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 32 * grp);
+    if constexpr (B == 3) {
+        // the 3-bit order permutes across all 32 codes of a run
+        const int ngrp = kc / 32;
+        for (int idx = threadIdx.x; idx < nt * ngrp; idx += kThreads) {
+            const int n = idx / ngrp, grp = idx - n * ngrp;
+            _Float16 v[32];
+            if constexpr (MODE == 0) {
+                const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 32 * grp);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 u = src[q];
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 u = src[q];
+                    const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        v[8 * q + 2 * h] = (_Float16)bf16_to_f32((uint16_t)(ww[h] & 0xffffu));
+                        v[8 * q + 2 * h + 1] = (_Float16)bf16_to_f32((uint16_t)(ww[h] >> 16));
+                    }
+                }
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(a.w.H + (int64_t)(hrow0 + n) * a.F + k0 + 32 * grp);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    union {
+                        uint4 u;
+                        _Float16 h[8];
+                    } t;
+                    t.u = src[q];
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) v[8 * q + h] = t.h[h];
+                }
+            }
+            union {
+                uint4 u[4];
+                _Float16 h[32];
+            } o;
+#pragma unroll
+            for (int s = 0; s < 32; ++s) o.h[s] = v[perm_slot<B>(s)];
+            uint4* dst = reinterpret_cast<uint4*>(xs + n * stride + 32 * grp);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = o.u[q];
+        }
+    } else {
+        // 4- and 8-bit orders permute within groups of 8: one 16-byte chunk
+        // of 8 activations per thread and iteration
+        const int nch = kc / 8;
+        for (int idx = threadIdx.x; idx < nt * nch; idx += kThreads) {
+            const int n = idx / nch, ch = idx - n * nch;
+            _Float16 v[8];
+            if constexpr (MODE == 0) {
+                const uint4 u = *reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 8 * ch);
                 const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    v[8 * q + 2 * h] = (_Float16)bf16_to_f32((uint16_t)(ww[h] & 0xffffu));
-                    v[8 * q + 2 * h + 1] = (_Float16)bf16_to_f32((uint16_t)(ww[h] >> 16));
+                    v[2 * h] = (_Float16)bf16_to_f32((uint16_t)(ww[h] & 0xffffu));
+                    v[2 * h + 1] = (_Float16)bf16_to_f32((uint16_t)(ww[h] >> 16));
                 }
-            }
-        } else {
-            const uint4* src = reinterpret_cast<const uint4*>(a.w.H + (int64_t)(hrow0 + n) * a.F + k0 + 32 * grp);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            } else {
                 union {
                     uint4 u;
                     _Float16 h[8];
                 } t;
-                t.u = src[q];
+                t.u = *reinterpret_cast<const uint4*>(a.w.H + (int64_t)(hrow0 + n) * a.F + k0 + 8 * ch);
 #pragma unroll
-                for (int h = 0; h < 8; ++h) v[8 * q + h] = t.h[h];
+                for (int h = 0; h < 8; ++h) v[h] = t.h[h];
             }
+            union {
+                uint4 u;
+                _Float16 h[8];
+            } o;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) o.h[s] = v[perm_slot<B>(s)];
+            *reinterpret_cast<uint4*>(xs + n * stride + 8 * ch) = o.u;
         }
-        union {
-            uint4 u[4];
-            _Float16 h[32];
-        } o;
-#pragma unroll
-        for (int s = 0; s < 32; ++s) o.h[s] = v[perm_slot<B>(s)];
-        uint4* dst = reinterpret_cast<uint4*>(xs + n * stride + 32 * grp);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = o.u[q];
     }
 }
 

@@ -13,8 +13,11 @@ Plain, slow and written to be checked by eye against the pages:
              Quantization"): brute force and an exact dynamic programme.
 * ``moe``    the forward pass of section "Dynamic Paging": top-k router,
              SwiGLU experts on dequantized weights, weighted combine.
+* ``sched``  the KV-pressure budget scheduler (section "Implementation
+             Details", memory management): occupancy -> budget with
+             hysteresis.
 
 All floating-point arithmetic is float64 except where a rounding step is part
 of the definition (the fp32 scale, the bf16 activations).
 """
-from . import quant, alloc, moe  # noqa: F401
+from . import quant, alloc, moe, sched  # noqa: F401

@@ -155,6 +155,53 @@ pw_status pw_get_loss_table(pw_ctx* ctx, double* out, void* stream);
 pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, const double* L,
                               uint64_t budget_bits, uint8_t* bits_out);
 
+/* ---- KV-pressure budget scheduler ----
+ * The pool's budget follows the KV-cache occupancy (PagedWeight page,
+ * section "Implementation Details": the scheduler adjusts page sizes from
+ * the current KV-cache occupancy; the news digest's paging comparison:
+ * precision drops as the cache grows and comes back when pressure eases).
+ * Reading of the policy (the pages give none):
+ *   A = memory - kv_used - reserve bytes (at least 0) may hold the pool;
+ *   target = 8 * (floor(A * (1 - headroom)) - 256 * E) code bits (at least
+ *     0; a page is its codes rounded up to 256 bytes, so any allocation
+ *     within target fits in A), clamped to [3 W, 8 W], W = sum_e W_e;
+ *   INIT: no allocation yet -> target;
+ *   SHRINK: the current pool does not fit in A and target is lower than the
+ *     current budget -> target (never held back);
+ *   GROW: at least min_interval steps since the last change, target above
+ *     the current budget and >= ceil(budget * (1 + headroom)) -> target;
+ *   KEEP otherwise. pressure = 1 when even the all-3-bit pool does not fit
+ *   in A (the caller has to free KV cache). Fractions in double, floored. */
+typedef struct {
+    uint64_t memory_bytes;   /* bytes the weight pool and the KV cache share */
+    uint64_t reserve_bytes;  /* bytes kept free */
+    double headroom;         /* in [0, 0.5] */
+    int32_t min_interval;    /* >= 0: steps from a change to the next grow */
+} pw_budget_policy;
+
+enum { PW_BUDGET_KEEP = 0, PW_BUDGET_SHRINK = 1, PW_BUDGET_GROW = 2, PW_BUDGET_INIT = 3 };
+
+/* The decision alone (host only, no device work): W[E] weights per expert,
+ * pool_bytes_now = bytes of the current pages (sum of their 256-byte
+ * aligned sizes) and budget_now its budget, or UINT64_MAX and 0 before the
+ * first allocation; steps_since_change >= 0. Writes action, the budget to
+ * move to (budget_now on KEEP) and pressure. Errors: INVALID_ARG for null
+ * pointers, E <= 0, a W_e of 0, headroom outside [0, 0.5], min_interval < 0. */
+pw_status pw_budget_decide(const pw_budget_policy* policy, uint64_t kv_used_bytes, int32_t E,
+                           const uint64_t* W, uint64_t pool_bytes_now, uint64_t budget_now,
+                           int32_t steps_since_change, int32_t* action, uint64_t* budget_out,
+                           int32_t* pressure);
+
+/* One scheduler step on a layer: the decision from the layer's pages (their
+ * bytes; the budget of the last scheduler move, or the bits of pages set by
+ * pw_quantize_experts) and the steps since the last move; on INIT, SHRINK or
+ * GROW it calls pw_set_budget with importance and loss (host, as there) on
+ * stream. The step counter advances only on KEEP. A failed pw_set_budget
+ * leaves pages, table and scheduler state unchanged and returns its status. */
+pw_status pw_budget_step(pw_ctx* ctx, const pw_budget_policy* policy, uint64_t kv_used_bytes,
+                         const double* importance, const double* loss, int32_t* action,
+                         uint64_t* budget_out, int32_t* pressure, void* stream);
+
 /* Timing of the forward kernels on the forward's stream: each timed kernel
  * is launched with start/stop HIP events stamped by its own dispatch
  * (hipExtLaunchKernel). mask selects the kernels: bit 0 router/grouping,

@@ -3,5 +3,6 @@
 The compute path is libpagedweight.so (HIP kernels for gfx950 behind the C
 ABI in include/pagedweight.h); this package only binds it.
 """
-from .pagedweight import (BITS, PagedMoELayer, PagedWeightError, lib, library_path,  # noqa: F401
+from .pagedweight import (BITS, BUDGET_GROW, BUDGET_INIT, BUDGET_KEEP, BUDGET_SHRINK,  # noqa: F401
+                          PagedMoELayer, PagedWeightError, budget_decide, lib, library_path,
                           solve_allocation)

@@ -55,6 +55,11 @@ struct pw_ctx {
     hipEvent_t upload_done = nullptr;
     int cur = 0;                // active device table
 
+    // budget of the current pages (set by pw_set_budget; the bits' total
+    // after pw_quantize_experts) and pw_budget_step calls since they changed
+    uint64_t budget_now = 0;
+    int32_t steps_since_change = 0;
+
     // profiling
     int profile_mask = 0;      // bit 0 route, 1 gate/up, 2 down, 3 combine
     std::vector<hipEvent_t> ev_pool;
@@ -489,7 +494,11 @@ pw_status pw_quantize_experts(pw_ctx* c, const uint8_t* bits, void* stream) {
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = ensure_absmax(c, s)) != PW_OK) return st;
-    return apply_bits(c, bits, s);
+    if ((st = apply_bits(c, bits, s)) != PW_OK) return st;
+    c->budget_now = 0;
+    for (int e = 0; e < c->E; ++e) c->budget_now += (uint64_t)bits[e] * c->We;
+    c->steps_since_change = 0;
+    return PW_OK;
 }
 
 pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importance,
@@ -514,7 +523,37 @@ pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importanc
     st = solve_allocation(c->E, W.data(), importance, L, budget_bits, bits.data(), &c->err);
     if (st != PW_OK) return st;
     if ((st = apply_bits(c, bits.data(), s)) != PW_OK) return st;
+    c->budget_now = budget_bits;
+    c->steps_since_change = 0;
     if (bits_out) std::memcpy(bits_out, bits.data(), c->E);
+    return PW_OK;
+}
+
+pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_used_bytes,
+                         const double* importance, const double* loss, int32_t* action,
+                         uint64_t* budget_out, int32_t* pressure, void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!policy || !importance || !action || !budget_out || !pressure)
+        return fail(c, PW_ERR_INVALID_ARG, "null policy, importance or output pointer");
+    uint64_t pool_now = UINT64_MAX;
+    if (c->pages_valid) {
+        pool_now = 0;
+        for (int e = 0; e < c->E; ++e) pool_now += c->table[e].nbytes;
+    }
+    std::vector<uint64_t> W(c->E, c->We);
+    int32_t act = PW_BUDGET_KEEP, press = 0;
+    uint64_t target = 0;
+    pw_status st = pw_budget_decide(policy, kv_used_bytes, c->E, W.data(), pool_now, c->budget_now,
+                                    c->steps_since_change, &act, &target, &press);
+    if (st != PW_OK) return fail(c, st, "invalid budget policy");
+    if (act != PW_BUDGET_KEEP) {
+        if ((st = pw_set_budget(c, target, importance, loss, nullptr, stream)) != PW_OK) return st;
+    } else {
+        c->steps_since_change++;
+    }
+    *action = act;
+    *budget_out = target;
+    *pressure = press;
     return PW_OK;
 }
 

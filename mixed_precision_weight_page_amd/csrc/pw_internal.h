@@ -102,6 +102,11 @@ FfnPlan plan_ffn(int K, int T, int nsplit);
 // K-splits of the down product for a layer (partials summed by the combine)
 int down_splits(int F, int d, int max_act, int max_splits);
 
+// KV-pressure budget scheduler decision (budget.cpp); arguments checked by the caller.
+pw_status budget_decide(const pw_budget_policy& pol, uint64_t kv_used, int E, const uint64_t* W,
+                        uint64_t pool_now, uint64_t budget_now, int steps_since, int32_t* action,
+                        uint64_t* budget_out, int32_t* pressure);
+
 struct FfnArgs {
     const uint8_t* pool;
     DevTable tab;

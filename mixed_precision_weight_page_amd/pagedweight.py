@@ -48,6 +48,15 @@ class ProfileData(ctypes.Structure):
                 ("forwards", ctypes.c_int64)]
 
 
+class BudgetPolicy(ctypes.Structure):
+    """pw_budget_policy: memory shared by the pool and the KV cache, bytes
+    kept free, headroom fraction, steps from a change to the next grow."""
+    _fields_ = [("memory_bytes", ctypes.c_uint64), ("reserve_bytes", ctypes.c_uint64),
+                ("headroom", ctypes.c_double), ("min_interval", ctypes.c_int32)]
+
+
+BUDGET_KEEP, BUDGET_SHRINK, BUDGET_GROW, BUDGET_INIT = 0, 1, 2, 3
+
 _P = ctypes.c_void_p
 _SIGNATURES = {
     "pw_create": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(_P)]),
@@ -64,6 +73,9 @@ _SIGNATURES = {
     "pw_get_page_table": (ctypes.c_int, [_P, ctypes.POINTER(PageEntry)]),
     "pw_get_loss_table": (ctypes.c_int, [_P, _P, _P]),
     "pw_solve_allocation": (ctypes.c_int, [ctypes.c_int32, _P, _P, _P, ctypes.c_uint64, _P]),
+    "pw_budget_decide": (ctypes.c_int, [ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, ctypes.c_int32, _P,
+                                        ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, _P, _P, _P]),
+    "pw_budget_step": (ctypes.c_int, [_P, ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, _P, _P, _P, _P, _P, _P]),
     "pw_profile": (ctypes.c_int, [_P, ctypes.c_int32]),
     "pw_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(ProfileData)]),
     "pw_last_error": (ctypes.c_char_p, [_P]),
@@ -134,6 +146,29 @@ def solve_allocation(W: Sequence[int], p: Sequence[float], L, budget_bits: int) 
     return out
 
 
+NO_POOL = (1 << 64) - 1   # pool_bytes_now before the first allocation
+
+
+def _policy(memory_bytes, reserve_bytes, headroom, min_interval) -> BudgetPolicy:
+    return BudgetPolicy(int(memory_bytes), int(reserve_bytes), float(headroom), int(min_interval))
+
+
+def budget_decide(memory_bytes: int, reserve_bytes: int, headroom: float, min_interval: int,
+                  kv_used_bytes: int, W: Sequence[int], pool_bytes_now: Optional[int],
+                  budget_now: Optional[int], steps_since_change: int):
+    """pw_budget_decide (host only): (action, budget_bits, pressure)."""
+    E = len(W)
+    Wa = _host_array(W, np.uint64, E, "W")
+    pol = _policy(memory_bytes, reserve_bytes, headroom, min_interval)
+    act, press = ctypes.c_int32(0), ctypes.c_int32(0)
+    out = ctypes.c_uint64(0)
+    _check(lib().pw_budget_decide(ctypes.byref(pol), int(kv_used_bytes), E, Wa.ctypes.data,
+                                  NO_POOL if pool_bytes_now is None else int(pool_bytes_now),
+                                  0 if budget_now is None else int(budget_now), int(steps_since_change),
+                                  ctypes.byref(act), ctypes.byref(out), ctypes.byref(press)))
+    return act.value, out.value, bool(press.value)
+
+
 class PagedMoELayer:
     """One MoE expert layer bound to its masters, pool and workspace."""
 
@@ -193,6 +228,20 @@ class PagedMoELayer:
                                    None if L is None else L.ctypes.data, out.ctypes.data,
                                    _stream(stream)), self._ctx)
         return out
+
+    def budget_step(self, memory_bytes: int, reserve_bytes: int, headroom: float, min_interval: int,
+                    kv_used_bytes: int, importance, loss=None, stream=None):
+        """pw_budget_step: one KV-pressure scheduler step (re-quantizes on
+        INIT, SHRINK and GROW). Returns (action, budget_bits, pressure)."""
+        p = _host_array(importance, np.float64, self.E, "importance")
+        L = None if loss is None else np.ascontiguousarray(np.asarray(loss, dtype=np.float64).reshape(self.E * 3))
+        pol = _policy(memory_bytes, reserve_bytes, headroom, min_interval)
+        act, press = ctypes.c_int32(0), ctypes.c_int32(0)
+        out = ctypes.c_uint64(0)
+        _check(lib().pw_budget_step(self._ctx, ctypes.byref(pol), int(kv_used_bytes), p.ctypes.data,
+                                    None if L is None else L.ctypes.data, ctypes.byref(act),
+                                    ctypes.byref(out), ctypes.byref(press), _stream(stream)), self._ctx)
+        return act.value, out.value, bool(press.value)
 
     def moe_forward(self, x: torch.Tensor, logits: torch.Tensor, y: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:

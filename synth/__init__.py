@@ -15,6 +15,9 @@ Workloads (all SwiGLU experts; W1 = gate, W3 = up, W2 = down):
 * ``dynamic``        the decode_fine layer with fp16 masters and a budget
                      stepped through avg 8, 6, 4, 3.5, 5 bits every 8 steps
 
+``kv_trace`` draws a KV-cache occupancy trace (sequences arriving, growing
+and finishing) for the budget scheduler.
+
 Distributions: weights N(0, 0.02) in fp32 (optionally with Bernoulli outliers
 multiplied by 20, optionally rounded to fp16), router logits N(0, 1) in fp32,
 activations N(0, 1) rounded to bf16 (round to nearest even), expert
@@ -143,3 +146,20 @@ def importance(wl: Workload):
         import numpy as np
         return np.full(wl.E, 1.0 / wl.E)
     return zipf_importance(wl.E, wl.zipf_s)
+
+
+def kv_trace(steps: int, kv_peak_bytes: int, seed: int = 0, name: str = "kv"):
+    """KV-cache occupancy in bytes over ``steps`` decode steps: sequences
+    arrive (probability 0.35 per step, with a prompt of 1..64 tokens), grow by
+    one token per step and finish (probability 0.04 per step); a token takes
+    kv_peak_bytes / 1024 bytes. Occupancy is capped at kv_peak_bytes."""
+    import random
+    rng = random.Random(_seed(seed, name, steps, kv_peak_bytes))
+    per_token = max(1, kv_peak_bytes // 1024)
+    live, out = [], []
+    for _ in range(steps):
+        if rng.random() < 0.35:
+            live.append(rng.randrange(1, 65))
+        out.append(min(kv_peak_bytes, sum(live) * per_token))
+        live = [t + 1 for t in live if rng.random() >= 0.04]
+    return out

@@ -183,3 +183,68 @@ def test_python_binding_raises_with_status(L):
         layer.quantize_experts([3, 4, 8, 4], stream=0)
     assert ei.value.status == STATE
     assert "masters" in str(ei.value)
+
+
+# ---- KV-pressure budget scheduler: the decision is host code ----
+from oracle import sched  # noqa: E402
+
+
+def _decide_both(args):
+    got = pwb.budget_decide(*args)
+    want = sched.decide(*args[:5], args[5], args[6], args[7], args[8])
+    return got, want
+
+
+def test_budget_decide_hand_trace_matches_oracle(L):
+    W = [1000, 1000]
+    M, R, h, n = 4000, 0, 0.1, 2
+    cases = [(0, None, None, 0), (1000, 2048, 16000, 1), (1952, 2048, 16000, 1),
+             (2000, 2048, 16000, 2), (3100, 1024, 10304, 0), (3100, 1024, 6000, 0),
+             (0, 1024, 6000, 1), (0, 1024, 6000, 2), (2400, 1024, 7000, 5), (2300, 1024, 7000, 5)]
+    for kv, pool, budget, since in cases:
+        got, want = _decide_both((M, R, h, n, kv, W, pool, budget, since))
+        assert got == want, (kv, pool, budget, since)
+
+
+def test_budget_decide_random_matches_oracle(L):
+    rng = random.Random(11)
+    for _ in range(4000):
+        E = rng.randrange(1, 130)
+        scale = rng.choice([1, 1000, 3 * 4096 * 14336])
+        W = [rng.randrange(1, 400) * scale for _ in range(E)]
+        total = sum(W)
+        memory = rng.randrange(0, 3 * total + 2)
+        reserve = rng.randrange(0, total // 2 + 2)
+        kv = rng.randrange(0, memory + 2)
+        h = rng.choice([0.0, 0.01, 0.05, 0.1, 0.3, 0.5])
+        n = rng.randrange(0, 6)
+        if rng.random() < 0.1:
+            pool = budget = None
+        else:
+            budget = rng.randrange(3 * total, 8 * total + 1)
+            pool = rng.randrange(0, budget // 8 + 256 * E + 2)
+        since = rng.randrange(0, 8)
+        got, want = _decide_both((memory, reserve, h, n, kv, W, pool, budget, since))
+        assert got == want, (E, memory, reserve, kv, h, n, pool, budget, since)
+
+
+def test_budget_decide_argument_errors(L):
+    W = (ctypes.c_uint64 * 2)(1000, 1000)
+    act, press = ctypes.c_int32(0), ctypes.c_int32(0)
+    out = ctypes.c_uint64(0)
+    ok = pwb.BudgetPolicy(4000, 0, 0.1, 2)
+
+    def call(pol, E=2, w=W, since=0):
+        return L.pw_budget_decide(ctypes.byref(pol) if pol is not None else None, 0, E, w,
+                                  pwb.NO_POOL, 0, since, ctypes.byref(act), ctypes.byref(out),
+                                  ctypes.byref(press))
+    assert call(ok) == PW_OK and act.value == pwb.BUDGET_INIT
+    assert call(None) == INVALID
+    assert call(ok, E=0) == INVALID
+    assert call(ok, w=None) == INVALID
+    assert call(ok, since=-1) == INVALID
+    assert call(pwb.BudgetPolicy(4000, 0, 0.6, 2)) == INVALID
+    assert call(pwb.BudgetPolicy(4000, 0, -0.1, 2)) == INVALID
+    assert call(pwb.BudgetPolicy(4000, 0, float("nan"), 2)) == INVALID
+    assert call(pwb.BudgetPolicy(4000, 0, 0.1, -1)) == INVALID
+    assert call(ok, w=(ctypes.c_uint64 * 2)(1000, 0)) == INVALID

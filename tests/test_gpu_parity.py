@@ -9,6 +9,7 @@ import torch
 import synth
 from layer_cases import (check_pages, compare_y, cpu_threads, log, make_layer, oracle_bits,
                          oracle_y)
+from oracle import sched as osched
 from oracle import alloc, moe, quant
 
 pytestmark = pytest.mark.gpu
@@ -257,6 +258,48 @@ def test_rounding_ties_and_neighbours():
     for e, j in enumerate((8, 5, 4)):
         assert layer.get_page_table()[e]["scale"] == 2.0 ** -j
     check_pages(layer, pool, masters, wl.bits)
+
+
+def test_budget_scheduler_follows_a_kv_trace():
+    """The KV-pressure scheduler (reading in include/pagedweight.h) on a
+    layer with fp16 masters over 48 decode steps of a synthetic KV-cache
+    trace: each step's action and budget equal the oracle's decision from
+    the oracle's own state; after every move the allocation (Eq. 1) and the
+    pages are the oracle's and the pool fits in the memory left."""
+    wl = SMALL_DYN
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    p = synth.importance(wl)
+    _, Ltab = quant.loss_table(*masters)
+    W = [wl.W_e] * wl.E
+    pool8 = osched.pool_nbytes(W, [8] * wl.E)
+    memory, reserve, h, n = pool8 + pool8 // 8, pool8 // 16, 0.05, 3
+    trace = synth.kv_trace(48, pool8)
+    o_pool = o_budget = None
+    o_since = 0
+    seen = set()
+    for t, kv in enumerate(trace):
+        got = layer.budget_step(memory, reserve, h, n, kv, p)
+        want = osched.decide(memory, reserve, h, n, kv, W, o_pool, o_budget, o_since)
+        assert got == want, (t, kv, got, want)
+        action, B, pressure = got
+        seen.add(action)
+        if action != osched.KEEP:
+            bits_want, _ = alloc.solve(p, Ltab.tolist(), W, B)
+            table = layer.get_page_table()
+            bits = [int(e["bits"]) for e in table]
+            assert bits == list(bits_want), t
+            o_pool, o_budget, o_since = osched.pool_nbytes(W, bits), B, 0
+            assert sum(int(e["nbytes"]) for e in table) == o_pool
+            if not pressure:
+                assert o_pool <= memory - kv - reserve
+            check_pages(layer, pool, masters, bits, rows_per_matrix=2)
+        else:
+            o_since += 1
+    assert {osched.INIT, osched.SHRINK, osched.GROW, osched.KEEP} <= seen, seen
+    x, logits = synth.tokens(wl)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, bits), "after the KV trace")
 
 
 def test_mostly_zero_codes_keep_precision():

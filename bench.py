@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_coarse",
-                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "tiny"])
+                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "kvtrace", "tiny"])
     ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")
     ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,6 +224,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
+    if args.workload == "kvtrace":
+        return bench_kvtrace(args, synth.WORKLOADS["dynamic"], log)
     wl = synth.WORKLOADS[args.workload]
     if args.workload == "dynamic":
         return bench_dynamic(args, wl, log)
@@ -351,6 +353,58 @@ def bench_dynamic(args, wl, log):
                                   "masters, budget avg 8->6->4->3.5->5 bits every 8 steps"},
            "requant_GBps": req_bytes / t_req / 1e9 if t_req else None,
            "requant_s_total": t_req}
+    print(json.dumps(out), flush=True)
+
+
+def bench_kvtrace(args, wl, log):
+    """The dynamic layer (fp16 masters) under the KV-pressure budget
+    scheduler: 128 decode steps of 64 tokens (the first, which makes the first
+    allocation, untimed); before each forward one
+    pw_budget_step with the KV-cache occupancy of a synthetic trace (peaking
+    near the all-8-bit pool size; memory = the all-8-bit pool plus 1/8,
+    reserve 1/16, headroom 5%, at least 4 steps between a change and a grow).
+    Reports end-to-end tokens/s including the re-quantizations."""
+    import torch
+
+    import synth
+    from mixed_precision_weight_page_amd import BUDGET_KEEP, PagedMoELayer
+    masters = synth.expert_weights(wl, device="cuda")
+    layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=wl.T, master_dtype=wl.master)
+    layer.bind_masters(*masters)
+    pool8 = layer.pool_bytes_for_bits([8] * wl.E)
+    layer.alloc_pool(pool8)
+    layer.alloc_workspace()
+    p = synth.importance(wl)
+    layer.get_loss_table()            # statistics measured once, outside the timed steps
+    memory, reserve, h, n = pool8 + pool8 // 8, pool8 // 16, 0.05, 4
+    steps = 128
+    trace = synth.kv_trace(steps, pool8)
+    batches = [synth.tokens(wl, device="cuda", step=i) for i in range(8)]
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    layer.budget_step(memory, reserve, h, n, trace[0], p)      # first allocation (INIT), untimed
+    for _ in range(args.warmup):
+        layer.moe_forward(*batches[0], y)
+    torch.cuda.synchronize()
+    actions, bits_sum = [], 0.0
+    t0 = time.perf_counter()
+    for i in range(1, steps):
+        act, B, pressure = layer.budget_step(memory, reserve, h, n, trace[i], p)
+        actions.append(act)
+        bits_sum += B / (wl.E * wl.W_e)
+        layer.moe_forward(*batches[i % 8], y)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    changes = sum(1 for a in actions if a != BUDGET_KEEP)
+    timed = steps - 1
+    out = {"metric": METRIC, "value": wl.T * timed / el, "unit": "tokens/s", "n_gpus": 1,
+           "steps": timed, "warmup": args.warmup, "ms_per_step": 1e3 * el / timed,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": "kvtrace: dynamic layer (E=128, d_model=2048, d_ff=768, top-8, 64 tokens, "
+                                  "fp16 masters) under the KV-pressure budget scheduler over a synthetic "
+                                  "KV-cache trace"},
+           "budget_changes": changes, "shrinks": actions.count(1), "grows": actions.count(2),
+           "mean_budget_bits_per_weight": bits_sum / timed}
     print(json.dumps(out), flush=True)
 
 

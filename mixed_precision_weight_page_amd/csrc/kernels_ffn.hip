@@ -92,8 +92,31 @@ __device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, u
 
 // The 16 fp16 pairs (each "1024 + code") of a 3-bit group of 32 codes held
 // in three dwords; pair p = (slot 2p, slot 2p+1) of the staging permutation.
-__device__ __forceinline__ void pairs3(const uint32_t* w, uint32_t p[16]) {
-    const uint32_t M3 = 0x00070007u;
+// A 32-bit constant held in a VGPR. A VOP3 instruction on this target can
+// read at most one SGPR or literal, so with the masks and the exponent
+// pattern in VGPRs each (w & mask) | magic is one v_and_or_b32 instead of a
+// v_and plus a v_or.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+struct DeqConst {
+    uint32_t magic;   // 0x64006400: fp16 1024 in both halves
+    uint32_t m4;      // 0x000f000f
+    uint32_t m3;      // 0x00070007
+    uint32_t e8;      // 0x64646464: exponent byte for v_perm_b32
+};
+
+__device__ __forceinline__ DeqConst deq_const() {
+    return DeqConst{vgpr_const(kMagic), vgpr_const(0x000f000fu), vgpr_const(0x00070007u),
+                    vgpr_const(0x64646464u)};
+}
+
+__device__ __forceinline__ void pairs3(const uint32_t* w, uint32_t p[16], const DeqConst& c) {
+    const uint32_t M3 = c.m3;
+    const uint32_t kMagic = c.magic;
     const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
     const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
     const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
@@ -214,18 +237,20 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
 template <int B>
 __device__ __forceinline__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
 
-// A fragment i (K-slots 8i..8i+7 of the lane's 32 codes) of a 4- or 8-bit step
+// A fragment i (K-slots 8i..8i+7 of the lane's 32 codes) of a 4- or 8-bit
+// step. 8-bit: bytes (b0, 0x64, b2, 0x64) and (b1, 0x64, b3, 0x64) of each
+// word by v_perm_b32 (selector bytes 0-3 pick from the word, 4 from the
+// exponent pattern).
 template <int B>
-__device__ __forceinline__ half8_t frag(const Codes<B>& c, int i) {
+__device__ __forceinline__ half8_t frag(const Codes<B>& cd, int i, const DeqConst& c) {
     if constexpr (B == 4) {
-        const uint32_t w = c.w[i];
-        return to_frag((w & 0x000f000fu) | kMagic, ((w >> 4) & 0x000f000fu) | kMagic,
-                       ((w >> 8) & 0x000f000fu) | kMagic, ((w >> 12) & 0x000f000fu) | kMagic,
-                       (_Float16)1032.0f);
+        const uint32_t w = cd.w[i];
+        return to_frag((w & c.m4) | c.magic, ((w >> 4) & c.m4) | c.magic, ((w >> 8) & c.m4) | c.magic,
+                       ((w >> 12) & c.m4) | c.magic, (_Float16)1032.0f);
     } else {
-        const uint32_t w0 = c.w[2 * i], w1 = c.w[2 * i + 1];
-        return to_frag((w0 & 0x00ff00ffu) | kMagic, ((w0 >> 8) & 0x00ff00ffu) | kMagic,
-                       (w1 & 0x00ff00ffu) | kMagic, ((w1 >> 8) & 0x00ff00ffu) | kMagic,
+        const uint32_t w0 = cd.w[2 * i], w1 = cd.w[2 * i + 1];
+        return to_frag(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u), __builtin_amdgcn_perm(c.e8, w0, 0x04030401u),
+                       __builtin_amdgcn_perm(c.e8, w1, 0x04020400u), __builtin_amdgcn_perm(c.e8, w1, 0x04030401u),
                        (_Float16)1152.0f);
     }
 }
@@ -234,11 +259,11 @@ __device__ __forceinline__ half8_t frag(const Codes<B>& c, int i) {
 // step's 128 staged activations of this lane's token row and K-group.
 template <int B, int NMAT>
 __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* bp,
-                                         f32x4 (&acc)[NMAT]) {
+                                         f32x4 (&acc)[NMAT], const DeqConst& dc) {
     if constexpr (B == 3) {
         uint32_t pr[NMAT][16];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) pairs3(cur[m].w, pr[m]);
+        for (int m = 0; m < NMAT; ++m) pairs3(cur[m].w, pr[m], dc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
@@ -255,7 +280,7 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
             const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag<B>(cur[m], i), bfr, acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag<B>(cur[m], i, dc), bfr, acc[m], 0, 0, 0);
         }
     }
 }
@@ -282,6 +307,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
+    const DeqConst dc = deq_const();
     // this wave's 16-row block is one contiguous run of K/128 tiles
     const uint8_t* ap[NMAT];
 #pragma unroll
@@ -333,7 +359,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                     cur[m] = buf[m][j];
                     buf[m][j] = load_codes<B>(ap[m] + (int64_t)(s0 + j + PD) * SB);
                 }
-                step_mma<B, NMAT>(cur, bp + j * kStep, acc);
+                step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
             }
         }
         for (; s0 < nsteps; s0 += PD) {   // last 1..2 groups: no loads past the end
@@ -354,7 +380,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                         cur[m] = buf[m][j];
                         if (st + PD < nsteps) buf[m][j] = load_codes<B>(ap[m] + (int64_t)(st + PD) * SB);
                     }
-                    step_mma<B, NMAT>(cur, bp + j * kStep, acc);
+                    step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
                 }
             }
         }

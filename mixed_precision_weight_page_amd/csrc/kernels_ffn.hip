@@ -75,27 +75,22 @@ __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
     return c;
 }
 
-// Four dwords, each holding two fp16 values 1024 + u (the code u ORed into
-// the mantissa of 1024), minus 1024 + 2^(B-1): the exact signed code q in
-// fp16 (one packed subtract per pair). Exact q keeps the MFMA sums free of
-// the offset 2^(B-1) sum(x), which would otherwise dominate them when most
-// codes are 0 (weights far below an expert's largest weight).
-__device__ __forceinline__ half8_t to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                           _Float16 bias) {
-    union {
-        uint32_t u[4];
-        half8_t h;
-    } x;
-    x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
-    return x.h - bias;
-}
+// Dequantization to exact fp16 integers. A code u placed in the mantissa of
+// fp16 1024 (exponent pattern 0x6400) at bit S <= 7 of a 16-bit half gives the
+// exact value 1024 + 2^S u; a fused multiply-add by 2^-S minus
+// 2^(10-S) + 2^(B-1) then yields the signed code q = u - 2^(B-1) exactly (for
+// S = 0 a plain subtract). Exact q keeps the MFMA sums free of the offset
+// 2^(B-1) sum(x), which would otherwise dominate them when most codes are 0
+// (weights far below an expert's largest weight). Allowing S > 0 saves the
+// shift that would bring each code down to bit 0: one v_and_or_b32 per pair
+// of codes plus one packed fp16 operation.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// The 16 fp16 pairs (each "1024 + code") of a 3-bit group of 32 codes held
-// in three dwords; pair p = (slot 2p, slot 2p+1) of the staging permutation.
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
 // A 32-bit constant held in a VGPR. A VOP3 instruction on this target can
-// read at most one SGPR or literal, so with the masks and the exponent
-// pattern in VGPRs each (w & mask) | magic is one v_and_or_b32 instead of a
-// v_and plus a v_or.
+// read at most one SGPR or literal: with the exponent pattern in a VGPR,
+// (w & mask) | magic is one v_and_or_b32 with the mask as the SGPR operand.
 __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
     uint32_t r;
     asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
@@ -104,32 +99,64 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
 
 struct DeqConst {
     uint32_t magic;   // 0x64006400: fp16 1024 in both halves
-    uint32_t m4;      // 0x000f000f
-    uint32_t m3;      // 0x00070007
     uint32_t e8;      // 0x64646464: exponent byte for v_perm_b32
 };
 
 __device__ __forceinline__ DeqConst deq_const() {
-    return DeqConst{vgpr_const(kMagic), vgpr_const(0x000f000fu), vgpr_const(0x00070007u),
-                    vgpr_const(0x64646464u)};
+    return DeqConst{vgpr_const(kMagic), vgpr_const(0x64646464u)};
 }
 
-__device__ __forceinline__ void pairs3(const uint32_t* w, uint32_t p[16], const DeqConst& c) {
-    const uint32_t M3 = c.m3;
-    const uint32_t kMagic = c.magic;
-    const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
-    const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
-    const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
-#pragma unroll
-    for (int j = 0; j < 5; ++j) p[j] = ((v01 >> (3 * j)) & M3) | kMagic;          // (j, j+16)
-    p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u) |
-           kMagic;                                                                 // (5, 21)
-#pragma unroll
-    for (int j = 6; j < 10; ++j) p[j] = ((v02 >> (3 * j - 16)) & M3) | kMagic;    // (j+16, j)
-    p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u) |
-            kMagic;                                                                // (10, 26)
-#pragma unroll
-    for (int j = 11; j < 16; ++j) p[j] = ((v12 >> (3 * j - 32)) & M3) | kMagic;   // (j, j+16)
+// The two B-bit codes at bit S of each 16-bit half of x, as exact signed
+// fp16 values (low half, high half).
+template <int B, int S>
+__device__ __forceinline__ half2_t code_pair(uint32_t x, const DeqConst& c) {
+    constexpr uint32_t mask = ((1u << B) - 1u) * 0x00010001u << S;
+    const half2_t v = as_half2((x & mask) | c.magic);
+    if constexpr (S == 0) {
+        constexpr _Float16 bias = (_Float16)(1024 + (1 << (B - 1)));
+        return v - half2_t{bias, bias};
+    } else {
+        constexpr _Float16 m = (_Float16)(1.0f / (1 << S));
+        constexpr _Float16 bias = (_Float16)(-(float)((1024 >> S) + (1 << (B - 1))));
+        return __builtin_elementwise_fma(v, half2_t{m, m}, half2_t{bias, bias});
+    }
+}
+
+__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
+    return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
+                                   __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The 16 signed pairs of a 3-bit group of 32 codes held in three dwords
+// (code c at bits 3c..3c+2); pair p = (slot 2p, slot 2p+1) of the staging
+// permutation. Half-words of two dwords are merged so that codes j and
+// j + 16 sit at the same offset of the two halves.
+__device__ __forceinline__ void pairs3(const uint32_t* w, half2_t p[16], const DeqConst& c) {
+    const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);   // codes 0-4 | 16-20 at 3j
+    const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);   // codes 22-25 | 6-9 at 3j-16
+    const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);   // codes 11-15 | 27-31 at 3j-32
+    // every code is taken at bit 0, 3 or 6 of its half (two multiply-add
+    // constants in registers instead of seven)
+    const uint32_t t01 = v01 >> 9, t02 = v02 >> 2, u02 = v02 >> 11, t12 = v12 >> 1, u12 = v12 >> 10;
+    p[0] = code_pair<3, 0>(v01, c);    // (0, 16)
+    p[1] = code_pair<3, 3>(v01, c);    // (1, 17)
+    p[2] = code_pair<3, 6>(v01, c);    // (2, 18)
+    p[3] = code_pair<3, 0>(t01, c);    // (3, 19)
+    p[4] = code_pair<3, 3>(t01, c);    // (4, 20)
+    // code 5 (bits 15-17) and code 21 (bits 63-65) straddle dword boundaries
+    p[5] = code_pair<3, 0>((w[0] >> 15 & 0xffffu) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0xffff0000u), c);
+    p[6] = code_pair<3, 0>(t02, c);    // (22, 6)
+    p[7] = code_pair<3, 3>(t02, c);    // (23, 7)
+    p[8] = code_pair<3, 6>(t02, c);    // (24, 8)
+    p[9] = code_pair<3, 0>(u02, c);    // (25, 9)
+    // code 10 (bits 30-32) and code 26 (bits 78-80)
+    p[10] = code_pair<3, 0>((__builtin_amdgcn_alignbit(w[1], w[0], 30) & 0xffffu) |
+                                (__builtin_amdgcn_alignbit(w[2], w[1], 30) & 0xffff0000u), c);
+    p[11] = code_pair<3, 0>(t12, c);   // (11, 27)
+    p[12] = code_pair<3, 3>(t12, c);   // (12, 28)
+    p[13] = code_pair<3, 6>(t12, c);   // (13, 29)
+    p[14] = code_pair<3, 0>(u12, c);   // (14, 30)
+    p[15] = code_pair<3, 3>(u12, c);   // (15, 31)
 }
 
 // Code (within a 32-code group) whose activation goes to LDS slot s.
@@ -238,20 +265,22 @@ template <int B>
 __device__ __forceinline__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
 
 // A fragment i (K-slots 8i..8i+7 of the lane's 32 codes) of a 4- or 8-bit
-// step. 8-bit: bytes (b0, 0x64, b2, 0x64) and (b1, 0x64, b3, 0x64) of each
-// word by v_perm_b32 (selector bytes 0-3 pick from the word, 4 from the
-// exponent pattern).
+// step. 4-bit: nibbles (0, 4), (1, 5), (2, 6), (3, 7) of dword i. 8-bit:
+// bytes (0, 2) and (1, 3) of dwords 2i and 2i + 1, moved next to the
+// exponent byte by v_perm_b32 (selector bytes 0-3 pick from the dword, 4
+// from the exponent pattern).
 template <int B>
 __device__ __forceinline__ half8_t frag(const Codes<B>& cd, int i, const DeqConst& c) {
     if constexpr (B == 4) {
-        const uint32_t w = cd.w[i];
-        return to_frag((w & c.m4) | c.magic, ((w >> 4) & c.m4) | c.magic, ((w >> 8) & c.m4) | c.magic,
-                       ((w >> 12) & c.m4) | c.magic, (_Float16)1032.0f);
+        const uint32_t w = cd.w[i], t = w >> 8;
+        return cat(code_pair<4, 0>(w, c), code_pair<4, 4>(w, c), code_pair<4, 0>(t, c), code_pair<4, 4>(t, c));
     } else {
         const uint32_t w0 = cd.w[2 * i], w1 = cd.w[2 * i + 1];
-        return to_frag(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u), __builtin_amdgcn_perm(c.e8, w0, 0x04030401u),
-                       __builtin_amdgcn_perm(c.e8, w1, 0x04020400u), __builtin_amdgcn_perm(c.e8, w1, 0x04030401u),
-                       (_Float16)1152.0f);
+        const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+        return cat(as_half2(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u)) - bias,
+                   as_half2(__builtin_amdgcn_perm(c.e8, w0, 0x04030401u)) - bias,
+                   as_half2(__builtin_amdgcn_perm(c.e8, w1, 0x04020400u)) - bias,
+                   as_half2(__builtin_amdgcn_perm(c.e8, w1, 0x04030401u)) - bias);
     }
 }
 
@@ -261,7 +290,7 @@ template <int B, int NMAT>
 __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* bp,
                                          f32x4 (&acc)[NMAT], const DeqConst& dc) {
     if constexpr (B == 3) {
-        uint32_t pr[NMAT][16];
+        half2_t pr[NMAT][16];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) pairs3(cur[m].w, pr[m], dc);
 #pragma unroll
@@ -270,9 +299,8 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    to_frag(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3],
-                            (_Float16)1028.0f),
-                    bfr, acc[m], 0, 0, 0);
+                    cat(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]), bfr, acc[m], 0, 0,
+                    0);
         }
     } else {
 #pragma unroll
@@ -362,7 +390,12 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
                 step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
             }
         }
-        for (; s0 < nsteps; s0 += PD) {   // last 1..2 groups: no loads past the end
+        // The last one or two groups. A group that still has loads to issue
+        // clamps their addresses to the last tile (the loads past the end
+        // are never used; a conditional load would make the ring slot's old
+        // value need a copy while it is still being consumed). The final
+        // group issues no loads.
+        if (nsteps - s0 > PD) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
                 stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
@@ -372,14 +405,30 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
             const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
             for (int j = 0; j < PD; ++j) {
-                const int st = s0 + j;
-                if (st < nsteps) {
+                Codes<B> cur[NMAT];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    cur[m] = buf[m][j];
+                    buf[m][j] = load_codes<B>(ap[m] + (int64_t)min(s0 + j + PD, nsteps - 1) * SB);
+                }
+                step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
+            }
+            s0 += PD;
+        }
+        if (s0 < nsteps) {
+            if (s0 != 0 && s0 % spc == 0) {
+                __syncthreads();
+                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                               min(spc, nsteps - s0) * kStep);
+                __syncthreads();
+            }
+            const _Float16* bp = bp0 + (s0 % spc) * kStep;
+#pragma unroll
+            for (int j = 0; j < PD; ++j) {
+                if (s0 + j < nsteps) {
                     Codes<B> cur[NMAT];
 #pragma unroll
-                    for (int m = 0; m < NMAT; ++m) {
-                        cur[m] = buf[m][j];
-                        if (st + PD < nsteps) buf[m][j] = load_codes<B>(ap[m] + (int64_t)(st + PD) * SB);
-                    }
+                    for (int m = 0; m < NMAT; ++m) cur[m] = buf[m][j];
                     step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
                 }
             }
@@ -415,7 +464,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
 // grid: (active expert, 64-row tile, K split) flattened; experts beyond the
 // device-side active count exit at once.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
+__global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     __shared__ int tok[16];
     const int per_expert = tiles * nsplit;
@@ -469,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
 }  // namespace
 
 // LDS for the staged token rows: all of the K range for up to min(T, 16)
-// tokens if that fits 48 KB, else 48 KB (the kernel then stages K in chunks
+// tokens if that fits 34 KB, else 34 KB (the kernel then stages K in chunks
 // sized by the expert's actual token count).
 FfnPlan plan_ffn(int K, int T, int nsplit) {
     FfnPlan p;

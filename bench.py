@@ -147,8 +147,11 @@ class Bench:
             x, lg = batches[i % nb]
             self.layers[i % L].moe_forward(x, lg, ys[i % nb])
         torch.cuda.synchronize()
+        # a layer whose profiling is off keeps the records of its last timed
+        # run: read only the layers timed in this one
+        timed_layers = [j for j in range(L) if profile and (j == 0 or not sample)]
         for j, layer in enumerate(self.layers):
-            layer.profile(profile if (j == 0 or not sample) else 0)
+            layer.profile(profile if j in timed_layers else 0)
         t0 = time.perf_counter()
         for i in range(steps):
             x, lg = batches[i % nb]
@@ -158,9 +161,9 @@ class Bench:
         prof = {"gate_up_ms": 0.0, "down_ms": 0.0, "route_ms": 0.0, "combine_ms": 0.0}
         timed = 0
         if profile:
-            for layer in self.layers:
-                p = layer.profile_read()
-                layer.profile(0)
+            for j in timed_layers:
+                p = self.layers[j].profile_read()
+                self.layers[j].profile(0)
                 timed += p["forwards"]
                 for k in prof:
                     prof[k] += p[k]

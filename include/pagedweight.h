@@ -202,9 +202,11 @@ pw_status pw_budget_step(pw_ctx* ctx, const pw_budget_policy* policy, uint64_t k
                          const double* importance, const double* loss, int32_t* action,
                          uint64_t* budget_out, int32_t* pressure, void* stream);
 
-/* Timing of the forward kernels on the forward's stream: each timed kernel
- * is launched with start/stop HIP events stamped by its own dispatch
- * (hipExtLaunchKernel). mask selects the kernels: bit 0 router/grouping,
+/* Timing of the forward kernels on the forward's stream: HIP events
+ * (created without the system-scope fence) are recorded just before and
+ * after each timed kernel; an event delays the next dispatch by a few
+ * microseconds, so the sums read slightly above the kernels' own durations
+ * and untimed forwards run slightly faster. mask selects the kernels: bit 0 router/grouping,
  * bit 1 gate/up, bit 2 down, bit 3 combine; a nonzero mask starts (and
  * clears) collection, 0 stops it. pw_profile_read waits for the recorded
  * events and returns the per-class sums over the timed forwards. */

@@ -323,10 +323,12 @@ pw_status need_masters_pool(pw_ctx* c) {
     return PW_OK;
 }
 
+// Profiling events only carry timestamps, so they are created without the
+// system-scope fence (a cache writeback and invalidate at each record).
 hipEvent_t next_event(pw_ctx* c) {
     if (c->ev_used == c->ev_pool.size()) {
         hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         c->ev_pool.push_back(e);
     }
     return c->ev_pool[c->ev_used++];

@@ -60,8 +60,10 @@ struct Layout {
 
 Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit);
 
-// Optional timing of a launch: the events are stamped by the kernel's own
-// dispatch (hipExtLaunchKernel), so timing adds no packets between kernels.
+// Optional timing of a launch: events recorded on the stream just before and
+// after the kernel. Each recorded event delays the next dispatch by a few
+// microseconds, part of which falls inside the pair, so the pair reads a
+// little longer than the kernel itself.
 struct KTimer {
     hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -69,10 +71,15 @@ struct KTimer {
 template <typename Kern, typename... Args>
 inline hipError_t launch_timed(Kern kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
                                hipEvent_t start, hipEvent_t stop, Args... args) {
-    if (start || stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0u, args...);
-    else
-        kernel<<<grid, block, lds, s>>>(args...);
+    if (start) {
+        const hipError_t e = hipEventRecord(start, s);
+        if (e != hipSuccess) return e;
+    }
+    kernel<<<grid, block, lds, s>>>(args...);
+    if (stop) {
+        const hipError_t e = hipEventRecord(stop, s);
+        if (e != hipSuccess) return e;
+    }
     return hipGetLastError();
 }
 

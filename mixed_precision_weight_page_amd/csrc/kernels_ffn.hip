@@ -7,8 +7,8 @@
 // 128 codes) are contiguous in the page, so every load instruction of a
 // wave reads one contiguous run. One 4B-byte load per lane per tile
 // (B = bits), prefetched several steps ahead; they are turned into exact
-// fp16 integers q in registers (magic-exponent OR, then one packed fp16
-// subtract) and multiplied on the
+// fp16 integers q in registers (dequant.h: magic-exponent OR, then one
+// packed fp16 subtract or multiply-add per pair) and multiplied on the
 // matrix cores (v_mfma_f32_16x16x32_f16: 16 weight rows x 16 token columns,
 // K = 32), accumulating in fp32. Token rows are staged once per K chunk in
 // LDS as fp16, permuted so that each lane's 8 K-slots line up with the
@@ -20,22 +20,22 @@
 // dot2), which exceeds the VALU issue budget at HBM speed (about 2.5
 // lane-instructions per 4-bit weight at 8 TB/s) as soon as T_e > 2. The
 // MFMA does the multiply-adds for up to 16 tokens at once and leaves the
-// VALU only the unpack (about 1.4 instructions per 4-bit weight).
+// VALU only the unpack (about 1.1 instructions per 4-bit weight).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 
+#include "dequant.h"
 #include "pw_internal.h"
 
 namespace pw {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+using dq::half8_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kStep = 128;   // codes per wave per step (4 K-groups x 32)
-constexpr uint32_t kMagic = 0x64006400u;   // two fp16 1024.0
 
 template <int B>
 struct Codes {
@@ -75,105 +75,8 @@ __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
     return c;
 }
 
-// Dequantization to exact fp16 integers. A code u placed in the mantissa of
-// fp16 1024 (exponent pattern 0x6400) at bit S <= 7 of a 16-bit half gives the
-// exact value 1024 + 2^S u; a fused multiply-add by 2^-S minus
-// 2^(10-S) + 2^(B-1) then yields the signed code q = u - 2^(B-1) exactly (for
-// S = 0 a plain subtract). Exact q keeps the MFMA sums free of the offset
-// 2^(B-1) sum(x), which would otherwise dominate them when most codes are 0
-// (weights far below an expert's largest weight). Allowing S > 0 saves the
-// shift that would bring each code down to bit 0: one v_and_or_b32 per pair
-// of codes plus one packed fp16 operation.
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
-
-// A 32-bit constant held in a VGPR. A VOP3 instruction on this target can
-// read at most one SGPR or literal: with the exponent pattern in a VGPR,
-// (w & mask) | magic is one v_and_or_b32 with the mask as the SGPR operand.
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-    return r;
-}
-
-struct DeqConst {
-    uint32_t magic;   // 0x64006400: fp16 1024 in both halves
-    uint32_t e8;      // 0x64646464: exponent byte for v_perm_b32
-};
-
-__device__ __forceinline__ DeqConst deq_const() {
-    return DeqConst{vgpr_const(kMagic), vgpr_const(0x64646464u)};
-}
-
-// The two B-bit codes at bit S of each 16-bit half of x, as exact signed
-// fp16 values (low half, high half).
-template <int B, int S>
-__device__ __forceinline__ half2_t code_pair(uint32_t x, const DeqConst& c) {
-    constexpr uint32_t mask = ((1u << B) - 1u) * 0x00010001u << S;
-    const half2_t v = as_half2((x & mask) | c.magic);
-    if constexpr (S == 0) {
-        constexpr _Float16 bias = (_Float16)(1024 + (1 << (B - 1)));
-        return v - half2_t{bias, bias};
-    } else {
-        constexpr _Float16 m = (_Float16)(1.0f / (1 << S));
-        constexpr _Float16 bias = (_Float16)(-(float)((1024 >> S) + (1 << (B - 1))));
-        return __builtin_elementwise_fma(v, half2_t{m, m}, half2_t{bias, bias});
-    }
-}
-
-__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
-    return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
-                                   __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// The 16 signed pairs of a 3-bit group of 32 codes held in three dwords
-// (code c at bits 3c..3c+2); pair p = (slot 2p, slot 2p+1) of the staging
-// permutation. Half-words of two dwords are merged so that codes j and
-// j + 16 sit at the same offset of the two halves.
-__device__ __forceinline__ void pairs3(const uint32_t* w, half2_t p[16], const DeqConst& c) {
-    const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);   // codes 0-4 | 16-20 at 3j
-    const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);   // codes 22-25 | 6-9 at 3j-16
-    const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);   // codes 11-15 | 27-31 at 3j-32
-    // every code is taken at bit 0, 3 or 6 of its half (two multiply-add
-    // constants in registers instead of seven)
-    const uint32_t t01 = v01 >> 9, t02 = v02 >> 2, u02 = v02 >> 11, t12 = v12 >> 1, u12 = v12 >> 10;
-    p[0] = code_pair<3, 0>(v01, c);    // (0, 16)
-    p[1] = code_pair<3, 3>(v01, c);    // (1, 17)
-    p[2] = code_pair<3, 6>(v01, c);    // (2, 18)
-    p[3] = code_pair<3, 0>(t01, c);    // (3, 19)
-    p[4] = code_pair<3, 3>(t01, c);    // (4, 20)
-    // code 5 (bits 15-17) and code 21 (bits 63-65) straddle dword boundaries
-    p[5] = code_pair<3, 0>((w[0] >> 15 & 0xffffu) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0xffff0000u), c);
-    p[6] = code_pair<3, 0>(t02, c);    // (22, 6)
-    p[7] = code_pair<3, 3>(t02, c);    // (23, 7)
-    p[8] = code_pair<3, 6>(t02, c);    // (24, 8)
-    p[9] = code_pair<3, 0>(u02, c);    // (25, 9)
-    // code 10 (bits 30-32) and code 26 (bits 78-80)
-    p[10] = code_pair<3, 0>((__builtin_amdgcn_alignbit(w[1], w[0], 30) & 0xffffu) |
-                                (__builtin_amdgcn_alignbit(w[2], w[1], 30) & 0xffff0000u), c);
-    p[11] = code_pair<3, 0>(t12, c);   // (11, 27)
-    p[12] = code_pair<3, 3>(t12, c);   // (12, 28)
-    p[13] = code_pair<3, 6>(t12, c);   // (13, 29)
-    p[14] = code_pair<3, 0>(u12, c);   // (14, 30)
-    p[15] = code_pair<3, 3>(u12, c);   // (15, 31)
-}
-
-// Code (within a 32-code group) whose activation goes to LDS slot s.
-template <int B>
-__device__ __forceinline__ constexpr int perm_slot(int s) {
-    if constexpr (B == 4) {
-        constexpr int p[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        return (s & ~7) + p[s & 7];
-    } else if constexpr (B == 8) {
-        constexpr int p[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-        return (s & ~7) + p[s & 7];
-    } else {
-        constexpr int p[32] = {0, 16, 1, 17, 2, 18, 3, 19, 4, 20, 5, 21, 22, 6, 23, 7,
-                               24, 8, 25, 9, 10, 26, 11, 27, 12, 28, 13, 29, 14, 30, 15, 31};
-        return p[s];
-    }
-}
+using dq::half2_t;
+using dq::perm_slot;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
@@ -264,43 +167,23 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
 template <int B>
 __device__ __forceinline__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
 
-// A fragment i (K-slots 8i..8i+7 of the lane's 32 codes) of a 4- or 8-bit
-// step. 4-bit: nibbles (0, 4), (1, 5), (2, 6), (3, 7) of dword i. 8-bit:
-// bytes (0, 2) and (1, 3) of dwords 2i and 2i + 1, moved next to the
-// exponent byte by v_perm_b32 (selector bytes 0-3 pick from the dword, 4
-// from the exponent pattern).
-template <int B>
-__device__ __forceinline__ half8_t frag(const Codes<B>& cd, int i, const DeqConst& c) {
-    if constexpr (B == 4) {
-        const uint32_t w = cd.w[i], t = w >> 8;
-        return cat(code_pair<4, 0>(w, c), code_pair<4, 4>(w, c), code_pair<4, 0>(t, c), code_pair<4, 4>(t, c));
-    } else {
-        const uint32_t w0 = cd.w[2 * i], w1 = cd.w[2 * i + 1];
-        const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-        return cat(as_half2(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u)) - bias,
-                   as_half2(__builtin_amdgcn_perm(c.e8, w0, 0x04030401u)) - bias,
-                   as_half2(__builtin_amdgcn_perm(c.e8, w1, 0x04020400u)) - bias,
-                   as_half2(__builtin_amdgcn_perm(c.e8, w1, 0x04030401u)) - bias);
-    }
-}
-
 // The four MFMAs of one 128-code step for each matrix; bp points at the
 // step's 128 staged activations of this lane's token row and K-group.
 template <int B, int NMAT>
 __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* bp,
-                                         f32x4 (&acc)[NMAT], const DeqConst& dc) {
+                                         f32x4 (&acc)[NMAT], const dq::Const& dc) {
     if constexpr (B == 3) {
         half2_t pr[NMAT][16];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) pairs3(cur[m].w, pr[m], dc);
+        for (int m = 0; m < NMAT; ++m) dq::pairs3(cur[m].w, pr[m], dc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    cat(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]), bfr, acc[m], 0, 0,
-                    0);
+                    dq::cat(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]), bfr, acc[m], 0,
+                    0, 0);
         }
     } else {
 #pragma unroll
@@ -308,7 +191,7 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
             const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag<B>(cur[m], i, dc), bfr, acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq::frag48<B>(cur[m].w, i, dc), bfr, acc[m], 0, 0, 0);
         }
     }
 }
@@ -335,7 +218,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
-    const DeqConst dc = deq_const();
+    const dq::Const dc = dq::make_const();
     // this wave's 16-row block is one contiguous run of K/128 tiles
     const uint8_t* ap[NMAT];
 #pragma unroll

@@ -26,12 +26,13 @@
 
 #include <math.h>
 
+#include "dequant.h"
 #include "pw_internal.h"
 
 namespace pw {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+using dq::half8_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -42,7 +43,6 @@ template <int MODE>
 constexpr int tile_rows() { return MODE == 0 ? 128 : 256; }
 constexpr int BN = kGemmTokens;  // tokens per tile
 constexpr int NJ = BN / 16;      // 16-token blocks per tile
-constexpr uint32_t kMagic = 0x64006400u;
 
 template <int B>
 struct Run {
@@ -75,97 +75,7 @@ __device__ __forceinline__ Run<B> load_run_at(const uint8_t* p) {
     return r;
 }
 
-__device__ __forceinline__ uint4 sub_bias(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                          _Float16 bias) {
-    union {
-        uint32_t u[4];
-        half8_t h;
-        uint4 v;
-    } x;
-    x.u[0] = a; x.u[1] = b; x.u[2] = c; x.u[3] = d;
-    x.h = x.h - bias;
-    return x.v;
-}
-
-// A 32-bit constant held in a VGPR. A VOP3 instruction on this target can
-// read at most one SGPR or literal, so with the masks and the exponent
-// pattern in VGPRs each (w & mask) | magic is one v_and_or_b32 instead of a
-// v_and plus a v_or.
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
-    uint32_t r;
-    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-    return r;
-}
-
-struct DeqConst {
-    uint32_t magic;   // 0x64006400: fp16 1024 in both halves
-    uint32_t m4;      // 0x000f000f
-    uint32_t e8;      // 0x64646464: exponent byte for v_perm_b32
-};
-
-__device__ __forceinline__ DeqConst deq_const() {
-    return DeqConst{vgpr_const(kMagic), vgpr_const(0x000f000fu), vgpr_const(0x64646464u)};
-}
-
-// The 32 codes of a run as exact fp16 q, in the K-slot order of the staging
-// permutation (4 x 16 bytes).
-template <int B>
-__device__ __forceinline__ void run_to_f16(const Run<B>& r, uint4 out[4], const DeqConst& c) {
-    if constexpr (B == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = r.w[i];
-            out[i] = sub_bias((w & c.m4) | c.magic, ((w >> 4) & c.m4) | c.magic,
-                              ((w >> 8) & c.m4) | c.magic, ((w >> 12) & c.m4) | c.magic,
-                              (_Float16)1032.0f);
-        }
-    } else if constexpr (B == 8) {
-        // bytes (b0, 0x64, b2, 0x64) and (b1, 0x64, b3, 0x64) of each word:
-        // selector bytes 0-3 pick from the word, 4 from the exponent pattern
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w0 = r.w[2 * i], w1 = r.w[2 * i + 1];
-            out[i] = sub_bias(__builtin_amdgcn_perm(c.e8, w0, 0x04020400u),
-                              __builtin_amdgcn_perm(c.e8, w0, 0x04030401u),
-                              __builtin_amdgcn_perm(c.e8, w1, 0x04020400u),
-                              __builtin_amdgcn_perm(c.e8, w1, 0x04030401u), (_Float16)1152.0f);
-        }
-    } else {
-        const uint32_t* w = r.w;
-        const uint32_t M3 = 0x00070007u;
-        const uint32_t v01 = (w[0] & 0xffffu) | (w[1] & 0xffff0000u);
-        const uint32_t v12 = (w[1] & 0xffffu) | (w[2] & 0xffff0000u);
-        const uint32_t v02 = (w[2] & 0xffffu) | (w[0] & 0xffff0000u);
-        uint32_t p[16];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) p[j] = ((v01 >> (3 * j)) & M3) | kMagic;
-        p[5] = ((w[0] >> 15) & 7u) | (__builtin_amdgcn_alignbit(w[2], w[1], 15) & 0x70000u) | kMagic;
-#pragma unroll
-        for (int j = 6; j < 10; ++j) p[j] = ((v02 >> (3 * j - 16)) & M3) | kMagic;
-        p[10] = (__builtin_amdgcn_alignbit(w[1], w[0], 30) & 7u) | ((w[2] << 2) & 0x70000u) | kMagic;
-#pragma unroll
-        for (int j = 11; j < 16; ++j) p[j] = ((v12 >> (3 * j - 32)) & M3) | kMagic;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[i] = sub_bias(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3], (_Float16)1028.0f);
-    }
-}
-
-// Code (within a 32-code run) whose activation goes to K-slot s.
-template <int B>
-__device__ __forceinline__ constexpr int perm_slot(int s) {
-    if constexpr (B == 4) {
-        constexpr int p[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        return (s & ~7) + p[s & 7];
-    } else if constexpr (B == 8) {
-        constexpr int p[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-        return (s & ~7) + p[s & 7];
-    } else {
-        constexpr int p[32] = {0, 16, 1, 17, 2, 18, 3, 19, 4, 20, 5, 21, 22, 6, 23, 7,
-                               24, 8, 25, 9, 10, 26, 11, 27, 12, 28, 13, 29, 14, 30, 15, 31};
-        return p[s];
-    }
-}
+using dq::perm_slot;
 
 // K-slot that code c (within a 32-code run) takes in the K order of B-bit
 // codes: the inverse of perm_slot.
@@ -244,14 +154,16 @@ __device__ __forceinline__ int swz(int n, int c) { return n * (LDX / 8) + (c ^ (
 template <int B>
 __device__ __forceinline__ constexpr int gemm_depth() { return 2; }  // even
 
+// Fragment i (K-slots 8i .. 8i + 7) of a run as exact fp16 q.
 template <int B>
-__device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i, const DeqConst& c) {
-    union {
-        uint4 v[4];
-        half8_t h[4];
-    } o;
-    run_to_f16<B>(r, o.v, c);   // the compiler keeps only fragment i alive
-    return o.h[i];
+__device__ __forceinline__ half8_t frag_of(const Run<B>& r, int i, const dq::Const& c) {
+    if constexpr (B == 3) {
+        dq::half2_t p[16];
+        dq::pairs3(r.w, p, c);   // the compiler keeps only fragment i's pairs
+        return dq::cat(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+    } else {
+        return dq::frag48<B>(r.w, i, c);
+    }
 }
 
 // Token rows of one step (already fp16 in the codes' K order): thread t
@@ -326,7 +238,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     const _Float16* act_row = MODE == 0 ? a.xp + (int64_t)bits_index(B) * a.xp_plane + (int64_t)my_tok * a.d
                                         : a.w.H + (int64_t)my_tok * a.F;
     _Float16* xs[2] = {smem, smem + BN * LDX};
-    const DeqConst dc = deq_const();
+    const dq::Const dc = dq::make_const();
 
     // prologue: codes for steps 0..PD-1 in flight, token rows of step 0 staged
     Run<B> ring[PD][NMAT][2];

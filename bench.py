@@ -64,7 +64,7 @@ def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
     src = "kernels_gemm.hip" if workload == "prefill" else "kernels_ffn.hip"
-    for f in (src, "pw_internal.h"):
+    for f in (src, "pw_internal.h", "dequant.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -42,7 +42,6 @@ constexpr int kThreads = 256;
 template <int MODE>
 constexpr int tile_rows() { return MODE == 0 ? 128 : 256; }
 constexpr int BN = kGemmTokens;  // tokens per tile
-constexpr int NJ = BN / 16;      // 16-token blocks per tile
 
 template <int B>
 struct Run {
@@ -185,20 +184,21 @@ __device__ __forceinline__ void store_act(const u32x4 (&xr)[XR], _Float16* xs, i
 
 // Scheduling groups for one step (64 MFMAs, 16 LDS reads, 16 fragments of
 // dequantization): masks 0x8 MFMA, 0x2 VALU, 0x100 LDS read.
-template <int B>
+template <int B, int NA>
 __device__ __forceinline__ void sched_step() {
-    constexpr int kValuPerMfma = B == 8 ? 2 : 3;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr int kMfma = 16 * NA;                          // 4 K groups x 4 code streams x NA
+    constexpr int kValuPerMfma = (B == 8 ? 8 : 12) / NA;    // the dequantization spread over them
+    __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);
     __builtin_amdgcn_sched_group_barrier(0x2, B == 8 ? 32 : 44, 0);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < kMfma; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x2, kValuPerMfma, 0);
         if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 }
 
-template <int MODE, int B>
+template <int MODE, int B, int NA>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
                                           int* tok) {
     constexpr int NMAT = 2;   // stream pairs: W1 / W3 (MODE 0), two 32-row halves of W2 (MODE 1)
@@ -255,13 +255,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     store_act(xr, xs[0], tid);
     __syncthreads();
 
-    f32x4 acc[NMAT][2][NJ];
+    f32x4 acc[NMAT][2][NA];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NA; ++j) acc[m][blk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one step: token rows of step st + 1 into registers; the MFMAs of step
     // st, with the token fragments of K-group kc + 1 read from LDS while
@@ -279,14 +279,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         // kc uses codes 32g + 8kc..+8, so the token fragment is the same 8
         // K-slots of token row 16 jt + r
         const u32x4* xl = reinterpret_cast<const u32x4*>(cur);
-        half8_t bq[2][NJ];
+        half8_t bq[2][NA];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) bq[0][jt] = __builtin_bit_cast(half8_t, xl[swz(16 * jt + r, 4 * g)]);
+        for (int jt = 0; jt < NA; ++jt) bq[0][jt] = __builtin_bit_cast(half8_t, xl[swz(16 * jt + r, 4 * g)]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             if (kc < 3) {
 #pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
+                for (int jt = 0; jt < NA; ++jt)
                     bq[(kc + 1) & 1][jt] = __builtin_bit_cast(half8_t, xl[swz(16 * jt + r, 4 * g + kc + 1)]);
             }
             half8_t af[NMAT][2];
@@ -302,7 +302,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                         ring_j[m][blk] = load_run_at<B>(ap[m][blk] + (int64_t)min(st + PD, S - 1) * TB);
             }
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
+            for (int jt = 0; jt < NA; ++jt)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -313,7 +313,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         // issue order for the step: the first K group's token fragments and
         // codes, then each MFMA followed by a few VALU instructions (the next
         // groups' dequantization) and, every fourth MFMA, one LDS read
-        sched_step<B>();
+        sched_step<B, NA>();
         if (st + 1 < S) store_act(xr, nxt, tid);
         __syncthreads();
     };
@@ -331,7 +331,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
         if (s0 + j < S) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) {
+    for (int jt = 0; jt < NA; ++jt) {
         const int n = 16 * jt + r;
         if (n >= nt) continue;
         const int pos = base + t0 + n;
@@ -364,6 +364,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     }
 }
 
+template <int MODE, int B>
+__device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
+                                            int* tok) {
+    if (na >= 4) gemm_tile<MODE, B, 4>(a, e, tt, rt, smem, tok);
+    else if (na == 3) gemm_tile<MODE, B, 3>(a, e, tt, rt, smem, tok);
+    else if (na == 2) gemm_tile<MODE, B, 2>(a, e, tt, rt, smem, tok);
+    else gemm_tile<MODE, B, 1>(a, e, tt, rt, smem, tok);
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_tiles, int ntiles) {
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
@@ -387,9 +396,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     const int rt = l / ntt;
     const int tt = l - rt * ntt;
     const int b = a.tab.bits[e];
-    if (b == 4) gemm_tile<MODE, 4>(a, e, tt, rt, smem, tok);
-    else if (b == 8) gemm_tile<MODE, 8>(a, e, tt, rt, smem, tok);
-    else gemm_tile<MODE, 3>(a, e, tt, rt, smem, tok);
+    // 16-token blocks holding real tokens (fewer than four only in an
+    // expert's last token tile): the MFMAs of the empty ones are skipped
+    const int nblk = (min(BN, a.w.cnt[e] - tt * BN) + 15) >> 4;
+    if (b == 4) dispatch_na<MODE, 4>(nblk, a, e, tt, rt, smem, tok);
+    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, e, tt, rt, smem, tok);
+    else dispatch_na<MODE, 3>(nblk, a, e, tt, rt, smem, tok);
 }
 
 template <int MODE>

@@ -114,3 +114,54 @@ def solve(p, L, W, B):
     if len(p) <= 8:
         return solve_bruteforce(p, L, W, B)
     return solve_dp(p, L, W, B)
+
+
+# ---- comparison mode and a budget shared by several layers ----
+
+def proportional(p, W, B):
+    """The page's simplified illustration (PagedWeight page, the code sketch
+    after "Implementation Details"): each expert's share of the budget is
+    proportional to its importance, divided by its weight count, and the
+    result is bucketized to {3, 4, 8} rounding up (a value equal to an option
+    takes that option; above 8 it is clamped to 8).
+
+    Reading: the budget is taken in bits, so share / W_e is bits per weight
+    (the sketch divides a byte budget by a parameter count). The result need
+    not respect the budget; returns (bits, used_bits).
+    """
+    p = [float(v) for v in p]
+    W = [int(w) for w in W]
+    total = sum(p)
+    if not total > 0.0:
+        raise ValueError("importances must not all be zero")
+    bits = []
+    for pe, we in zip(p, W):
+        x = float(B) * pe / total / we
+        if x <= 3.0:
+            bits.append(3)
+        elif x <= 4.0:
+            bits.append(4)
+        else:
+            bits.append(8)
+    return bits, used_bits(bits, W)
+
+
+def solve_layers(ps, Ls, Ws, B, layer_weights=None):
+    """Eq. 1 with one budget B over the experts of several layers: minimise
+    sum_l w_l sum_e p_{l,e} L_{l,e}(b) subject to sum over all experts of
+    b W <= B. The constraint and the objective are sums over the union of
+    the layers' experts, so this is Eq. 1 on that union with importances
+    w_l p_{l,e}. Returns (per-layer bit lists, objective)."""
+    n = len(ps)
+    w = [1.0] * n if layer_weights is None else [float(v) for v in layer_weights]
+    p_all, L_all, W_all = [], [], []
+    for l in range(n):
+        p_all += [w[l] * float(v) for v in ps[l]]
+        L_all += [list(map(float, row)) for row in Ls[l]]
+        W_all += [int(v) for v in Ws[l]]
+    bits, obj = solve(p_all, L_all, W_all, B)
+    out, i = [], 0
+    for l in range(n):
+        out.append(bits[i:i + len(ps[l])])
+        i += len(ps[l])
+    return out, obj

@@ -155,6 +155,30 @@ pw_status pw_get_loss_table(pw_ctx* ctx, double* out, void* stream);
 pw_status pw_solve_allocation(int32_t E, const uint64_t* W, const double* p, const double* L,
                               uint64_t budget_bits, uint8_t* bits_out);
 
+/* One budget shared by several layers (host, no GPU): Eq. 1 over the union
+ * of the layers' experts, minimising sum_l w_l sum_e p_{l,e} L_{l,e}(b)
+ * subject to sum over all experts of b W <= B. E[n_layers] experts per
+ * layer; W, p, bits_out have sum(E) entries and L has 3 sum(E), all in
+ * layer order; layer_weight[n_layers] may be NULL (all 1). Writes the
+ * objective to objective_out if not NULL. At most 65536 experts in all;
+ * PW_ERR_INFEASIBLE_BUDGET when B < 3 sum W, PW_ERR_INVALID_ARG for bad
+ * sizes, negative or non-finite inputs, or a budget too finely divided for
+ * the exact solver. Each layer then applies its share with
+ * pw_quantize_experts. */
+pw_status pw_solve_allocation_layers(int32_t n_layers, const int32_t* E, const uint64_t* W, const double* p,
+                                     const double* L, const double* layer_weight, uint64_t budget_bits,
+                                     uint8_t* bits_out, double* objective_out);
+
+/* Comparison mode, not a solver of Eq. 1: the simplified sketch printed on
+ * the PagedWeight page (after "Implementation Details"): expert e's share
+ * B p_e / sum(p) divided by W_e, bucketized up to {3, 4, 8} (a share equal
+ * to an option takes it; above 8 gives 8). The budget is read in bits. The
+ * bits may exceed the budget: used_bits_out (may be NULL) receives
+ * sum_e b_e W_e. PW_ERR_INVALID_ARG for E outside [1, 65536], W_e = 0,
+ * negative or non-finite p, or all p zero. */
+pw_status pw_proportional_bits(int32_t E, const uint64_t* W, const double* p, uint64_t budget_bits,
+                               uint8_t* bits_out, uint64_t* used_bits_out);
+
 /* ---- KV-pressure budget scheduler ----
  * The pool's budget follows the KV-cache occupancy (PagedWeight page,
  * section "Implementation Details": the scheduler adjusts page sizes from

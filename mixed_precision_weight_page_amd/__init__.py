@@ -5,4 +5,5 @@ ABI in include/pagedweight.h); this package only binds it.
 """
 from .pagedweight import (BITS, BUDGET_GROW, BUDGET_INIT, BUDGET_KEEP, BUDGET_SHRINK,  # noqa: F401
                           PagedMoELayer, PagedWeightError, budget_decide, lib, library_path,
-                          solve_allocation)
+                          proportional_bits, set_budget_layers, solve_allocation,
+                          solve_allocation_layers)

@@ -15,13 +15,15 @@
 
 namespace pw {
 
-pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,
-                           uint64_t B, uint8_t* bits_out, std::string* err) {
+namespace {
+
+pw_status solve_core(int E, int max_experts, const uint64_t* W, const double* p, const double* L,
+                     uint64_t B, uint8_t* bits_out, double* objective, std::string* err) {
     auto fail = [&](pw_status s, const char* m) {
         if (err) *err = m;
         return s;
     };
-    if (E <= 0 || E > kMaxExperts || !W || !p || !L || !bits_out)
+    if (E <= 0 || E > max_experts || !W || !p || !L || !bits_out)
         return fail(PW_ERR_INVALID_ARG, "solve_allocation: bad E or null pointer");
     unsigned __int128 sumW = 0;
     uint64_t g = 0;
@@ -77,6 +79,7 @@ pw_status solve_allocation(int E, const uint64_t* W, const double* p, const doub
     uint64_t cb = 0;
     for (uint64_t c = 1; c <= C; ++c)
         if (best[c] < best[cb]) cb = c;
+    if (objective) *objective = best[cb];
     for (int e = E - 1; e >= 0; --e) {
         const int b = choice[(size_t)e * (C + 1) + cb];
         bits_out[e] = (uint8_t)b;
@@ -85,4 +88,67 @@ pw_status solve_allocation(int E, const uint64_t* W, const double* p, const doub
     return PW_OK;
 }
 
+}  // namespace
+
+pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,
+                           uint64_t B, uint8_t* bits_out, std::string* err) {
+    return solve_core(E, kMaxExperts, W, p, L, B, bits_out, nullptr, err);
+}
+
 }  // namespace pw
+
+namespace {
+// Experts over all layers of one shared budget (the exact solver's table is
+// E x (budget units + 1) bytes and is capped separately).
+constexpr int kMaxSolveExperts = 1 << 16;
+}  // namespace
+
+extern "C" {
+
+// One budget over several layers: Eq. 1 over the union of their experts with
+// importances w_l p_{l,e} (the constraint and the objective are sums over
+// that union).
+pw_status pw_solve_allocation_layers(int32_t n_layers, const int32_t* E, const uint64_t* W, const double* p,
+                                     const double* L, const double* layer_weight, uint64_t budget_bits,
+                                     uint8_t* bits_out, double* objective_out) {
+    if (n_layers <= 0 || !E || !W || !p || !L || !bits_out) return PW_ERR_INVALID_ARG;
+    int64_t total = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        if (E[l] <= 0) return PW_ERR_INVALID_ARG;
+        total += E[l];
+        if (total > kMaxSolveExperts) return PW_ERR_INVALID_ARG;
+        if (layer_weight && !(layer_weight[l] >= 0.0 && std::isfinite(layer_weight[l])))
+            return PW_ERR_INVALID_ARG;
+    }
+    std::vector<double> pw_(total);
+    for (int l = 0, i = 0; l < n_layers; ++l)
+        for (int e = 0; e < E[l]; ++e, ++i) pw_[i] = (layer_weight ? layer_weight[l] : 1.0) * p[i];
+    return pw::solve_core((int)total, kMaxSolveExperts, W, pw_.data(), L, budget_bits, bits_out, objective_out,
+                          nullptr);
+}
+
+// The page's simplified sketch, for comparison (not a solver of Eq. 1): the
+// budget shared in proportion to importance, divided by each expert's
+// weight count, bucketized up to {3, 4, 8}. The result may exceed the
+// budget; used_bits_out receives sum_e b_e W_e.
+pw_status pw_proportional_bits(int32_t E, const uint64_t* W, const double* p, uint64_t budget_bits,
+                               uint8_t* bits_out, uint64_t* used_bits_out) {
+    if (E <= 0 || E > kMaxSolveExperts || !W || !p || !bits_out) return PW_ERR_INVALID_ARG;
+    double total = 0.0;
+    for (int e = 0; e < E; ++e) {
+        if (W[e] == 0 || !(p[e] >= 0.0) || !std::isfinite(p[e])) return PW_ERR_INVALID_ARG;
+        total += p[e];
+    }
+    if (!(total > 0.0) || !std::isfinite(total)) return PW_ERR_INVALID_ARG;
+    unsigned __int128 used = 0;
+    for (int e = 0; e < E; ++e) {
+        const double x = (double)budget_bits * p[e] / total / (double)W[e];
+        const int b = x <= 3.0 ? 3 : (x <= 4.0 ? 4 : 8);
+        bits_out[e] = (uint8_t)b;
+        used += (unsigned __int128)b * W[e];
+    }
+    if (used_bits_out) *used_bits_out = used > UINT64_MAX ? UINT64_MAX : (uint64_t)used;
+    return PW_OK;
+}
+
+}  // extern "C"

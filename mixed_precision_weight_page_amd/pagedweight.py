@@ -73,6 +73,8 @@ _SIGNATURES = {
     "pw_get_page_table": (ctypes.c_int, [_P, ctypes.POINTER(PageEntry)]),
     "pw_get_loss_table": (ctypes.c_int, [_P, _P, _P]),
     "pw_solve_allocation": (ctypes.c_int, [ctypes.c_int32, _P, _P, _P, ctypes.c_uint64, _P]),
+    "pw_solve_allocation_layers": (ctypes.c_int, [ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P]),
+    "pw_proportional_bits": (ctypes.c_int, [ctypes.c_int32, _P, _P, ctypes.c_uint64, _P, _P]),
     "pw_budget_decide": (ctypes.c_int, [ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, ctypes.c_int32, _P,
                                         ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, _P, _P, _P]),
     "pw_budget_step": (ctypes.c_int, [_P, ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, _P, _P, _P, _P, _P, _P]),
@@ -144,6 +146,54 @@ def solve_allocation(W: Sequence[int], p: Sequence[float], L, budget_bits: int) 
     _check(lib().pw_solve_allocation(E, Wa.ctypes.data, pa.ctypes.data, La.ctypes.data,
                                      int(budget_bits), out.ctypes.data))
     return out
+
+
+def solve_allocation_layers(Ws, ps, Ls, budget_bits: int, layer_weights=None):
+    """pw_solve_allocation_layers: one exact solve of Eq. 1 for several layers
+    sharing budget_bits. Ws, ps, Ls hold one entry per layer (W[E_l], p[E_l],
+    L[E_l][3]). Returns (list of per-layer bit arrays, objective)."""
+    n = len(ps)
+    if not (len(Ws) == len(Ls) == n) or n == 0:
+        raise ValueError("Ws, ps and Ls need one entry per layer")
+    E = np.array([len(v) for v in ps], dtype=np.int32)
+    Wa = np.ascontiguousarray(np.concatenate([_host_array(W, np.uint64, int(e), "W") for W, e in zip(Ws, E)]))
+    pa = np.ascontiguousarray(np.concatenate([_host_array(p, np.float64, int(e), "p") for p, e in zip(ps, E)]))
+    La = np.ascontiguousarray(np.concatenate([np.asarray(L, dtype=np.float64).reshape(int(e) * 3)
+                                              for L, e in zip(Ls, E)]))
+    wa = None if layer_weights is None else _host_array(layer_weights, np.float64, n, "layer_weights")
+    out = np.zeros(int(E.sum()), dtype=np.uint8)
+    obj = ctypes.c_double(0.0)
+    _check(lib().pw_solve_allocation_layers(n, E.ctypes.data, Wa.ctypes.data, pa.ctypes.data, La.ctypes.data,
+                                            None if wa is None else wa.ctypes.data, int(budget_bits),
+                                            out.ctypes.data, ctypes.byref(obj)))
+    return np.split(out, np.cumsum(E)[:-1]), obj.value
+
+
+def proportional_bits(W: Sequence[int], p: Sequence[float], budget_bits: int):
+    """pw_proportional_bits: the pages' simplified proportional sketch (a
+    comparison mode; may exceed the budget). Returns (bits, used_bits)."""
+    E = len(p)
+    Wa = _host_array(W, np.uint64, E, "W")
+    pa = _host_array(p, np.float64, E, "p")
+    out = np.zeros(E, dtype=np.uint8)
+    used = ctypes.c_uint64(0)
+    _check(lib().pw_proportional_bits(E, Wa.ctypes.data, pa.ctypes.data, int(budget_bits), out.ctypes.data,
+                                      ctypes.byref(used)))
+    return out, used.value
+
+
+def set_budget_layers(layers, budget_bits: int, importances, layer_weights=None, stream=None):
+    """One budget shared by several PagedMoELayer objects: each layer's loss
+    table (pw_get_loss_table), one exact solve over all their experts
+    (pw_solve_allocation_layers), then each layer quantized to its share
+    (pw_quantize_experts; its pool must hold the new pages). Returns (list of
+    per-layer bit arrays, objective)."""
+    Ls = [layer.get_loss_table(stream) for layer in layers]
+    Ws = [[3 * layer.d * layer.F] * layer.E for layer in layers]
+    bits, obj = solve_allocation_layers(Ws, importances, Ls, budget_bits, layer_weights)
+    for layer, b in zip(layers, bits):
+        layer.quantize_experts(b, stream)
+    return bits, obj
 
 
 NO_POOL = (1 << 64) - 1   # pool_bytes_now before the first allocation

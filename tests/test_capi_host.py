@@ -248,3 +248,78 @@ def test_budget_decide_argument_errors(L):
     assert call(pwb.BudgetPolicy(4000, 0, float("nan"), 2)) == INVALID
     assert call(pwb.BudgetPolicy(4000, 0, 0.1, -1)) == INVALID
     assert call(ok, w=(ctypes.c_uint64 * 2)(1000, 0)) == INVALID
+
+
+def test_proportional_bits_match_oracle(L):
+    rng = random.Random(17)
+    for _ in range(300):
+        E = rng.randint(1, 40)
+        W = [rng.randint(1, 5000) for _ in range(E)]
+        p = [rng.random() for _ in range(E)]
+        B = rng.randint(1, 12 * sum(W))
+        bits, used = pwb.proportional_bits(W, p, B)
+        want, want_used = alloc.proportional(p, W, B)
+        assert bits.tolist() == want
+        assert used == want_used
+    # exact bucket boundaries, as pinned for the oracle
+    bits, used = pwb.proportional_bits([1] * 4, [3.0, 4.0, 4.5, 10.0], 21)
+    assert bits.tolist() == alloc.proportional([3.0, 4.0, 4.5, 10.0], [1] * 4, 21)[0]
+    for bad in ([0.0, 0.0], [1.0, float("nan")], [-1.0, 2.0]):
+        with pytest.raises(pwb.PagedWeightError) as ei:
+            pwb.proportional_bits([1, 1], bad, 10)
+        assert ei.value.status == INVALID
+    with pytest.raises(pwb.PagedWeightError):
+        pwb.proportional_bits([0, 1], [1.0, 1.0], 10)
+
+
+def test_layers_solver_matches_oracle(L):
+    rng = random.Random(29)
+    for trial in range(40):
+        n = rng.randint(1, 4)
+        ps, Ls, Ws = [], [], []
+        for _ in range(n):
+            E = rng.randint(1, 4)
+            Ws.append([rng.choice([2, 3, 4, 6]) for _ in range(E)])
+            ps.append([rng.random() for _ in range(E)])
+            rows = []
+            for _ in range(E):
+                a = rng.uniform(1e-4, 1e-2)
+                b = a + rng.uniform(1e-3, 0.3)
+                rows.append([b + rng.uniform(1e-3, 1.0), b, a])
+            Ls.append(rows)
+        Wsum = sum(sum(W) for W in Ws)
+        B = rng.randint(3 * Wsum, 8 * Wsum)
+        wts = None if trial % 3 == 0 else [rng.uniform(0.0, 2.0) for _ in range(n)]
+        got, obj = pwb.solve_allocation_layers(Ws, ps, Ls, B, wts)
+        want, want_obj = alloc.solve_layers(ps, Ls, Ws, B, wts)
+        assert [g.tolist() for g in got] == want, trial
+        assert obj == want_obj
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        pwb.solve_allocation_layers([[4, 4]], [[0.5, 0.5]], [[[1, 0.5, 0.1]] * 2], 3 * 8 - 1)
+    assert ei.value.status == INFEASIBLE
+    with pytest.raises(pwb.PagedWeightError) as ei:
+        pwb.solve_allocation_layers([[4]], [[0.5]], [[[1, 0.5, 0.1]]], 40, [-1.0])
+    assert ei.value.status == INVALID
+
+
+def test_layers_solver_at_model_scale(L):
+    # 24 layers x 128 equal experts under one budget of 4 bits on average:
+    # the union's optimum against the oracle's dynamic programme
+    rng = np.random.default_rng(3)
+    n, E, We = 24, 128, 4_718_592
+    ps, Ls, Ws = [], [], []
+    for _ in range(n):
+        p = rng.permutation(np.arange(1, E + 1) ** -1.1)
+        ps.append((p / p.sum()).tolist())
+        l8 = rng.uniform(1e-9, 1e-8, E)
+        l4 = l8 + rng.uniform(1e-7, 1e-6, E)
+        l3 = l4 + rng.uniform(1e-7, 3e-6, E)
+        Ls.append(np.stack([l3, l4, l8], 1).tolist())
+        Ws.append([We] * E)
+    B = 4 * n * E * We
+    got, obj = pwb.solve_allocation_layers(Ws, ps, Ls, B)
+    flat = [b for g in got for b in g.tolist()]
+    assert alloc.used_bits(flat, [We] * (n * E)) <= B
+    want, want_obj = alloc.solve_dp([v for p in ps for v in p], [r for Lx in Ls for r in Lx], [We] * (n * E), B)
+    assert flat == want
+    assert obj == want_obj

@@ -116,6 +116,36 @@ def test_set_budget_pages_and_forward(wl):
     compare_y(y, oracle_y(x, logits, wl, masters, bits), wl.name)
 
 
+def test_budget_shared_by_two_layers():
+    # two layers of different shapes under one budget of 4.5 bits per weight
+    # on average: bits as the oracle's solve over the union of their
+    # experts, pages bit-exact, outputs within tolerance
+    from mixed_precision_weight_page_amd import set_budget_layers
+    wls = [SMALL_FINE, TINY.scaled(name="tiny_b")]
+    layers, pools, masters, ps, Ls = [], [], [], [], []
+    for wl in wls:
+        m = synth.expert_weights(wl)
+        layer, pool = make_layer(wl, m, max_tokens=wl.T)
+        layers.append(layer)
+        pools.append(pool)
+        masters.append(m)
+        ps.append(list(synth.importance(wl)))
+        Ls.append(quant.loss_table(*m)[1])
+    B = int(4.5 * sum(wl.E * wl.W_e for wl in wls))
+    log("two layers: set_budget_layers")
+    bits, obj = set_budget_layers(layers, B, ps, layer_weights=[1.0, 2.0])
+    torch.cuda.synchronize()
+    want, want_obj = alloc.solve_layers(ps, Ls, [[wl.W_e] * wl.E for wl in wls], B, [1.0, 2.0])
+    assert [b.tolist() for b in bits] == want
+    assert obj == pytest.approx(want_obj, rel=1e-12)
+    assert sum(int(b.astype(np.int64).sum()) * wl.W_e for b, wl in zip(bits, wls)) <= B
+    for wl, layer, pool, m, b in zip(wls, layers, pools, masters, bits):
+        check_pages(layer, pool, m, b)
+        x, logits = synth.tokens(wl)
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, m, b), wl.name)
+
+
 def test_ragged_token_counts():
     # experts with more than 16 tokens (several token blocks), a ragged tail,
     # a single token, and T = 0

@@ -16,8 +16,10 @@ Plain, slow and written to be checked by eye against the pages:
 * ``sched``  the KV-pressure budget scheduler (section "Implementation
              Details", memory management): occupancy -> budget with
              hysteresis.
+* ``swap``   the host tier of section "Dynamic Paging": which expert pages
+             a device cache of page slots holds, pass by pass.
 
 All floating-point arithmetic is float64 except where a rounding step is part
 of the definition (the fp32 scale, the bf16 activations).
 """
-from . import quant, alloc, moe, sched  # noqa: F401
+from . import quant, alloc, moe, sched, swap  # noqa: F401

@@ -226,6 +226,36 @@ pw_status pw_budget_step(pw_ctx* ctx, const pw_budget_policy* policy, uint64_t k
                          const double* importance, const double* loss, int32_t* action,
                          uint64_t* budget_out, int32_t* pressure, void* stream);
 
+/* ---- Host tier: expert pages swapped out to CPU memory ----
+ * PagedWeight page, section "Dynamic Paging": the router decides which
+ * experts a pass needs and their pages are fetched; inactive experts' pages
+ * can be swapped out to CPU memory.
+ *
+ * pw_bind_host_tier binds `bytes` of pinned host memory (hipHostMalloc, or
+ * a pinned PyTorch tensor; 256-byte aligned, caller-owned, device
+ * accessible). From then on the pages are packed into it (placement and
+ * capacity as for the pool, PW_ERR_POOL_CAPACITY when they do not fit) and
+ * the pool bound with pw_bind_pool becomes a cache of min(E, pool bytes /
+ * slot) page slots of one 8-bit page each (align_up(3 d F, 256) bytes; no
+ * pool, or one smaller than a slot: no slots). Binding it, or NULL (back
+ * to pages in the pool), invalidates the pages: quantize again. Rebinding
+ * the pool empties the slots and keeps the pages. In each pw_moe_forward,
+ * on the device and without host synchronisation, the routed experts
+ * holding a slot are hits; the others, in ascending expert id, take empty
+ * slots (ascending index), then the slots of experts not routed in this
+ * pass, least recently used first (ties: lower expert id), and have their
+ * page copied in; those left without a slot are read from the host tier
+ * directly in this pass. Requantizing an expert empties its slot. The
+ * library allocates (40 E + 32) bytes of device memory for this state.
+ * Results equal those without a host tier bit for bit. */
+pw_status pw_bind_host_tier(pw_ctx* ctx, void* host, uint64_t bytes);
+
+/* Residency after the forwards enqueued so far (waits for the stream):
+ * slot_of[E] (slot holding each expert's page, -1 none; may be NULL) and
+ * stats[3] (cumulative routed experts that hit, pages copied in, pages read
+ * from the host tier; may be NULL). PW_ERR_STATE without a host tier. */
+pw_status pw_get_residency(pw_ctx* ctx, int32_t* slot_of, uint64_t* stats, void* stream);
+
 /* Timing of the forward kernels on the forward's stream: HIP events
  * (created without the system-scope fence) are recorded just before and
  * after each timed kernel; an event delays the next dispatch by a few

@@ -38,6 +38,12 @@ struct pw_ctx {
     uint8_t* ws = nullptr;
     uint64_t ws_bytes = 0;
 
+    // host tier: with pinned host memory bound, the pages live there and the
+    // pool is a cache of page slots (residency state on the device)
+    uint8_t* host = nullptr;
+    uint64_t host_cap = 0;
+    uint8_t* swap_dev = nullptr;
+
     // host mirror of the page table
     std::vector<pw_page_entry> table;
     bool pages_valid = false;
@@ -116,6 +122,37 @@ double* dev_loss(pw_ctx* c) {
     return reinterpret_cast<double*>(c->dev + 2 * table_bytes(c->E) + align_up((size_t)c->E * 4 + 16, kAlign));
 }
 
+// Host tier helpers. A slot holds any page (the 8-bit page size); at most
+// one slot per expert is useful.
+bool swap_mode(const pw_ctx* c) { return c->host != nullptr; }
+uint64_t slot_bytes(const pw_ctx* c) { return align_up(c->We, kPageAlign); }
+int n_slots(const pw_ctx* c) {
+    if (!c->pool) return 0;
+    return (int)std::min<uint64_t>((uint64_t)c->E, c->pool_cap / slot_bytes(c));
+}
+uint8_t* page_base(const pw_ctx* c) { return swap_mode(c) ? c->host : c->pool; }
+uint64_t page_cap(const pw_ctx* c) { return swap_mode(c) ? c->host_cap : c->pool_cap; }
+
+// residency arrays: addr u64[E], stats u64[3], then i32/u32 slot_of[E],
+// expert_of[E], last_use[E], copy_e[E], copy_s[E], step, ncopy
+size_t swap_bytes(int E) { return (size_t)E * 8 + 24 + (size_t)E * 20 + 8; }
+SwapState swap_state(pw_ctx* c) {
+    SwapState st;
+    uint8_t* b = c->swap_dev;
+    const size_t E = (size_t)c->E;
+    st.addr = reinterpret_cast<uint64_t*>(b);
+    st.stats = reinterpret_cast<uint64_t*>(b + E * 8);
+    int32_t* i = reinterpret_cast<int32_t*>(b + E * 8 + 24);
+    st.slot_of = i;
+    st.expert_of = i + E;
+    st.last_use = reinterpret_cast<uint32_t*>(i + 2 * E);
+    st.copy_e = i + 3 * E;
+    st.copy_s = i + 4 * E;
+    st.step = reinterpret_cast<uint32_t*>(i + 5 * E);
+    st.ncopy = i + 5 * E + 1;
+    return st;
+}
+
 pw_status ensure_device(pw_ctx* c) {
     if (c->dev) {
         int cur = -1;
@@ -156,6 +193,15 @@ FwdWork fwd_work(pw_ctx* c) {
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
     w.O = reinterpret_cast<float*>(b + c->lay.O);
     return w;
+}
+
+// Empty slots, nothing used yet, counters zero (ordered before later work
+// on any stream: hipMemset is synchronous with respect to the host).
+pw_status reset_swap(pw_ctx* c) {
+    const SwapState st = swap_state(c);
+    HIP_TRY(c, hipMemset(c->swap_dev, 0, swap_bytes(c->E)));
+    HIP_TRY(c, hipMemset(st.slot_of, 0xff, (size_t)c->E * 8));   // slot_of and expert_of
+    return PW_OK;
 }
 
 float scale_for(float m, int b) {
@@ -238,7 +284,7 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
             if (u.first > at) holes.push_back({at, u.first});
             at = std::max(at, u.second);
         }
-        if (c->pool_cap > at) holes.push_back({at, c->pool_cap});
+        if (page_cap(c) > at) holes.push_back({at, page_cap(c)});
         std::vector<int> order;
         for (int e = 0; e < E; ++e)
             if (changed[e]) order.push_back(e);
@@ -265,9 +311,10 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
             at += page_bytes(c, bits[e]);
             changed[e] = 1;
         }
-        if (at > c->pool_cap)
-            return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, pool holds %llu",
-                        (unsigned long long)at, (unsigned long long)c->pool_cap);
+        if (at > page_cap(c))
+            return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, %s holds %llu",
+                        (unsigned long long)at, swap_mode(c) ? "host tier" : "pool",
+                        (unsigned long long)page_cap(c));
     }
     list.clear();
     for (int e = 0; e < E; ++e)
@@ -300,7 +347,9 @@ pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s) {
     HIP_TRY(c, hipEventRecord(c->upload_done, s));
     const int f16 = c->desc.master_dtype == PW_MASTER_F16;
     HIP_TRY(c, launch_pack(c->w1, c->w3, c->w2, f16, c->d, c->F, dev_table(c, next), dev_list(c, next),
-                           (int)list.size(), c->pool, s));
+                           (int)list.size(), page_base(c), s));
+    // rewritten pages: their slot copies are stale
+    if (swap_mode(c)) HIP_TRY(c, launch_swap_invalidate(swap_state(c), dev_list(c, next), (int)list.size(), s));
     c->table = nt;
     c->cur = next;
     c->pages_valid = true;
@@ -319,7 +368,7 @@ pw_status check_bits(pw_ctx* c, const uint8_t* bits) {
 
 pw_status need_masters_pool(pw_ctx* c) {
     if (!c->w1 || !c->w3 || !c->w2) return fail(c, PW_ERR_STATE, "no masters bound");
-    if (!c->pool) return fail(c, PW_ERR_STATE, "no pool bound");
+    if (!swap_mode(c) && !c->pool) return fail(c, PW_ERR_STATE, "no pool bound");
     return PW_OK;
 }
 
@@ -431,6 +480,7 @@ void pw_destroy(pw_ctx* c) {
         (void)hipEventDestroy(c->upload_done);
     }
     if (c->host_stage) (void)hipHostFree(c->host_stage);
+    if (c->swap_dev) (void)hipFree(c->swap_dev);
     if (c->dev) (void)hipFree(c->dev);
     delete c;
 }
@@ -465,8 +515,57 @@ pw_status pw_bind_pool(pw_ctx* c, void* pool, uint64_t cap) {
         return fail(c, PW_ERR_INVALID_ARG, "pool must be non-NULL and 256-byte aligned");
     c->pool = static_cast<uint8_t*>(pool);
     c->pool_cap = cap;
+    if (swap_mode(c)) return reset_swap(c);   // pages stay in the host tier; slots start empty
     c->pages_valid = false;
     c->table.assign(c->E, pw_page_entry{});
+    return PW_OK;
+}
+
+pw_status pw_bind_host_tier(pw_ctx* c, void* host, uint64_t bytes) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (host && (uintptr_t)host % kPageAlign)
+        return fail(c, PW_ERR_INVALID_ARG, "host tier must be 256-byte aligned");
+    pw_status st = ensure_device(c);
+    if (st != PW_OK) return st;
+    c->pages_valid = false;
+    c->table.assign(c->E, pw_page_entry{});
+    if (!host) {
+        c->host = nullptr;
+        c->host_cap = 0;
+        return PW_OK;
+    }
+    // the kernels read and write the tier directly: it must be pinned host
+    // memory mapped into the device's address space at the same address
+    // (first and last byte)
+    for (const uint8_t* q : {static_cast<const uint8_t*>(host), static_cast<const uint8_t*>(host) + (bytes ? bytes - 1 : 0)}) {
+        hipPointerAttribute_t at{};
+        if (hipPointerGetAttributes(&at, q) != hipSuccess || at.type != hipMemoryTypeHost ||
+            at.devicePointer != (const void*)q) {
+            (void)hipGetLastError();
+            return fail(c, PW_ERR_INVALID_ARG, "host tier must be pinned, device-mapped host memory (hipHostMalloc)");
+        }
+    }
+    if (!c->swap_dev) {
+        void* p = nullptr;
+        HIP_TRY(c, hipMalloc(&p, swap_bytes(c->E)));
+        c->swap_dev = static_cast<uint8_t*>(p);
+    }
+    c->host = static_cast<uint8_t*>(host);
+    c->host_cap = bytes;
+    return reset_swap(c);
+}
+
+pw_status pw_get_residency(pw_ctx* c, int32_t* slot_of, uint64_t* stats, void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (!swap_mode(c)) return fail(c, PW_ERR_STATE, "no host tier bound");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const SwapState st = swap_state(c);
+    HIP_TRY(c, hipEventSynchronize(c->upload_done));   // staging buffer free
+    HIP_TRY(c, hipMemcpyAsync(c->host_stage, st.slot_of, (size_t)c->E * 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(c, hipMemcpyAsync(c->host_stage + (size_t)c->E * 4, st.stats, 24, hipMemcpyDeviceToHost, s));
+    HIP_TRY(c, hipStreamSynchronize(s));
+    if (slot_of) std::memcpy(slot_of, c->host_stage, (size_t)c->E * 4);
+    if (stats) std::memcpy(stats, c->host_stage + (size_t)c->E * 4, 24);
     return PW_OK;
 }
 
@@ -490,9 +589,10 @@ pw_status pw_quantize_experts(pw_ctx* c, const uint8_t* bits, void* stream) {
     if ((st = need_masters_pool(c)) != PW_OK) return st;
     uint64_t need = 0;
     for (int e = 0; e < c->E; ++e) need += page_bytes(c, bits[e]);
-    if (need > c->pool_cap)
-        return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, pool holds %llu",
-                    (unsigned long long)need, (unsigned long long)c->pool_cap);
+    if (need > page_cap(c))
+        return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, %s holds %llu",
+                    (unsigned long long)need, swap_mode(c) ? "host tier" : "pool",
+                    (unsigned long long)page_cap(c));
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = ensure_absmax(c, s)) != PW_OK) return st;
@@ -613,13 +713,25 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
     const int64_t pairs = (int64_t)T * c->k;
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
+    // pages: pool + offset, or with a host tier the addresses of this pass
+    // (slot or host tier) after the missing pages are copied in
+    const uint8_t* base = c->pool;
+    DevTable tab = dev_table(c, c->cur);
+    if (swap_mode(c)) {
+        const SwapState st = swap_state(c);
+        const int S = n_slots(c);
+        HIP_TRY(c, launch_swap_in(st, w, tab, c->E, S, std::min(S, max_act), c->We, c->pool, c->host,
+                                  slot_bytes(c), s));
+        tab.off = st.addr;
+        base = nullptr;
+    }
     const int P = c->desc.max_tokens * c->k;
     // many tokens per expert: dense tiles on the matrix cores (weights read
     // once per 64 tokens); few: the streaming kernels (weights read once)
     if (gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act) {
         GemmArgs ga;
-        ga.pool = c->pool;
-        ga.tab = dev_table(c, c->cur);
+        ga.pool = base;
+        ga.tab = tab;
         ga.w = w;
         ga.x = static_cast<const uint16_t*>(x);
         ga.d = c->d;
@@ -638,8 +750,8 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, 1, y, s, tm[3]));
     } else {
         FfnArgs fa;
-        fa.pool = c->pool;
-        fa.tab = dev_table(c, c->cur);
+        fa.pool = base;
+        fa.tab = tab;
         fa.w = w;
         fa.x = static_cast<const uint16_t*>(x);
         fa.d = c->d;

@@ -143,6 +143,23 @@ hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t = {});
 
+// Host tier: device state of the slot cache (kernels_swap.hip).
+struct SwapState {
+    int32_t* slot_of;     // [E] slot holding the expert's page, -1 none
+    int32_t* expert_of;   // [S] expert whose page a slot holds, -1 empty
+    uint32_t* last_use;   // [E] pass that last routed to the expert (0 never)
+    uint32_t* step;       // [1] passes so far
+    uint64_t* stats;      // [3] hits, pages copied in, pages read from the host tier
+    int32_t* ncopy;       // [1] copies of the current pass
+    int32_t* copy_e;      // [S] expert of each copy
+    int32_t* copy_s;      // [S] slot of each copy
+    uint64_t* addr;       // [E] page address for the current pass
+};
+hipError_t launch_swap_in(const SwapState& st, const FwdWork& w, const DevTable& tab, int E, int S,
+                          int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host, uint64_t slot_bytes,
+                          hipStream_t s);
+hipError_t launch_swap_invalidate(const SwapState& st, const int32_t* list, int n, hipStream_t s);
+
 // ---- host allocator (alloc.cpp) ----
 pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,
                            uint64_t B, uint8_t* bits_out, std::string* err);

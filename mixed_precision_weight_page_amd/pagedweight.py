@@ -78,6 +78,8 @@ _SIGNATURES = {
     "pw_budget_decide": (ctypes.c_int, [ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, ctypes.c_int32, _P,
                                         ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, _P, _P, _P]),
     "pw_budget_step": (ctypes.c_int, [_P, ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, _P, _P, _P, _P, _P, _P]),
+    "pw_bind_host_tier": (ctypes.c_int, [_P, _P, ctypes.c_uint64]),
+    "pw_get_residency": (ctypes.c_int, [_P, _P, _P, _P]),
     "pw_profile": (ctypes.c_int, [_P, ctypes.c_int32]),
     "pw_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(ProfileData)]),
     "pw_last_error": (ctypes.c_char_p, [_P]),
@@ -257,6 +259,31 @@ class PagedMoELayer:
         _check(lib().pw_bind_pool(self._ctx, _dev(pool, torch.uint8, "pool"), pool.numel()), self._ctx)
         self._keep["pool"] = pool
 
+    def bind_host_tier(self, host: Optional[torch.Tensor]):
+        """Pages in pinned host memory, the pool a cache of page slots
+        (pw_bind_host_tier); None goes back to pages in the pool."""
+        if host is None:
+            _check(lib().pw_bind_host_tier(self._ctx, None, 0), self._ctx)
+            self._keep.pop("host", None)
+            return
+        if host.device.type != "cpu" or not host.is_pinned() or host.dtype != torch.uint8 or not host.is_contiguous():
+            raise ValueError("host tier must be a contiguous pinned uint8 CPU tensor")
+        _check(lib().pw_bind_host_tier(self._ctx, host.data_ptr(), host.numel()), self._ctx)
+        self._keep["host"] = host
+
+    def slot_bytes(self) -> int:
+        """Bytes of one page slot of the host tier's device cache (an 8-bit page)."""
+        return (3 * self.d * self.F + 255) // 256 * 256
+
+    def residency(self, stream=None):
+        """pw_get_residency: (slot of each expert, -1 none; dict of hits,
+        pages copied in, pages read from the host tier)."""
+        slots = np.zeros(self.E, dtype=np.int32)
+        stats = np.zeros(3, dtype=np.uint64)
+        _check(lib().pw_get_residency(self._ctx, slots.ctypes.data, stats.ctypes.data, _stream(stream)),
+               self._ctx)
+        return slots, dict(hits=int(stats[0]), copies=int(stats[1]), host_reads=int(stats[2]))
+
     def workspace_bytes(self) -> int:
         return int(lib().pw_workspace_bytes(self._ctx))
 
@@ -346,6 +373,11 @@ class PagedMoELayer:
         pool = torch.zeros(max(256, int(nbytes)), dtype=torch.uint8, device=device)
         self.bind_pool(pool)
         return pool
+
+    def alloc_host_tier(self, nbytes: int) -> torch.Tensor:
+        host = torch.zeros(max(256, int(nbytes)), dtype=torch.uint8, pin_memory=True)
+        self.bind_host_tier(host)
+        return host
 
     def alloc_workspace(self, device="cuda") -> torch.Tensor:
         ws = torch.empty(max(256, self.workspace_bytes()), dtype=torch.uint8, device=device)

@@ -16,7 +16,7 @@ bytes = packed W1 + W3 bytes of the experts the step routes to, divided by
 the kernel's mean duration from HIP events on the forward's stream.
 cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample.
 
-Other workloads: --workload decode_fine | prefill | dynamic | tiny.
+Other workloads: --workload decode_fine | prefill | dynamic | kvtrace | swap | tiny.
 """
 from __future__ import annotations
 
@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_coarse",
-                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "kvtrace", "tiny"])
+                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "kvtrace", "swap", "tiny"])
     ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")
     ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,6 +229,8 @@ def main():
         del src, dst
     if args.workload == "kvtrace":
         return bench_kvtrace(args, synth.WORKLOADS["dynamic"], log)
+    if args.workload == "swap":
+        return bench_swap(args, synth.WORKLOADS["decode_fine"], log)
     wl = synth.WORKLOADS[args.workload]
     if args.workload == "dynamic":
         return bench_dynamic(args, wl, log)
@@ -408,6 +410,78 @@ def bench_kvtrace(args, wl, log):
                                   "KV-cache trace"},
            "budget_changes": changes, "shrinks": actions.count(1), "grows": actions.count(2),
            "mean_budget_bits_per_weight": bits_sum / timed}
+    print(json.dumps(out), flush=True)
+
+
+def bench_swap(args, wl, log, T=8, slots=32):
+    """The decode_fine layer with its pages in a pinned host tier and 32
+    device slots for its 128 experts: T = 8 tokens per step, logits N(0, 1)
+    plus log p_e (routing in proportion to importance), 5 warm-up and
+    `steps` timed forwards (at least 200). Reports tokens/s with the hits,
+    copies and host reads the timed steps made, and the same steps with
+    every page in the device pool for comparison."""
+    import numpy as np
+    import torch
+
+    import synth
+    from mixed_precision_weight_page_amd import PagedMoELayer
+    masters = synth.expert_weights(wl, device="cuda")
+    p = np.asarray(synth.importance(wl), dtype=np.float64)
+    bias = torch.tensor(np.log(p), dtype=torch.float32, device="cuda")
+    steps = max(200, args.steps)
+    batches = []
+    for i in range(64):
+        x, lg = synth.tokens(wl, T=T, device="cuda", step=i)
+        batches.append((x, (lg + bias).contiguous()))
+    y = torch.empty((T, wl.d), dtype=torch.float32, device="cuda")
+
+    def layer_with(host_tier):
+        layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=T, master_dtype=wl.master)
+        layer.bind_masters(*masters)
+        layer.alloc_workspace()
+        if host_tier:
+            layer.alloc_host_tier(layer.pool_bytes_for_bits([8] * wl.E))
+            layer.alloc_pool(slots * layer.slot_bytes())
+        else:
+            layer.alloc_pool(layer.pool_bytes_for_bits([8] * wl.E))
+        layer.set_budget(wl.budget_bits(), p)
+        torch.cuda.synchronize()
+        return layer
+
+    def timed(layer):
+        for i in range(args.warmup):
+            layer.moe_forward(*batches[i % 64], y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            layer.moe_forward(*batches[i % 64], y)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    tiered = layer_with(True)
+    _, st0 = tiered.residency()
+    el = timed(tiered)
+    _, st1 = tiered.residency()
+    table = tiered.get_page_table()
+    mean_page = float(np.mean([t["nbytes"] for t in table]))
+    d = {k: st1[k] - st0[k] for k in st1}
+    routed = d["hits"] + d["copies"] + d["host_reads"]
+    del tiered
+    resident = layer_with(False)
+    el_res = timed(resident)
+    log(f"swap: {d} over {steps + args.warmup} forwards")
+    out = {"metric": METRIC, "value": T * steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "ms_per_step": 1e3 * el / steps, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": f"swap: decode_fine layer (E=128, d_model=2048, d_ff=768, top-8, avg 4 bits) "
+                                  f"with its pages in pinned host memory and {slots} device page slots, "
+                                  f"{T} tokens per step routed in proportion to importance",
+                      "slots": slots, "tokens": T},
+           "hit_rate": d["hits"] / routed if routed else None,
+           "pages_copied_per_step": d["copies"] / (steps + args.warmup),
+           "host_reads_per_step": d["host_reads"] / (steps + args.warmup),
+           "host_link_GBps": (d["copies"] + d["host_reads"]) * mean_page / (el * (steps + args.warmup) / steps) / 1e9,
+           "all_resident_tokens_per_s": T * steps / el_res}
     print(json.dumps(out), flush=True)
 
 

@@ -151,3 +151,25 @@ def test_unbinding_the_host_tier_needs_new_pages():
         b.moe_forward(x.cuda(), logits.cuda())
     with pytest.raises(PagedWeightError):
         b.residency()
+
+
+def test_many_experts_and_slots():
+    # 300 experts (one wave per token in the router), 100 slots: the plan
+    # kernel's scans and ranks over more than 256 entries
+    wl = synth.WORKLOADS["tiny"].scaled(name="swap_e300", E=300, k=6, T=48)
+    rng = np.random.default_rng(3)
+    bits = rng.choice([3, 4, 8], size=wl.E).tolist()
+    _, a, b, host, slots = _pair(100, bits, wl)
+    res = oswap.Residency(wl.E, 100)
+    for step in range(8):
+        T = [48, 5, 30, 1][step % 4]
+        x, logits = synth.tokens(wl, T=T, step=400 + step)
+        log(f"swap e300 step {step}: T={T}")
+        ya = a.moe_forward(x.cuda(), logits.cuda())
+        yb = b.moe_forward(x.cuda(), logits.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb)
+        ids, _ = moe.route(logits, wl.k)
+        res.forward(sorted(set(ids.flatten().tolist())))
+        _check_slots(b, host, slots, res)
+    assert res.host_reads > 0 and res.copies > 100

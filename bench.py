@@ -247,7 +247,10 @@ def main():
     tokens_per_s = T * r["steps"] / r["elapsed"]
     ms = 1e3 * r["elapsed"] / r["steps"]
     gu_ms = r["prof"]["gate_up_ms"]
-    gu_bytes = r["bytes_gu_timed"] / r["timed_forwards"] if r["timed_forwards"] else 0.0
+    # packed W1+W3 bytes per launch: of the forwards that carried events, or
+    # of all timed forwards when none did (--no-profile)
+    gu_bytes = (r["bytes_gu_timed"] / r["timed_forwards"] if r["timed_forwards"]
+                else r["bytes_gu"] / r["steps"])
     gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms > 0 else None
     fwd_gbps = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
     traffic = traffic_from_profiles(args.workload, T)

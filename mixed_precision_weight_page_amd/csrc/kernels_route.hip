@@ -10,8 +10,8 @@
 // by expert id), so the longest tiles are dispatched first.
 //
 // Top-k per token: with at most 256 experts a row of 16 lanes routes one
-// token (DPP reductions within the row), else a wave (shuffles). Up to 16
-// tokens: one workgroup does everything. Up to kFusedMaxPairs pairs: a router kernel over many workgroups, then one
+// token (DPP reductions within the row), else a wave (shuffles). Up to 64
+// tokens (16 with more than 256 experts): one workgroup does everything. Up to kFusedMaxPairs pairs: a router kernel over many workgroups, then one
 // workgroup ranks and offsets. Larger batches: router; ranks per expert and
 // chunk of kRankChunk tokens; counts, chunk prefixes and offsets in one
 // workgroup; pair positions over many workgroups. Kernel boundaries carry
@@ -31,9 +31,11 @@ constexpr int kMaxPerLane = kMaxExperts / 64;  // 16 logits per lane
 constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / 64;
 constexpr int kRowMaxExperts = 256;             // 16 lanes per token up to this many experts
-// One workgroup routes and groups up to this many tokens; beyond, the top-k
-// (VALU-bound) is spread over many workgroups and only the grouping stays in
-// one.
+// One workgroup routes and groups up to this many tokens (one pass of its
+// 64 rows of 16 lanes with at most 256 experts, one token per wave else);
+// beyond, the top-k is spread over many workgroups and only the grouping
+// stays in one.
+constexpr int kFusedMaxTokensRow = 64;
 constexpr int kFusedMaxTokens = 16;
 
 __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
@@ -325,7 +327,7 @@ __device__ __forceinline__ void rank_small(int T, int E, int k, const int* s_ids
     else rank_small_t<32>(T, E, k, s_ids, s_rank, s_cnt, w);
 }
 
-// ---- small batches (T <= kFusedMaxTokens): everything in one workgroup ----
+// ---- small batches (up to one pass of rows or waves): everything in one workgroup ----
 __global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWork w,
                                                              const int32_t* bits) {
     __shared__ int s_ids[kFusedMaxPairs];
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWo
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
                         KTimer t) {
     const hipEvent_t none = nullptr;
-    if (a.T <= kFusedMaxTokens && a.T * a.k <= kFusedMaxPairs)
+    if (a.T <= (a.E <= kRowMaxExperts ? kFusedMaxTokensRow : kFusedMaxTokens) && a.T * a.k <= kFusedMaxPairs)
         return launch_timed(route_fused_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
     const int per_block = a.E <= kRowMaxExperts ? 16 : 4;
     hipError_t err = launch_timed(route_kernel, dim3((a.T + per_block - 1) / per_block), dim3(256), 0, s, t.start,

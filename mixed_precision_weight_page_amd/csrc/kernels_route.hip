@@ -132,47 +132,79 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+// (logit, expert) as one 64-bit key ordered like better(): the logit's bits
+// made order-preserving as an unsigned integer above, the complement of the
+// expert id below (equal logits: lower id is larger). 0 is below every key;
+// a zero logit decodes as +0.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);   // -0 ties with +0, as in better()
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const int lo = dpp_i<CTRL>((int)(uint32_t)x), hi = dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t row_max_key(uint64_t k) {
+    uint64_t o = dpp_u64<kQuadXor1>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kQuadXor2>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kRowHalfMirror>(k);
+    k = o > k ? o : k;
+    o = dpp_u64<kRowMirror>(k);
+    return o > k ? o : k;
+}
+
 // The row of 16 lanes containing this thread routes token t (all lanes of
 // the row call it with the same t; `valid` false for a row past the batch).
+// Top-k: k rounds of the row's largest key, each removed from its lane; the
+// softmax weights use the native base-2 exponential of (v - top) log2(e).
 template <int PER>
 __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w, int t, bool valid,
                                             int* s_ids) {
     const int l16 = threadIdx.x & 15;
     const float* row = a.logits + (int64_t)t * a.E;
     float v[PER];
+    uint64_t key[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = l16 + 16 * i;
-        v[i] = (valid && e < a.E) ? row[e] : -INFINITY;
+        const bool in = valid && e < a.E;
+        v[i] = in ? row[e] : -INFINITY;
+        key[i] = in ? route_key(v[i], e) : 0ull;
     }
     int id0 = 0, id1 = 0;
     float val0 = -INFINITY, val1 = -INFINITY, top = -INFINITY;
-    uint32_t taken = 0;   // bit i: v[i] already chosen
     for (int j = 0; j < a.k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+        uint64_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = l16 + 16 * i;
-            if (e < a.E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-                bv = v[i];
-                be = e;
-            }
-        }
-        row_argmax(bv, be);
-        if ((be & 15) == l16) taken |= 1u << (be >> 4);
+        for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
+        best = row_max_key(best);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) key[i] = key[i] == best ? 0ull : key[i];
+        const float bv = key_value(best);
+        const int be = key_expert(best);
         if (j == 0) top = bv;
         if (j == l16) { id0 = be; val0 = bv; }
         if (j == l16 + 16) { id1 = be; val1 = bv; }
     }
+    constexpr float kLog2e = 1.4426950408889634f;
     float sum_all = 0.0f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = l16 + 16 * i;
-        if (e < a.E) sum_all += expf(v[i] - top);
+        if (e < a.E) sum_all += __builtin_amdgcn_exp2f((v[i] - top) * kLog2e);
     }
-    const float m0 = l16 < a.k ? expf(val0 - top) : 0.0f;
-    const float m1 = l16 + 16 < a.k ? expf(val1 - top) : 0.0f;
+    const float m0 = l16 < a.k ? __builtin_amdgcn_exp2f((val0 - top) * kLog2e) : 0.0f;
+    const float m1 = l16 + 16 < a.k ? __builtin_amdgcn_exp2f((val1 - top) * kLog2e) : 0.0f;
     const float den = row_sum(a.renorm ? m0 + m1 : sum_all);
     if (!valid) return;
     if (l16 < a.k) {

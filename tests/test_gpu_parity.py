@@ -68,6 +68,9 @@ def test_router_matches_oracle(wl, T):
     # plant exact ties: equal logits must resolve to the lower index
     logits[0, :] = 0.25
     logits[1, 3] = logits[1, 5] = logits[1].max() + 1.0
+    # -0 and +0 are equal logits too: the lower index (holding -0) first
+    logits[2, :] = -1.0
+    logits[2, 1], logits[2, 4] = -0.0, 0.0
     ids, g, counts = layer.route(logits.cuda())
     torch.cuda.synchronize()
     rid, rg = moe.route(logits, wl.k)

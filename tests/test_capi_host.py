@@ -323,3 +323,19 @@ def test_layers_solver_at_model_scale(L):
     want, want_obj = alloc.solve_dp([v for p in ps for v in p], [r for Lx in Ls for r in Lx], [We] * (n * E), B)
     assert flat == want
     assert obj == want_obj
+
+
+def test_host_tier_errors_without_gpu(L):
+    st, ctx = make_ctx(L)
+    assert st == PW_OK
+    try:
+        # misaligned host tier: rejected before any device call
+        assert L.pw_bind_host_tier(ctx, ctypes.c_void_p(0x1001), 4096) == INVALID
+        # no host tier bound: residency is a state error
+        slots = np.zeros(4, dtype=np.int32)
+        stats = np.zeros(3, dtype=np.uint64)
+        assert L.pw_get_residency(ctx, slots.ctypes.data, stats.ctypes.data, None) == STATE
+        assert L.pw_bind_host_tier(None, None, 0) == INVALID
+        assert L.pw_get_residency(None, None, None, None) == INVALID
+    finally:
+        L.pw_destroy(ctx)

@@ -19,9 +19,10 @@
 // v_mfma_f32_16x16x32_f16, fp32 accumulate.
 //
 // Tile order: expert (in the active list, 8-bit first), row tile, token
-// tile; workgroup b runs tile (b % 8) * N/8 + b / 8, so each XCD (which
-// receives every eighth workgroup) walks one contiguous range: the workgroups
-// resident on an XCD share weight tiles and token rows through its L2.
+// tile; with N tiles in this forward, workgroup b runs tile
+// (b % 8) * ceil(N/8) + b / 8, so each XCD (which receives every eighth
+// workgroup) walks one contiguous eighth: the workgroups resident on an XCD
+// share weight tiles and token rows through its L2.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -374,14 +375,19 @@ __device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, int e, in
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_tiles, int ntiles) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_tiles) {
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
     __shared__ int tok[BN];
-    // XCD swizzle: the eighth of the tile range that this workgroup's XCD walks
-    const int L = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
-    const int tg = L / row_tiles;                  // L lies in the range of token tile tg's expert
+    // XCD swizzle: the eighth of this forward's tiles (the grid is sized for
+    // the most a batch can have) that this workgroup's XCD walks, so the
+    // XCDs get equal shares and the unused workgroups are spread over them
     const int na = a.w.n_act[0];
-    if (tg >= a.w.tt_off[na]) return;
+    const int used = a.w.tt_off[na] * row_tiles;
+    const int share = (used + 7) >> 3;
+    const int i = blockIdx.x >> 3;
+    const int L = (blockIdx.x & 7) * share + i;
+    if (i >= share || L >= used) return;
+    const int tg = L / row_tiles;                  // L lies in the range of token tile tg's expert
     int lo = 0, hi = na;                           // expert slot: tt_off[lo] <= tg < tt_off[lo + 1]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -414,7 +420,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
     ntiles = (ntiles + 7) / 8 * 8;
     const size_t lds = 2 * (size_t)BN * LDX * 2;
     return launch_timed(gemm_kernel<MODE>, dim3((unsigned)ntiles), dim3(kThreads), lds, s, t.start,
-                        t.stop, a, row_tiles, (int)ntiles);
+                        t.stop, a, row_tiles);
 }
 
 }  // namespace

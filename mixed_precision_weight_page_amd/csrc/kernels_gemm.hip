@@ -331,25 +331,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     for (int j = 0; j < PD; ++j)
         if (s0 + j < S) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
+    if constexpr (MODE == 0) {
+        // SwiGLU rows h = silu(s W1 x) * (s W3 x) of the tile's 64 tokens x
+        // 128 rows go through LDS (the token buffers are free after the last
+        // step's barrier), already at the K-slots the down projection's
+        // B-bit codes expect, then to H in coalesced 16-byte chunks. silu with
+        // the native base-2 exponential and reciprocal: h is stored as fp16.
+        constexpr int HS = tile_rows<0>() + 8;   // LDS row (halves), padded against bank conflicts
+        constexpr float kLog2e = 1.4426950408889634f;
+        _Float16* hs = smem;
 #pragma unroll
-    for (int jt = 0; jt < NA; ++jt) {
-        const int n = 16 * jt + r;
-        if (n >= nt) continue;
-        const int pos = base + t0 + n;
+        for (int jt = 0; jt < NA; ++jt) {
+            const int n = 16 * jt + r;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            if constexpr (MODE == 0) {
-                // rows 32 c0 + 16 blk + 4 g + v of H, stored at the K-slots
-                // the down projection's B-bit codes expect
-                const int c0 = (rt * tile_rows<0>() + 32 * wave) / 32;
-                _Float16* hrow = a.w.H + (int64_t)pos * a.F + 32 * c0;
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float av = s * acc[0][blk][jt][v];
                     const float cv = s * acc[1][blk][jt][v];
-                    hrow[slot_of<B>(16 * blk + 4 * g + v)] = (_Float16)(av / (1.0f + expf(-av)) * cv);
+                    const float h = av * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-av * kLog2e)) * cv;
+                    hs[n * HS + 32 * wave + slot_of<B>(16 * blk + 4 * g + v)] = (_Float16)h;
                 }
-            } else {
+        }
+        __syncthreads();
+        const int col0 = rt * tile_rows<0>();
+        for (int c = tid; c < nt * (tile_rows<0>() / 8); c += kThreads) {
+            const int n = c / (tile_rows<0>() / 8), ch = c % (tile_rows<0>() / 8);
+            *reinterpret_cast<u32x4*>(a.w.H + (int64_t)(base + t0 + n) * a.F + col0 + 8 * ch) =
+                *reinterpret_cast<const u32x4*>(hs + n * HS + 8 * ch);
+        }
+    } else {
+#pragma unroll
+        for (int jt = 0; jt < NA; ++jt) {
+            const int n = 16 * jt + r;
+            if (n >= nt) continue;
+            const int pos = base + t0 + n;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     const int row = rt * tile_rows<1>() + 64 * wave + 32 * m + 16 * blk + 4 * g;
@@ -360,7 +378,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                     o.w = s * acc[m][blk][jt][3];
                     *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + row) = o;
                 }
-            }
         }
     }
 }

@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "dequant.h"
 #include "pw_internal.h"
 
@@ -43,6 +45,9 @@ constexpr int kThreads = 256;
 template <int MODE>
 constexpr int tile_rows() { return MODE == 0 ? 128 : 256; }
 constexpr int BN = kGemmTokens;  // tokens per tile
+// LDS row (floats) of the down tile's output staging: 256 rows + padding
+// against bank conflicts; 32 tokens at a time
+constexpr int kOutStride = 256 + 4;
 
 template <int B>
 struct Run {
@@ -361,23 +366,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
                 *reinterpret_cast<const u32x4*>(hs + n * HS + 8 * ch);
         }
     } else {
+        // the tile's 256 output rows of each token are contiguous in O: 32
+        // tokens at a time go through LDS, then out as whole rows of 16-byte
+        // chunks
+        float* os = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int jt = 0; jt < NA; ++jt) {
-            const int n = 16 * jt + r;
-            if (n >= nt) continue;
-            const int pos = base + t0 + n;
+        for (int half = 0; half < 2; ++half) {
+            if (2 * half >= NA) break;
+            if (half) __syncthreads();   // the previous half's rows are out
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int q = 0; q < 2; ++q) {
+                const int jt = 2 * half + q;
+                if (jt < NA) {
+                    const int n = 16 * q + r;
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    const int row = rt * tile_rows<1>() + 64 * wave + 32 * m + 16 * blk + 4 * g;
-                    float4 o;
-                    o.x = s * acc[m][blk][jt][0];
-                    o.y = s * acc[m][blk][jt][1];
-                    o.z = s * acc[m][blk][jt][2];
-                    o.w = s * acc[m][blk][jt][3];
-                    *reinterpret_cast<float4*>(a.w.O + (int64_t)pos * a.d + row) = o;
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int blk = 0; blk < 2; ++blk) {
+                            const int row = 64 * wave + 32 * m + 16 * blk + 4 * g;
+                            *reinterpret_cast<f32x4*>(os + n * kOutStride + row) = s * acc[m][blk][jt];
+                        }
                 }
+            }
+            __syncthreads();
+            const int n0 = 32 * half;
+            const int rows = min(32, nt - n0);
+            constexpr int kChunks = tile_rows<1>() / 4;   // 16-byte chunks per token row
+            for (int c = tid; c < rows * kChunks; c += kThreads) {
+                const int n = c / kChunks, ch = c % kChunks;
+                *reinterpret_cast<u32x4*>(a.w.O + (int64_t)(base + t0 + n0 + n) * a.d + rt * tile_rows<1>() +
+                                          4 * ch) = *reinterpret_cast<const u32x4*>(os + n * kOutStride + 4 * ch);
+            }
         }
     }
 }
@@ -435,7 +454,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
     const int64_t tt_max = (a.P_used + BN - 1) / BN + a.max_act;
     int64_t ntiles = tt_max * row_tiles;
     ntiles = (ntiles + 7) / 8 * 8;
-    const size_t lds = 2 * (size_t)BN * LDX * 2;
+    // two token-row buffers; the down tile's output staging may need more
+    const size_t lds = std::max<size_t>(2 * (size_t)BN * LDX * 2, MODE == 1 ? 32 * kOutStride * 4 : 0);
     return launch_timed(gemm_kernel<MODE>, dim3((unsigned)ntiles), dim3(kThreads), lds, s, t.start,
                         t.stop, a, row_tiles);
 }

@@ -129,20 +129,25 @@ __device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4]) {
 
 // Token rows for the gate/up tiles, once per forward: xp[i][t] = x[t] as
 // fp16 in the K order of the codes of bit-width kBits[i], for each
-// bit-width some expert uses (bit i of mask). grid (T, 3).
-__global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int d, int mask,
+// bit-width some expert uses (bit i of mask). One thread per 32-activation
+// group of a token: the group is read once and written to every plane in
+// use. grid ceil(T d / 32 / 256).
+__global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int T, int d, int mask,
                                                           _Float16* xp, int64_t plane) {
-    const int i = blockIdx.y;
-    if (!((mask >> i) & 1)) return;
-    const int64_t t = blockIdx.x;
-    for (int grp = threadIdx.x; grp < d / 32; grp += kThreads) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + t * d + 32 * grp);
-        uint4 in[4] = {src[0], src[1], src[2], src[3]};
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int gpr = d / 32;
+    if (idx >= (int64_t)T * gpr) return;
+    const int64_t off = idx * 32;   // t * d + 32 grp
+    const uint4* src = reinterpret_cast<const uint4*>(x + off);
+    const uint4 in[4] = {src[0], src[1], src[2], src[3]};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        if (!((mask >> i) & 1)) continue;
         uint4 o[4];
         if (i == 0) permute32<true, 3>(in, o);
         else if (i == 1) permute32<true, 4>(in, o);
         else permute32<true, 8>(in, o);
-        uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + t * d + 32 * grp);
+        uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + off);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = o[q];
     }
@@ -465,8 +470,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
 bool gemm_supported(int d, int F) { return d % tile_rows<1>() == 0 && F % tile_rows<0>() == 0; }
 
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
-    return launch_timed(prep_x_kernel, dim3((unsigned)a.T, 3), dim3(kThreads), 0, s, (hipEvent_t) nullptr,
-                        (hipEvent_t) nullptr, a.x, a.d, a.bits_mask, const_cast<_Float16*>(a.xp), a.xp_plane);
+    const int64_t groups = (int64_t)a.T * (a.d / 32);
+    return launch_timed(prep_x_kernel, dim3((unsigned)((groups + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                        (hipEvent_t) nullptr, (hipEvent_t) nullptr, a.x, a.T, a.d, a.bits_mask,
+                        const_cast<_Float16*>(a.xp), a.xp_plane);
 }
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<0>(a, s, t); }
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<1>(a, s, t); }

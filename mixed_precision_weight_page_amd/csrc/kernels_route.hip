@@ -261,6 +261,49 @@ __device__ __forceinline__ T block_scan(T v, T* s_wave, T* total) {
     return v + (wave > 0 ? s_wave[wave - 1] : T(0));
 }
 
+// Inclusive scans of two values at once over the 1024 threads (one set of
+// barriers for both).
+__device__ __forceinline__ void block_scan2(int& a, long long& b, int* sa, long long* sb, int* ta, long long* tb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int na = __shfl_up(a, o);
+        const long long nb = __shfl_up(b, o);
+        if (lane >= o) {
+            a += na;
+            b += nb;
+        }
+    }
+    __syncthreads();
+    if (lane == 63) {
+        sa[wave] = a;
+        sb[wave] = b;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int x = lane < kWaves ? sa[lane] : 0;
+        long long y = lane < kWaves ? sb[lane] : 0ll;
+        for (int o = 1; o < kWaves; o <<= 1) {
+            const int nx = __shfl_up(x, o);
+            const long long ny = __shfl_up(y, o);
+            if (lane >= o) {
+                x += nx;
+                y += ny;
+            }
+        }
+        if (lane < kWaves) {
+            sa[lane] = x;
+            sb[lane] = y;
+        }
+    }
+    __syncthreads();
+    *ta = sa[kWaves - 1];
+    *tb = sb[kWaves - 1];
+    if (wave > 0) {
+        a += sa[wave - 1];
+        b += sb[wave - 1];
+    }
+}
+
 // Offsets, bit-ordered active list and token tiles; cnt_of(e) gives the
 // count of expert e. Leaves the offsets in s_off.
 template <class CntF>
@@ -270,19 +313,19 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
     __shared__ long long s_wave_l[kWaves];
     const int tid = threadIdx.x;
     const int c = tid < E ? cnt_of(tid) : 0;
-    int tot;
-    const int inc = block_scan<int>(c, s_wave_i, &tot);
+    // classes: 0 = 8-bit, 1 = 4-bit, 2 = 3-bit; 21-bit counters per class
+    const int b = my_bits;   // bit-width of expert tid (loaded by the caller at kernel entry)
+    const int cls = b == 8 ? 0 : (b == 4 ? 1 : 2);
+    const long long flag = (tid < E && c > 0) ? (1ll << (21 * cls)) : 0ll;
+    // the offsets' scan and the class counters' scan together
+    int inc = c, tot;
+    long long linc = flag, ltot;
+    block_scan2(inc, linc, s_wave_i, s_wave_l, &tot, &ltot);
     if (tid < E) {
         s_off[tid] = inc - c;
         w.off[tid] = inc - c;
     }
     if (tid == 0) w.off[E] = tot;
-    // classes: 0 = 8-bit, 1 = 4-bit, 2 = 3-bit; 21-bit counters per class
-    const int b = my_bits;   // bit-width of expert tid (loaded by the caller at kernel entry)
-    const int cls = b == 8 ? 0 : (b == 4 ? 1 : 2);
-    const long long flag = (tid < E && c > 0) ? (1ll << (21 * cls)) : 0ll;
-    long long ltot;
-    const long long linc = block_scan<long long>(flag, s_wave_l, &ltot);
     const int n8 = (int)(ltot & 0x1fffff), n4 = (int)((ltot >> 21) & 0x1fffff),
               n3 = (int)((ltot >> 42) & 0x1fffff);
     // token tiles of the large-batch kernels, in active-list order
@@ -328,6 +371,26 @@ template <int KMAX>
 __device__ __forceinline__ void rank_small_t(int T, int E, int k, const int* s_ids, int* s_rank, int* s_cnt,
                                              const FwdWork& w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (T <= 64) {
+        // one chunk: ranks and counts straight from the ballots, no running
+        // counts to read back
+        int my[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) my[j] = (j < k && lane < T) ? s_ids[lane * k + j] : -1;
+        for (int e = wave; e < E; e += kWaves) {
+            int slot = -1;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (my[j] == e) slot = j;
+            const uint64_t m = __ballot(slot >= 0);
+            if (slot >= 0) s_rank[lane * k + slot] = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == 0) {
+                s_cnt[e] = __popcll(m);
+                w.cnt[e] = __popcll(m);
+            }
+        }
+        return;
+    }
     for (int e = wave; e < E; e += kWaves)
         if (lane == 0) s_cnt[e] = 0;
     for (int t0 = 0; t0 < T; t0 += 64) {

@@ -677,7 +677,7 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const FwdWork w = fwd_work(c);
-    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
+    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, 1};
     HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s));
     const size_t P = (size_t)T * c->k;
     HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
@@ -709,10 +709,13 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
             c->ev_kind.push_back(j);
         }
     }
-    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
     const int64_t pairs = (int64_t)T * c->k;
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
+    // many tokens per expert: dense tiles on the matrix cores (weights read
+    // once per 64 tokens); few: the streaming kernels (weights read once)
+    const bool dense = gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act;
+    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, dense ? 1 : 0};
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
     // pages: pool + offset, or with a host tier the addresses of this pass
     // (slot or host tier) after the missing pages are copied in
     const uint8_t* base = c->pool;
@@ -726,9 +729,7 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         base = nullptr;
     }
     const int P = c->desc.max_tokens * c->k;
-    // many tokens per expert: dense tiles on the matrix cores (weights read
-    // once per 64 tokens); few: the streaming kernels (weights read once)
-    if (gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act) {
+    if (dense) {
         GemmArgs ga;
         ga.pool = base;
         ga.tab = tab;

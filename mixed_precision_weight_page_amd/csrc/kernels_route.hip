@@ -307,7 +307,7 @@ __device__ __forceinline__ void block_scan2(int& a, long long& b, int* sa, long 
 // Offsets, bit-ordered active list and token tiles; cnt_of(e) gives the
 // count of expert e. Leaves the offsets in s_off.
 template <class CntF>
-__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my_bits, CntF cnt_of,
+__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my_bits, int tiles, CntF cnt_of,
                                                  int* s_off) {
     __shared__ int s_wave_i[kWaves];
     __shared__ long long s_wave_l[kWaves];
@@ -338,6 +338,7 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
     }
     if (tid == 0) w.n_act[0] = n8 + n4 + n3;
     __syncthreads();
+    if (!tiles) return;   // only the large-batch kernels read the token tiles
     const int na = n8 + n4 + n3;
     const int ntt = tid < na ? (s_slot_cnt[tid] + kGemmTokens - 1) / kGemmTokens : 0;
     int ttot;
@@ -350,10 +351,10 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
 // Offsets and pair positions in one workgroup; rank_of(p) gives the rank of
 // pair p, id_of(p) its expert.
 template <class CntF, class RankF, class IdF>
-__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, int my_bits,
+__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, int my_bits, int tiles,
                                          CntF cnt_of, RankF rank_of, IdF id_of) {
     __shared__ int s_off[kMaxExperts];
-    finalize_offsets(E, w, my_bits, cnt_of, s_off);
+    finalize_offsets(E, w, my_bits, tiles, cnt_of, s_off);
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) {
         const int e = id_of(p);
@@ -440,12 +441,12 @@ __global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWor
     __syncthreads();
     rank_small(a.T, a.E, a.k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(a.T, a.E, a.k, w, my_bits, [&](int e) { return s_cnt[e]; },
+    finalize(a.T, a.E, a.k, w, my_bits, a.tiles, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
 // ---- small batches: ranking and offsets of routed pairs in one workgroup ----
-__global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k, FwdWork w,
+__global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k, int tiles, FwdWork w,
                                                              const int32_t* bits) {
     __shared__ int s_ids[kFusedMaxPairs];
     __shared__ int s_rank[kFusedMaxPairs];
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k
     __syncthreads();
     rank_small(T, E, k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(T, E, k, w, my_bits, [&](int e) { return s_cnt[e]; },
+    finalize(T, E, k, w, my_bits, tiles, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(256) void rank_kernel(int T, int k, int C, FwdWork 
 
 // One workgroup: per-expert counts and chunk prefixes, then offsets, the
 // active list and the token tiles.
-__global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, FwdWork w, const int32_t* bits) {
+__global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, int tiles, FwdWork w, const int32_t* bits) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
     const int my_bits = threadIdx.x < E ? bits[threadIdx.x] : 0;
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, FwdWork w
         w.cnt[e] = run;
     }
     __syncthreads();
-    finalize_offsets(E, w, my_bits, [&](int e) { return s_cnt[e]; }, s_off);
+    finalize_offsets(E, w, my_bits, tiles, [&](int e) { return s_cnt[e]; }, s_off);
 }
 
 // grid ceil(P / 256): position of every pair in expert-sorted order.
@@ -543,11 +544,11 @@ hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bit
     if (err != hipSuccess) return err;
     if (a.T * a.k <= kFusedMaxPairs)
         return launch_timed(group_small_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k,
-                            w, bits);
+                            a.tiles, w, bits);
     const int C = (a.T + kRankChunk - 1) / kRankChunk;
     err = launch_timed(rank_kernel, dim3(a.E, C), dim3(256), 0, s, none, none, a.T, a.k, C, w);
     if (err != hipSuccess) return err;
-    err = launch_timed(offsets_kernel, dim3(1), dim3(kBlock), 0, s, none, none, a.E, C, w, bits);
+    err = launch_timed(offsets_kernel, dim3(1), dim3(kBlock), 0, s, none, none, a.E, C, a.tiles, w, bits);
     if (err != hipSuccess) return err;
     const int P = a.T * a.k;
     return launch_timed(scatter_kernel, dim3((P + 255) / 256), dim3(256), 0, s, none, t.stop, P, a.k, C, w);

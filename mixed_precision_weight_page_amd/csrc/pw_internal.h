@@ -96,6 +96,7 @@ hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, 
 struct RouteArgs {
     const float* logits;
     int T, E, k, renorm;
+    int tiles;   // also the large-batch kernels' token tiles (tt_off)
 };
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
                         KTimer t = {});

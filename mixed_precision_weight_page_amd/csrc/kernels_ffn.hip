@@ -374,26 +374,41 @@ hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer 
 }
 
 // y[t] = sum_j g[t,j] * (sum_s O[s][pos(t,j)]) in slot and split order;
-// grid (ceil(d/1024), T)
+// grid (ceil(d/1024), T). The loads of up to 8 slots are issued before any
+// of them is used (a load per slot behind its position's load would expose
+// one memory round trip per slot); the sums keep the slot and split order.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int k, int P, int nsplit,
                                                            float* y) {
     const int t = blockIdx.y;
     const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (col >= d) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const float gj = w.g[p];
-        const float* src = w.O + (int64_t)w.pos[p] * d + col;
-        float4 o = *reinterpret_cast<const float4*>(src);
-        for (int sp = 1; sp < nsplit; ++sp) {
-            const float4 q = *reinterpret_cast<const float4*>(src + (int64_t)sp * P * d);
-            o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 o[8];
+        float gj[8];
+        const float* src[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                const int p = t * k + j0 + u;
+                gj[u] = w.g[p];
+                src[u] = w.O + (int64_t)w.pos[p] * d + col;
+                o[u] = *reinterpret_cast<const float4*>(src[u]);
+            }
         }
-        acc.x = fmaf(gj, o.x, acc.x);
-        acc.y = fmaf(gj, o.y, acc.y);
-        acc.z = fmaf(gj, o.z, acc.z);
-        acc.w = fmaf(gj, o.w, acc.w);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                for (int sp = 1; sp < nsplit; ++sp) {
+                    const float4 q = *reinterpret_cast<const float4*>(src[u] + (int64_t)sp * P * d);
+                    o[u].x += q.x; o[u].y += q.y; o[u].z += q.z; o[u].w += q.w;
+                }
+                acc.x = fmaf(gj[u], o[u].x, acc.x);
+                acc.y = fmaf(gj[u], o[u].y, acc.y);
+                acc.z = fmaf(gj[u], o[u].z, acc.z);
+                acc.w = fmaf(gj[u], o[u].w, acc.w);
+            }
+        }
     }
     *reinterpret_cast<float4*>(y + (int64_t)t * d + col) = acc;
 }

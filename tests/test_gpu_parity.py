@@ -367,3 +367,30 @@ def test_large_batch_matrix_core_path(T):
     layer.quantize_experts(wl.bits)
     y = layer.moe_forward(x.cuda(), logits.cuda())
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
+
+
+EXTREME = [
+    # one expert, top-1, the smallest rows (one 128-code step, two 64-row tiles)
+    (synth.WORKLOADS["tiny"].scaled(name="one", E=1, d=128, F=128, k=1, T=5, bits=(3,)), (5, 1)),
+    (synth.WORKLOADS["tiny"].scaled(name="one8", E=1, d=128, F=128, k=1, T=3, bits=(8,)), (3,)),
+    # the most experts and the largest top-k the library takes
+    (synth.WORKLOADS["tiny"].scaled(name="e1024", E=1024, d=128, F=128, k=32, T=40,
+                                    bits=tuple([8, 4, 3, 4] * 256)), (40, 7)),
+    # on both sides of the matrix-core threshold (mean 64 tokens per routed expert)
+    (synth.WORKLOADS["tiny"].scaled(name="edge", E=2, d=256, F=128, k=1, T=128, bits=(4, 3)), (128, 127)),
+]
+
+
+@pytest.mark.parametrize("wl,Ts", EXTREME, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_extreme_shapes(wl, Ts):
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=max(Ts))
+    log(f"{wl.name}: quantize")
+    layer.quantize_experts(wl.bits)
+    torch.cuda.synchronize()
+    check_pages(layer, pool, masters, wl.bits)
+    for T in Ts:
+        x, logits = synth.tokens(wl, T=T)
+        log(f"{wl.name}: forward T={T}")
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"{wl.name} T={T}")

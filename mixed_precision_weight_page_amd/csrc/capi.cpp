@@ -187,7 +187,7 @@ FwdWork fwd_work(pw_ctx* c) {
     w.off = reinterpret_cast<int32_t*>(b + c->lay.off);
     w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
     w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
-    w.tt_off = reinterpret_cast<int32_t*>(b + c->lay.tt_off);
+    w.tiles = reinterpret_cast<TileDesc*>(b + c->lay.tiles);
     w.ccnt = reinterpret_cast<int32_t*>(b + c->lay.ccnt);
     w.cpre = reinterpret_cast<int32_t*>(b + c->lay.cpre);
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
@@ -405,8 +405,8 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.cnt = take(4 * (uint64_t)E);
     L.off = take(4 * (uint64_t)(E + 1));
     L.act = take(4 * (uint64_t)E);
-    L.n_act = take(4);
-    L.tt_off = take(4 * (uint64_t)(E + 1));
+    L.n_act = take(8);
+    L.tiles = take(sizeof(TileDesc) * ((P + kGemmTokens - 1) / kGemmTokens + (uint64_t)E));
     const uint64_t chunks = ((uint64_t)max_tokens + kRankChunk - 1) / kRankChunk;
     L.ccnt = take(4 * (uint64_t)E * chunks);
     L.cpre = take(4 * (uint64_t)E * chunks);

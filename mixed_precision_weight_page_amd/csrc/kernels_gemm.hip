@@ -155,10 +155,17 @@ __global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int
 
 constexpr int SK = 128;            // K codes per step (one page tile)
 constexpr int LDX = SK;            // LDS row of staged tokens (halves): 256 B, no padding
-// 16-byte chunk c of token row n lives at chunk position c ^ (n % 16) of its
-// row, so the 16 lanes reading one chunk of 16 consecutive rows hit 16
-// different bank groups.
-__device__ __forceinline__ int swz(int n, int c) { return n * (LDX / 8) + (c ^ (n & 15)); }
+// 16-byte chunk c of token row n lives at chunk position c ^ (c / 8 % 2) ^ f(n)
+// of its row, f(n) = n % 16 with its two low bits swapped. Any 8 consecutive
+// lanes then touch 8 different 16-byte bank groups of a 128-byte window (and
+// any 16 lanes 16 groups of 256 bytes), both for the MFMA operand reads (one
+// chunk of consecutive rows) and for the staging stores (two rows, chunks q,
+// q + 4, q + 8, q + 12). A plain c ^ (n % 16) leaves chunks q and q + 8 of a
+// row in the same group: the stores took two passes.
+__device__ __forceinline__ int swz(int n, int c) {
+    const int f = (n & 12) | ((n & 1) << 1) | ((n >> 1) & 1);
+    return n * (LDX / 8) + (c ^ ((c >> 3) & 1) ^ f);
+}
 
 // Steps of codes in flight per wave.
 template <int B>
@@ -210,8 +217,8 @@ __device__ __forceinline__ void sched_step() {
 }
 
 template <int MODE, int B, int NA>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
-                                          int* tok) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int base, int tt, int rt,
+                                          _Float16* smem, int* tok) {
     constexpr int NMAT = 2;   // stream pairs: W1 / W3 (MODE 0), two 32-row halves of W2 (MODE 1)
     constexpr int PD = gemm_depth<B>();
     constexpr int TB = 256 * B;                  // bytes of one 16-row x 128-code tile
@@ -220,8 +227,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int Te = a.w.cnt[e];
-    const int base = a.w.off[e];
     const int t0 = tt * BN;
     const int nt = min(BN, Te - t0);
     const float s = a.tab.scale[e];
@@ -407,12 +412,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int tt, int 
 }
 
 template <int MODE, int B>
-__device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, int e, int tt, int rt, _Float16* smem,
-                                            int* tok) {
-    if (na >= 4) gemm_tile<MODE, B, 4>(a, e, tt, rt, smem, tok);
-    else if (na == 3) gemm_tile<MODE, B, 3>(a, e, tt, rt, smem, tok);
-    else if (na == 2) gemm_tile<MODE, B, 2>(a, e, tt, rt, smem, tok);
-    else gemm_tile<MODE, B, 1>(a, e, tt, rt, smem, tok);
+__device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, const TileDesc& td, int tt, int rt,
+                                            _Float16* smem, int* tok) {
+    if (na >= 4) gemm_tile<MODE, B, 4>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
+    else if (na == 3) gemm_tile<MODE, B, 3>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
+    else if (na == 2) gemm_tile<MODE, B, 2>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
+    else gemm_tile<MODE, B, 1>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
 }
 
 template <int MODE>
@@ -422,33 +427,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     // XCD swizzle: the eighth of this forward's tiles (the grid is sized for
     // the most a batch can have) that this workgroup's XCD walks, so the
     // XCDs get equal shares and the unused workgroups are spread over them
-    const int na = a.w.n_act[0];
-    const int used = a.w.tt_off[na] * row_tiles;
+    const int used = a.w.n_act[1] * row_tiles;
     const int share = (used + 7) >> 3;
     const int i = blockIdx.x >> 3;
     const int L = (blockIdx.x & 7) * share + i;
     if (i >= share || L >= used) return;
-    const int tg = L / row_tiles;                  // L lies in the range of token tile tg's expert
-    int lo = 0, hi = na;                           // expert slot: tt_off[lo] <= tg < tt_off[lo + 1]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.w.tt_off[mid] <= tg) lo = mid; else hi = mid;
-    }
-    const int e = a.w.act[lo];
-    // within the expert's range, row tile major and token tile minor: the
-    // workgroups that stream the same codes are neighbours in dispatch order
-    // and run side by side on one XCD, so the codes come from its L2
-    const int ntt = a.w.tt_off[lo + 1] - a.w.tt_off[lo];
-    const int l = L - a.w.tt_off[lo] * row_tiles;
+    // L lies in the range of token tile L / row_tiles's expert; within an
+    // expert's range, row tile major and token tile minor: the workgroups
+    // that stream the same codes are neighbours in dispatch order and run
+    // side by side on one XCD, so the codes come from its L2
+    const TileDesc td = a.w.tiles[L / row_tiles];
+    const int ntt = (td.cnt + BN - 1) / BN;
+    const int l = L - td.first * row_tiles;
     const int rt = l / ntt;
     const int tt = l - rt * ntt;
-    const int b = a.tab.bits[e];
+    const int b = a.tab.bits[td.e];
     // 16-token blocks holding real tokens (fewer than four only in an
     // expert's last token tile): the MFMAs of the empty ones are skipped
-    const int nblk = (min(BN, a.w.cnt[e] - tt * BN) + 15) >> 4;
-    if (b == 4) dispatch_na<MODE, 4>(nblk, a, e, tt, rt, smem, tok);
-    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, e, tt, rt, smem, tok);
-    else dispatch_na<MODE, 3>(nblk, a, e, tt, rt, smem, tok);
+    const int nblk = (min(BN, td.cnt - tt * BN) + 15) >> 4;
+    if (b == 4) dispatch_na<MODE, 4>(nblk, a, td, tt, rt, smem, tok);
+    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, td, tt, rt, smem, tok);
+    else dispatch_na<MODE, 3>(nblk, a, td, tt, rt, smem, tok);
 }
 
 template <int MODE>

@@ -330,21 +330,36 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
               n3 = (int)((ltot >> 42) & 0x1fffff);
     // token tiles of the large-batch kernels, in active-list order
     __shared__ int s_slot_cnt[kMaxExperts];
+    __shared__ int s_slot_exp[kMaxExperts];
     if (flag) {
         const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
         const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
         w.act[base + before] = tid;
         s_slot_cnt[base + before] = c;
+        s_slot_exp[base + before] = tid;
     }
     if (tid == 0) w.n_act[0] = n8 + n4 + n3;
     __syncthreads();
     if (!tiles) return;   // only the large-batch kernels read the token tiles
     const int na = n8 + n4 + n3;
     const int ntt = tid < na ? (s_slot_cnt[tid] + kGemmTokens - 1) / kGemmTokens : 0;
+    __shared__ int s_first[kMaxExperts];
     int ttot;
     const int tinc = block_scan<int>(ntt, s_wave_i, &ttot);
-    if (tid < na) w.tt_off[tid] = tinc - ntt;
-    if (tid == 0) w.tt_off[na] = ttot;
+    if (tid < na) s_first[tid] = tinc - ntt;
+    if (tid == 0) w.n_act[1] = ttot;
+    __syncthreads();
+    // one descriptor per token tile: the slot whose range holds tile j is
+    // the last one starting at or before j (every slot has at least one tile)
+    for (int j = tid; j < ttot; j += kBlock) {
+        int lo = 0, hi = na;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_first[mid] <= j) lo = mid; else hi = mid;
+        }
+        const int e = s_slot_exp[lo];
+        w.tiles[j] = TileDesc{e, s_first[lo], s_slot_cnt[lo], s_off[e]};
+    }
     __syncthreads();
 }
 

@@ -34,6 +34,13 @@ struct DevTable {
     int32_t* bits;
 };
 
+// One token tile (kGemmTokens sorted pairs of one expert) of the
+// large-batch kernels: its expert, the index of that expert's first token
+// tile, the expert's pair count and its first sorted position.
+struct __attribute__((aligned(16))) TileDesc {
+    int32_t e, first, cnt, off;
+};
+
 // Forward-pass scratch carved out of the bound workspace.
 struct FwdWork {
     int32_t* ids;      // [P] expert of pair p = t*k + j
@@ -44,8 +51,8 @@ struct FwdWork {
     int32_t* cnt;      // [E] tokens per expert
     int32_t* off;      // [E+1] exclusive prefix of cnt
     int32_t* act;      // [E] experts with cnt > 0, ascending
-    int32_t* n_act;    // [1]
-    int32_t* tt_off;   // [E+1] prefix over the active list of ceil(cnt / kGemmTokens)
+    int32_t* n_act;    // [2] active experts; token tiles of the large-batch kernels
+    TileDesc* tiles;   // [ceil(P / kGemmTokens) + E] token tiles in active-list order
     int32_t* ccnt;     // [E, C] pairs of expert e among the tokens of chunk c (kRankChunk tokens)
     int32_t* cpre;     // [E, C] exclusive prefix of ccnt over the chunks
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
@@ -53,7 +60,7 @@ struct FwdWork {
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tt_off, ccnt, cpre, H, O, xp, fwd_end;
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tiles, ccnt, cpre, H, O, xp, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };
@@ -96,7 +103,7 @@ hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, 
 struct RouteArgs {
     const float* logits;
     int T, E, k, renorm;
-    int tiles;   // also the large-batch kernels' token tiles (tt_off)
+    int tiles;   // also the large-batch kernels' token tiles (FwdWork::tiles)
 };
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
                         KTimer t = {});

@@ -203,18 +203,26 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
 // of them. Codes are prefetched PD steps ahead in a register ring; the main
 // loop issues its loads unconditionally so the ring stays full, and LDS
 // chunks of the token rows are staged before the first load when K fits.
+// The expert's page-table entry and token range, read by the kernel in one
+// round of independent loads before its first code load.
+struct ExpertRef {
+    const uint8_t* page;
+    float s;
+    int Te, base;
+};
+
 template <int MODE, int B>
-__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e, int rt, int sp,
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const ExpertRef& ex, int rt, int sp,
                                          int ks0, int nsteps, _Float16* xs, int* tok) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
     constexpr int PD = prefetch_depth<B>();
     constexpr int SB = 16 * kStep * B / 8;   // bytes of one tile: 16 rows x 128 codes
     const int K = MODE == 0 ? a.d : a.F;
     const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
-    const uint8_t* page = a.pool + a.tab.off[e];
-    const float s = a.tab.scale[e];
-    const int Te = a.w.cnt[e];
-    const int base = a.w.off[e];
+    const uint8_t* page = ex.page;
+    const float s = ex.s;
+    const int Te = ex.Te;
+    const int base = ex.base;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
@@ -234,18 +242,18 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, int e,
         if (nt * (nsteps * kStep + 8) * 2 > lds_bytes)
             spc = ((lds_bytes / (2 * nt) - 8) / (kStep * PD)) * PD;
         const int stride = spc * kStep + 8;
-        __syncthreads();   // previous token block done with tok and xs
-        if constexpr (MODE == 0) {
-            if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
-        }
-        __syncthreads();
-        // first codes in flight before the token rows are staged, so the
-        // staging's wait overlaps their latency
+        // first codes in flight before the token ids are read and the token
+        // rows staged, so those round trips overlap their latency
         Codes<B> buf[NMAT][PD];
 #pragma unroll
         for (int j = 0; j < PD; ++j)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
+        __syncthreads();   // previous token block done with tok and xs
+        if constexpr (MODE == 0) {
+            if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
+        }
+        __syncthreads();
         stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
         __syncthreads();
         f32x4 acc[NMAT];
@@ -357,11 +365,12 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArg
     const int rt = rem / nsplit, sp = rem - rt * nsplit;
     const int e = a.w.act[ai];
     const int b = a.tab.bits[e];
+    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], a.w.cnt[e], a.w.off[e]};
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
-    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
-    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
-    else ffn_tile<MODE, 3>(a, lds_bytes, e, rt, sp, sp * nsteps, nsteps, xs, tok);
+    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
+    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
+    else ffn_tile<MODE, 3>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
 }
 
 template <int MODE>

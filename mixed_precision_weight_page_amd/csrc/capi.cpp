@@ -188,6 +188,7 @@ FwdWork fwd_work(pw_ctx* c) {
     w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
     w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
     w.tiles = reinterpret_cast<TileDesc*>(b + c->lay.tiles);
+    w.slots = reinterpret_cast<SlotDesc*>(b + c->lay.slots);
     w.ccnt = reinterpret_cast<int32_t*>(b + c->lay.ccnt);
     w.cpre = reinterpret_cast<int32_t*>(b + c->lay.cpre);
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
@@ -407,6 +408,7 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.act = take(4 * (uint64_t)E);
     L.n_act = take(8);
     L.tiles = take(sizeof(TileDesc) * ((P + kGemmTokens - 1) / kGemmTokens + (uint64_t)E));
+    L.slots = take(sizeof(SlotDesc) * (uint64_t)E);
     const uint64_t chunks = ((uint64_t)max_tokens + kRankChunk - 1) / kRankChunk;
     L.ccnt = take(4 * (uint64_t)E * chunks);
     L.cpre = take(4 * (uint64_t)E * chunks);
@@ -678,7 +680,7 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     hipStream_t s = static_cast<hipStream_t>(stream);
     const FwdWork w = fwd_work(c);
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, 1};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s));
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s));
     const size_t P = (size_t)T * c->k;
     HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(c, hipMemcpyAsync(g, w.g, P * 4, hipMemcpyDeviceToDevice, s));
@@ -715,7 +717,7 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     // once per 64 tokens); few: the streaming kernels (weights read once)
     const bool dense = gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act;
     RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, dense ? 1 : 0};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur).bits, s, tm[0]));
+    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s, tm[0]));
     // pages: pool + offset, or with a host tier the addresses of this pass
     // (slot or host tier) after the missing pages are copied in
     const uint8_t* base = c->pool;

@@ -360,12 +360,12 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArg
     __shared__ int tok[16];
     const int per_expert = tiles * nsplit;
     const int ai = blockIdx.x / per_expert;
+    const SlotDesc sd = a.w.slots[ai];   // stale past the active count, not used then
     if (ai >= a.w.n_act[0]) return;
     const int rem = blockIdx.x - ai * per_expert;
     const int rt = rem / nsplit, sp = rem - rt * nsplit;
-    const int e = a.w.act[ai];
-    const int b = a.tab.bits[e];
-    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], a.w.cnt[e], a.w.off[e]};
+    const int b = sd.bits;
+    const ExpertRef ex{a.pool + sd.page, sd.scale, sd.cnt, sd.off};
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
     if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);

@@ -304,17 +304,29 @@ __device__ __forceinline__ void block_scan2(int& a, long long& b, int* sa, long 
     }
 }
 
-// Offsets, bit-ordered active list and token tiles; cnt_of(e) gives the
-// count of expert e. Leaves the offsets in s_off.
+// Page-table entry of expert threadIdx.x, read at kernel entry.
+struct ExpertPage {
+    uint64_t off;
+    float scale;
+    int bits;
+};
+__device__ __forceinline__ ExpertPage load_page(const DevTable& tab, int E) {
+    const int e = threadIdx.x;
+    return e < E ? ExpertPage{tab.off[e], tab.scale[e], tab.bits[e]} : ExpertPage{0, 0.0f, 0};
+}
+
+// Offsets, bit-ordered active list, the streaming kernels' slot descriptors
+// and the token tiles; cnt_of(e) gives the count of expert e. Leaves the
+// offsets in s_off.
 template <class CntF>
-__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my_bits, int tiles, CntF cnt_of,
-                                                 int* s_off) {
+__device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const ExpertPage& my, int tiles,
+                                                 CntF cnt_of, int* s_off) {
     __shared__ int s_wave_i[kWaves];
     __shared__ long long s_wave_l[kWaves];
     const int tid = threadIdx.x;
     const int c = tid < E ? cnt_of(tid) : 0;
     // classes: 0 = 8-bit, 1 = 4-bit, 2 = 3-bit; 21-bit counters per class
-    const int b = my_bits;   // bit-width of expert tid (loaded by the caller at kernel entry)
+    const int b = my.bits;   // bit-width of expert tid (loaded by the caller at kernel entry)
     const int cls = b == 8 ? 0 : (b == 4 ? 1 : 2);
     const long long flag = (tid < E && c > 0) ? (1ll << (21 * cls)) : 0ll;
     // the offsets' scan and the class counters' scan together
@@ -335,6 +347,7 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
         const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
         const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
         w.act[base + before] = tid;
+        w.slots[base + before] = SlotDesc{my.off, my.scale, tid, b, c, inc - c, 0};
         s_slot_cnt[base + before] = c;
         s_slot_exp[base + before] = tid;
     }
@@ -366,10 +379,10 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, int my
 // Offsets and pair positions in one workgroup; rank_of(p) gives the rank of
 // pair p, id_of(p) its expert.
 template <class CntF, class RankF, class IdF>
-__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, int my_bits, int tiles,
+__device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, const ExpertPage& my, int tiles,
                                          CntF cnt_of, RankF rank_of, IdF id_of) {
     __shared__ int s_off[kMaxExperts];
-    finalize_offsets(E, w, my_bits, tiles, cnt_of, s_off);
+    finalize_offsets(E, w, my, tiles, cnt_of, s_off);
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) {
         const int e = id_of(p);
@@ -440,11 +453,11 @@ __device__ __forceinline__ void rank_small(int T, int E, int k, const int* s_ids
 
 // ---- small batches (up to one pass of rows or waves): everything in one workgroup ----
 __global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWork w,
-                                                             const int32_t* bits) {
+                                                             DevTable tab) {
     __shared__ int s_ids[kFusedMaxPairs];
     __shared__ int s_rank[kFusedMaxPairs];
     __shared__ int s_cnt[kMaxExperts];
-    const int my_bits = threadIdx.x < a.E ? bits[threadIdx.x] : 0;
+    const ExpertPage my = load_page(tab, a.E);
     if (a.E <= kRowMaxExperts) {
         const int r16 = threadIdx.x >> 4;          // 64 rows of 16 lanes
         for (int t0 = 0; t0 < a.T; t0 += kBlock / 16)
@@ -456,23 +469,23 @@ __global__ __launch_bounds__(kBlock) void route_fused_kernel(RouteArgs a, FwdWor
     __syncthreads();
     rank_small(a.T, a.E, a.k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(a.T, a.E, a.k, w, my_bits, a.tiles, [&](int e) { return s_cnt[e]; },
+    finalize(a.T, a.E, a.k, w, my, a.tiles, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
 // ---- small batches: ranking and offsets of routed pairs in one workgroup ----
 __global__ __launch_bounds__(kBlock) void group_small_kernel(int T, int E, int k, int tiles, FwdWork w,
-                                                             const int32_t* bits) {
+                                                             DevTable tab) {
     __shared__ int s_ids[kFusedMaxPairs];
     __shared__ int s_rank[kFusedMaxPairs];
     __shared__ int s_cnt[kMaxExperts];
-    const int my_bits = threadIdx.x < E ? bits[threadIdx.x] : 0;
+    const ExpertPage my = load_page(tab, E);
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) s_ids[p] = w.ids[p];
     __syncthreads();
     rank_small(T, E, k, s_ids, s_rank, s_cnt, w);
     __syncthreads();
-    finalize(T, E, k, w, my_bits, tiles, [&](int e) { return s_cnt[e]; },
+    finalize(T, E, k, w, my, tiles, [&](int e) { return s_cnt[e]; },
              [&](int p) { return s_rank[p]; }, [&](int p) { return s_ids[p]; });
 }
 
@@ -518,10 +531,10 @@ __global__ __launch_bounds__(256) void rank_kernel(int T, int k, int C, FwdWork 
 
 // One workgroup: per-expert counts and chunk prefixes, then offsets, the
 // active list and the token tiles.
-__global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, int tiles, FwdWork w, const int32_t* bits) {
+__global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, int tiles, FwdWork w, DevTable tab) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
-    const int my_bits = threadIdx.x < E ? bits[threadIdx.x] : 0;
+    const ExpertPage my = load_page(tab, E);
     for (int e = threadIdx.x; e < E; e += kBlock) {
         int run = 0;
         for (int c = 0; c < C; ++c) {
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(kBlock) void offsets_kernel(int E, int C, int tiles
         w.cnt[e] = run;
     }
     __syncthreads();
-    finalize_offsets(E, w, my_bits, tiles, [&](int e) { return s_cnt[e]; }, s_off);
+    finalize_offsets(E, w, my, tiles, [&](int e) { return s_cnt[e]; }, s_off);
 }
 
 // grid ceil(P / 256): position of every pair in expert-sorted order.
@@ -548,22 +561,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWo
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t) {
     const hipEvent_t none = nullptr;
     if (a.T <= (a.E <= kRowMaxExperts ? kFusedMaxTokensRow : kFusedMaxTokens) && a.T * a.k <= kFusedMaxPairs)
-        return launch_timed(route_fused_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, bits);
+        return launch_timed(route_fused_kernel, dim3(1), dim3(kBlock), 0, s, t.start, t.stop, a, w, tab);
     const int per_block = a.E <= kRowMaxExperts ? 16 : 4;
     hipError_t err = launch_timed(route_kernel, dim3((a.T + per_block - 1) / per_block), dim3(256), 0, s, t.start,
                                   none, a, w);
     if (err != hipSuccess) return err;
     if (a.T * a.k <= kFusedMaxPairs)
         return launch_timed(group_small_kernel, dim3(1), dim3(kBlock), 0, s, none, t.stop, a.T, a.E, a.k,
-                            a.tiles, w, bits);
+                            a.tiles, w, tab);
     const int C = (a.T + kRankChunk - 1) / kRankChunk;
     err = launch_timed(rank_kernel, dim3(a.E, C), dim3(256), 0, s, none, none, a.T, a.k, C, w);
     if (err != hipSuccess) return err;
-    err = launch_timed(offsets_kernel, dim3(1), dim3(kBlock), 0, s, none, none, a.E, C, a.tiles, w, bits);
+    err = launch_timed(offsets_kernel, dim3(1), dim3(kBlock), 0, s, none, none, a.E, C, a.tiles, w, tab);
     if (err != hipSuccess) return err;
     const int P = a.T * a.k;
     return launch_timed(scatter_kernel, dim3((P + 255) / 256), dim3(256), 0, s, none, t.stop, P, a.k, C, w);

@@ -125,6 +125,12 @@ __global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, F
         if (s_act[e]) st.last_use[e] = step;
     }
     for (int s = tid; s < S; s += kPlanThreads) st.expert_of[s] = s_exp[s];
+    // the streaming kernels' slot descriptors carry this pass's address
+    for (int i = tid; i < n_act; i += kPlanThreads) {
+        const int e = w.act[i];
+        const int s = s_slot[e];
+        w.slots[i].page = s >= 0 ? (uint64_t)(pool + (uint64_t)s * slot_bytes) : (uint64_t)(host + tab.off[e]);
+    }
     if (tid == 0) {
         st.step[0] = step;
         st.ncopy[0] = ncopy;

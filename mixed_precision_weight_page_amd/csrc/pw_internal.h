@@ -41,6 +41,17 @@ struct __attribute__((aligned(16))) TileDesc {
     int32_t e, first, cnt, off;
 };
 
+// One routed expert of the streaming kernels, in active-list order: its page
+// (offset into the pool, or with a host tier the page's address for this
+// pass), scale and bit-width, and its pair count and first sorted position.
+// The router writes it (the host tier's plan patches the page), so a
+// workgroup reads everything it needs before its first code load at once.
+struct __attribute__((aligned(16))) SlotDesc {
+    uint64_t page;
+    float scale;
+    int32_t e, bits, cnt, off, pad;
+};
+
 // Forward-pass scratch carved out of the bound workspace.
 struct FwdWork {
     int32_t* ids;      // [P] expert of pair p = t*k + j
@@ -53,6 +64,7 @@ struct FwdWork {
     int32_t* act;      // [E] experts with cnt > 0, ascending
     int32_t* n_act;    // [2] active experts; token tiles of the large-batch kernels
     TileDesc* tiles;   // [ceil(P / kGemmTokens) + E] token tiles in active-list order
+    SlotDesc* slots;   // [E] routed experts in active-list order
     int32_t* ccnt;     // [E, C] pairs of expert e among the tokens of chunk c (kRankChunk tokens)
     int32_t* cpre;     // [E, C] exclusive prefix of ccnt over the chunks
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
@@ -60,7 +72,7 @@ struct FwdWork {
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tiles, ccnt, cpre, H, O, xp, fwd_end;
+    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tiles, slots, ccnt, cpre, H, O, xp, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };
@@ -105,7 +117,7 @@ struct RouteArgs {
     int T, E, k, renorm;
     int tiles;   // also the large-batch kernels' token tiles (FwdWork::tiles)
 };
-hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const int32_t* bits, hipStream_t s,
+hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t = {});
 
 struct FfnPlan {

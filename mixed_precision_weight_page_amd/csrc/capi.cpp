@@ -181,7 +181,6 @@ FwdWork fwd_work(pw_ctx* c) {
     w.ids = reinterpret_cast<int32_t*>(b + c->lay.ids);
     w.g = reinterpret_cast<float*>(b + c->lay.g);
     w.rank = reinterpret_cast<int32_t*>(b + c->lay.rank);
-    w.pos = reinterpret_cast<int32_t*>(b + c->lay.pos);
     w.sorted = reinterpret_cast<int32_t*>(b + c->lay.sorted);
     w.cnt = reinterpret_cast<int32_t*>(b + c->lay.cnt);
     w.off = reinterpret_cast<int32_t*>(b + c->lay.off);
@@ -401,7 +400,6 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.ids = take(4 * P);
     L.g = take(4 * P);
     L.rank = take(4 * P);
-    L.pos = take(4 * P);
     L.sorted = take(4 * P);
     L.cnt = take(4 * (uint64_t)E);
     L.off = take(4 * (uint64_t)(E + 1));

@@ -254,6 +254,9 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
             if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
         }
         __syncthreads();
+        // the down product writes this lane's token row of O at its pair index
+        int my_pair = 0;
+        if constexpr (MODE == 1) my_pair = a.w.sorted[base + tb + min(r, nt - 1)];
         stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
         __syncthreads();
         f32x4 acc[NMAT];
@@ -346,7 +349,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
                 o.y = s * acc[0][1];
                 o.z = s * acc[0][2];
                 o.w = s * acc[0][3];
-                *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + pos) * a.d + orow) = o;
+                *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + my_pair) * a.d + orow) = o;
             }
         }
     }
@@ -382,10 +385,10 @@ hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer 
                         (int)p.lds, tiles, p.nsplit);
 }
 
-// y[t] = sum_j g[t,j] * (sum_s O[s][pos(t,j)]) in slot and split order;
-// grid (ceil(d/1024), T). The loads of up to 8 slots are issued before any
-// of them is used (a load per slot behind its position's load would expose
-// one memory round trip per slot); the sums keep the slot and split order.
+// y[t] = sum_j g[t,j] * (sum_s O[s][t k + j]) in slot and split order;
+// grid (ceil(d/1024), T). A token's k partial rows are consecutive in O;
+// the loads of up to 8 slots are issued before any of them is used, and
+// the sums keep the slot and split order.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int k, int P, int nsplit,
                                                            float* y) {
     const int t = blockIdx.y;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
             if (j0 + u < k) {
                 const int p = t * k + j0 + u;
                 gj[u] = w.g[p];
-                src[u] = w.O + (int64_t)w.pos[p] * d + col;
+                src[u] = w.O + (int64_t)p * d + col;
                 o[u] = *reinterpret_cast<const float4*>(src[u]);
             }
         }

@@ -218,7 +218,7 @@ __device__ __forceinline__ void sched_step() {
 
 template <int MODE, int B, int NA>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int base, int tt, int rt,
-                                          _Float16* smem, int* tok) {
+                                          _Float16* smem, int* tok, int* pair) {
     constexpr int NMAT = 2;   // stream pairs: W1 / W3 (MODE 0), two 32-row halves of W2 (MODE 1)
     constexpr int PD = gemm_depth<B>();
     constexpr int TB = 256 * B;                  // bytes of one 16-row x 128-code tile
@@ -248,6 +248,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
     if (tid < BN) {
         const int n = tid < nt ? tid : 0;   // past nt: repeat the first row, outputs dropped
         tok[tid] = MODE == 0 ? a.w.sorted[base + t0 + n] / a.k : base + t0 + n;
+        // the down product writes each token's rows of O at its pair index
+        if constexpr (MODE == 1) pair[tid] = a.w.sorted[base + t0 + n];
     }
     __syncthreads();
     const int my_tok = tok[tid >> 2];
@@ -404,7 +406,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
             constexpr int kChunks = tile_rows<1>() / 4;   // 16-byte chunks per token row
             for (int c = tid; c < rows * kChunks; c += kThreads) {
                 const int n = c / kChunks, ch = c % kChunks;
-                *reinterpret_cast<u32x4*>(a.w.O + (int64_t)(base + t0 + n0 + n) * a.d + rt * tile_rows<1>() +
+                *reinterpret_cast<u32x4*>(a.w.O + (int64_t)pair[n0 + n] * a.d + rt * tile_rows<1>() +
                                           4 * ch) = *reinterpret_cast<const u32x4*>(os + n * kOutStride + 4 * ch);
             }
         }
@@ -413,17 +415,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
 
 template <int MODE, int B>
 __device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, const TileDesc& td, int tt, int rt,
-                                            _Float16* smem, int* tok) {
-    if (na >= 4) gemm_tile<MODE, B, 4>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
-    else if (na == 3) gemm_tile<MODE, B, 3>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
-    else if (na == 2) gemm_tile<MODE, B, 2>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
-    else gemm_tile<MODE, B, 1>(a, td.e, td.cnt, td.off, tt, rt, smem, tok);
+                                            _Float16* smem, int* tok, int* pair) {
+    if (na >= 4) gemm_tile<MODE, B, 4>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
+    else if (na == 3) gemm_tile<MODE, B, 3>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
+    else if (na == 2) gemm_tile<MODE, B, 2>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
+    else gemm_tile<MODE, B, 1>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_tiles) {
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
     __shared__ int tok[BN];
+    __shared__ int pair[MODE == 1 ? BN : 1];
     // XCD swizzle: the eighth of this forward's tiles (the grid is sized for
     // the most a batch can have) that this workgroup's XCD walks, so the
     // XCDs get equal shares and the unused workgroups are spread over them
@@ -445,9 +448,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     // 16-token blocks holding real tokens (fewer than four only in an
     // expert's last token tile): the MFMAs of the empty ones are skipped
     const int nblk = (min(BN, td.cnt - tt * BN) + 15) >> 4;
-    if (b == 4) dispatch_na<MODE, 4>(nblk, a, td, tt, rt, smem, tok);
-    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, td, tt, rt, smem, tok);
-    else dispatch_na<MODE, 3>(nblk, a, td, tt, rt, smem, tok);
+    if (b == 4) dispatch_na<MODE, 4>(nblk, a, td, tt, rt, smem, tok, pair);
+    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, td, tt, rt, smem, tok, pair);
+    else dispatch_na<MODE, 3>(nblk, a, td, tt, rt, smem, tok, pair);
 }
 
 template <int MODE>

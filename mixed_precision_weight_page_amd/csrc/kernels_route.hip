@@ -386,9 +386,7 @@ __device__ __forceinline__ void finalize(int T, int E, int k, const FwdWork& w, 
     const int P = T * k;
     for (int p = threadIdx.x; p < P; p += kBlock) {
         const int e = id_of(p);
-        const int pos = s_off[e] + rank_of(p);
-        w.pos[p] = pos;
-        w.sorted[pos] = p;
+        w.sorted[s_off[e] + rank_of(p)] = p;
     }
 }
 
@@ -554,9 +552,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWo
     if (p >= P) return;
     const int e = w.ids[p];
     const int c = (p / k) / kRankChunk;
-    const int pos = w.off[e] + w.cpre[e * C + c] + w.rank[p];
-    w.pos[p] = pos;
-    w.sorted[pos] = p;
+    w.sorted[w.off[e] + w.cpre[e * C + c] + w.rank[p]] = p;
 }
 
 }  // namespace

@@ -57,7 +57,6 @@ struct FwdWork {
     int32_t* ids;      // [P] expert of pair p = t*k + j
     float* g;          // [P] routing weight
     int32_t* rank;     // [P] rank of the pair among its expert's pairs
-    int32_t* pos;      // [P] position of the pair in expert-sorted order
     int32_t* sorted;   // [P] pair at each sorted position
     int32_t* cnt;      // [E] tokens per expert
     int32_t* off;      // [E+1] exclusive prefix of cnt
@@ -68,11 +67,11 @@ struct FwdWork {
     int32_t* ccnt;     // [E, C] pairs of expert e among the tokens of chunk c (kRankChunk tokens)
     int32_t* cpre;     // [E, C] exclusive prefix of ccnt over the chunks
     _Float16* H;       // [P, F] SwiGLU output per sorted pair
-    float* O;          // [nsplit, P, d] down-projection partials per sorted pair (scaled by s_e)
+    float* O;          // [nsplit, P, d] down-projection partials per pair t k + j (scaled by s_e)
 };
 
 struct Layout {
-    uint64_t ids, g, rank, pos, sorted, cnt, off, act, n_act, tiles, slots, ccnt, cpre, H, O, xp, fwd_end;
+    uint64_t ids, g, rank, sorted, cnt, off, act, n_act, tiles, slots, ccnt, cpre, H, O, xp, fwd_end;
     uint64_t partial, stats_end;
     uint64_t total;
 };

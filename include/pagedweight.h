@@ -20,7 +20,8 @@
  *   - Device pointers are BORROWED: the caller (for example PyTorch) owns
  *     the memory and keeps it alive while the context uses it. Host
  *     pointers are read or written only during the call.
- *   - Layouts are row-major and contiguous.
+ *   - Tensor arguments are row-major and contiguous (the page layout is
+ *     described at pw_quantize_experts).
  *   - `stream` is a hipStream_t (NULL = the default stream). All device
  *     work is enqueued on it in call order; a later call on the same stream
  *     sees the results of an earlier one. Calls on different streams must be
@@ -112,8 +113,12 @@ pw_status pw_bind_workspace(pw_ctx* ctx, void* ws, uint64_t bytes);
  * masters into the pool and upload the page table. The first call after
  * pw_bind_masters measures max|w| per expert on the device and waits for
  * it (one stream synchronisation). Eq. 2; layout of a page: the W1 codes,
- * then W3, then W2, each row-major [out, in] as a little-endian
- * LSB-first bitstream of b-bit codes u = q + 2^(b-1). */
+ * then W3, then W2, each matrix [out, in] with every row a little-endian
+ * LSB-first bitstream of b-bit codes u = q + 2^(b-1), arranged in tiles of
+ * 16 rows x 128 codes in (row block, K step) order; inside a tile, lane
+ * l = 16 g + r of a 64-lane wave holds codes 32 g .. 32 g + 31 of row r
+ * (4 b bytes), cut into pieces of at most 16 bytes, and piece p of all 64
+ * lanes is stored together. Pages are 256-byte aligned. */
 pw_status pw_quantize_experts(pw_ctx* ctx, const uint8_t* bits, void* stream);
 
 /* Move the weight budget: solve Eq. 1 on the host for budget_bits B with

@@ -40,7 +40,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 500 untimed forwards (about 75 ms at 16 decode tokens, 0.5 s of prefill)
+    # bring the GPU to its steady clocks; after 5 the timed region still
+    # started below them (decode 97k against 109k tokens/s)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode_coarse",
                     choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "kvtrace", "swap", "tiny"])
     ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")

@@ -181,31 +181,40 @@ class Bench:
                     bytes_dn=tot_dn, mean_active=sum(n_act[i % nb] for i in range(steps)) / steps)
 
 
-def cpu_baseline(bench, T, log):
-    """Oracle forward (float64, from the fp32 masters) on one batch."""
+def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
+    """Oracle forward (float64, from the fp32 masters) on T-token batches of
+    the same layer, one after another until min_seconds of oracle time or
+    max_batches: each batch quantizes its routed experts and runs the
+    forward."""
     import torch
 
     from oracle import moe
     threads = min(16, os.cpu_count() or 1)
     torch.set_num_threads(threads)
-    x, lg = bench.batches(T, 1, seed=99)[0]
-    x, lg = x.cpu(), lg.cpu()
-    ids, _ = moe.route(lg, bench.wl.k)
-    experts = sorted(set(ids.flatten().tolist()))
-    t0 = time.time()
-    w = [m[experts].cpu() for m in bench.masters]   # only the routed experts
-    remap = {e: i for i, e in enumerate(experts)}
-    bits = bench.bits
-    getter = moe.quantized_experts(*w, [bits[e] for e in experts])
-    t_copy = time.time() - t0
-    t0 = time.time()
-    y = moe.forward(x, lg, bench.wl.k, lambda e: getter(remap[e]))
-    dt = time.time() - t0
-    log(f"oracle forward T={T}: {dt:.1f}s (+{t_copy:.1f}s host copy), {len(experts)} experts")
-    return {"value": T / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"one {T}-token batch of the same layer: quantize the {len(experts)} routed "
-                      f"experts from fp32 masters and run the float64 forward (host copy of the "
-                      f"masters excluded)"}, y
+    batches = bench.batches(T, max_batches, seed=99)
+    total, done, n_exp, t_copy, y0 = 0.0, 0, [], 0.0, None
+    for x, lg in batches:
+        x, lg = x.cpu(), lg.cpu()
+        ids, _ = moe.route(lg, bench.wl.k)
+        experts = sorted(set(ids.flatten().tolist()))
+        t0 = time.time()
+        w = [m[experts].cpu() for m in bench.masters]   # only the routed experts
+        t_copy += time.time() - t0
+        remap = {e: i for i, e in enumerate(experts)}
+        t0 = time.time()
+        getter = moe.quantized_experts(*w, [bench.bits[e] for e in experts])
+        y = moe.forward(x, lg, bench.wl.k, lambda e: getter(remap[e]))
+        total += time.time() - t0
+        done += 1
+        n_exp.append(len(experts))
+        y0 = y if y0 is None else y0
+        if total >= min_seconds:
+            break
+    log(f"oracle: {done} batches of {T} tokens in {total:.1f}s (+{t_copy:.1f}s host copy)")
+    return {"value": T * done / total, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{done} batch(es) of {T} tokens of the same layer, each quantizing its routed experts "
+                      f"({', '.join(map(str, n_exp))}) from fp32 masters and running the float64 forward "
+                      f"(host copies of the masters excluded)"}, y0
 
 
 def main():

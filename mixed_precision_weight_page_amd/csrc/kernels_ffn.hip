@@ -393,8 +393,8 @@ __device__ __forceinline__ float4 load_partial(const float* p) {
 
 // y[t] = sum_j g[t,j] * (sum_s O[s][t k + j]) in slot and split order;
 // grid (ceil(d/1024), T). A token's k partial rows are consecutive in O;
-// the loads of up to 8 slots are issued before any of them is used, and
-// the sums keep the slot and split order.
+// the loads of up to 8 slots (and of two further splits of each) are issued
+// before any of them is used, and the sums keep the slot and split order.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int k, int P, int nsplit,
                                                            float* y) {
     const int t = blockIdx.y;
@@ -414,13 +414,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
                 o[u] = load_partial(src[u]);
             }
         }
+        // the other K splits, two at a time: the loads of both splits for
+        // every slot are issued before any is added (one round trip per two
+        // splits, not one per slot and split); sums in split order
+        for (int sp = 1; sp < nsplit; sp += 2) {
+            const bool two = sp + 1 < nsplit;
+            float4 qa[8], qb[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < k) {
+                    qa[u] = load_partial(src[u] + (int64_t)sp * P * d);
+                    if (two) qb[u] = load_partial(src[u] + (int64_t)(sp + 1) * P * d);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < k) {
+                    o[u].x += qa[u].x; o[u].y += qa[u].y; o[u].z += qa[u].z; o[u].w += qa[u].w;
+                    if (two) {
+                        o[u].x += qb[u].x; o[u].y += qb[u].y; o[u].z += qb[u].z; o[u].w += qb[u].w;
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (j0 + u < k) {
-                for (int sp = 1; sp < nsplit; ++sp) {
-                    const float4 q = load_partial(src[u] + (int64_t)sp * P * d);
-                    o[u].x += q.x; o[u].y += q.y; o[u].z += q.z; o[u].w += q.w;
-                }
                 acc.x = fmaf(gj[u], o[u].x, acc.x);
                 acc.y = fmaf(gj[u], o[u].y, acc.y);
                 acc.z = fmaf(gj[u], o[u].z, acc.z);

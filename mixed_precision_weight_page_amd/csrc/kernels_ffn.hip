@@ -242,13 +242,19 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         if (nt * (nsteps * kStep + 8) * 2 > lds_bytes)
             spc = ((lds_bytes / (2 * nt) - 8) / (kStep * PD)) * PD;
         const int stride = spc * kStep + 8;
-        // first codes in flight before the token ids are read and the token
-        // rows staged, so those round trips overlap their latency
+        // the first PD steps of codes: the down product issues them before
+        // its token rows are staged (their round trips overlap), gate/up
+        // after (its token-id and token-row loads, which the first step
+        // waits for, are then not queued behind the codes): measured best
+        // for each
         Codes<B> buf[NMAT][PD];
+        auto issue_codes = [&]() {
 #pragma unroll
-        for (int j = 0; j < PD; ++j)
+            for (int j = 0; j < PD; ++j)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
+                for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
+        };
+        if constexpr (MODE == 1) issue_codes();
         __syncthreads();   // previous token block done with tok and xs
         if constexpr (MODE == 0) {
             if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
@@ -258,6 +264,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         int my_pair = 0;
         if constexpr (MODE == 1) my_pair = a.w.sorted[base + tb + min(r, nt - 1)];
         stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
+        if constexpr (MODE == 0) issue_codes();
         __syncthreads();
         f32x4 acc[NMAT];
 #pragma unroll

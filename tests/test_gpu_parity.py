@@ -369,6 +369,23 @@ def test_large_batch_matrix_core_path(T):
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
 
 
+@pytest.mark.parametrize("F", [384, 640, 896, 1024])
+def test_down_splits_summed_in_order(F):
+    """Small batches split the down product along d_ff (here into 3, 5, 7
+    and 8 parts for one and three tokens); the combine sums every split of
+    every slot, two splits per round of loads, odd counts included."""
+    wl = synth.WORKLOADS["tiny"].scaled(name=f"splits_F{F}", E=4, d=256, F=F, k=2, T=3,
+                                        bits=(8, 4, 3, 4))
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    for T in (1, 3):
+        x, logits = synth.tokens(wl, T=T)
+        log(f"splits F={F}: forward T={T}")
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"splits F={F} T={T}")
+
+
 EXTREME = [
     # one expert, top-1, the smallest rows (one 128-code step, two 64-row tiles)
     (synth.WORKLOADS["tiny"].scaled(name="one", E=1, d=128, F=128, k=1, T=5, bits=(3,)), (5, 1)),

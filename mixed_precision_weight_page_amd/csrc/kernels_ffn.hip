@@ -257,7 +257,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         if constexpr (MODE == 1) issue_codes();
         __syncthreads();   // previous token block done with tok and xs
         if constexpr (MODE == 0) {
-            if (threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
+            if ((int)threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
         }
         __syncthreads();
         // the down product writes this lane's token row of O at its pair index

@@ -27,7 +27,6 @@
 namespace pw {
 namespace {
 
-constexpr int kMaxPerLane = kMaxExperts / 64;  // 16 logits per lane
 constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / 64;
 constexpr int kRowMaxExperts = 256;             // 16 lanes per token up to this many experts
@@ -112,18 +111,6 @@ constexpr int kQuadXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& be) {
-    const float ov = dpp_f<CTRL>(bv);
-    const int oe = dpp_i<CTRL>(be);
-    if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
-}
-__device__ __forceinline__ void row_argmax(float& bv, int& be) {
-    argmax_step<kQuadXor1>(bv, be);
-    argmax_step<kQuadXor2>(bv, be);
-    argmax_step<kRowHalfMirror>(bv, be);
-    argmax_step<kRowMirror>(bv, be);
-}
 __device__ __forceinline__ float row_sum(float x) {
     x += dpp_f<kQuadXor1>(x);
     x += dpp_f<kQuadXor2>(x);

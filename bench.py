@@ -328,6 +328,41 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def cpu_requant_baseline(masters, wl, p, L, log, min_seconds=10.0):
+    """The oracle's re-precision on the host: Eq. 1 solved for the first
+    budget of the schedule (the library's measured loss table as input),
+    then experts re-quantized from the fp16 masters into pages (max |w|,
+    scale, codes, packed tiled page), alternating 8/4/3 bits, until
+    min_seconds; GB/s counts master bytes read plus page bytes written, as
+    requant_GBps does."""
+    import torch
+
+    from oracle import alloc, quant
+    threads = min(16, os.cpu_count() or 1)
+    torch.set_num_threads(threads)
+    W = [wl.W_e] * wl.E
+    t0 = time.time()
+    alloc.solve(list(p), L.tolist(), W, wl.budget_bits(wl.schedule[0]))
+    t_solve = time.time() - t0
+    total, nbytes, done = 0.0, 0.0, 0
+    for e in range(wl.E):
+        w = [m[e].cpu() for m in masters]                # fp16, not timed
+        b = (8, 4, 3)[e % 3]
+        t0 = time.time()
+        s = quant.scale(quant.expert_absmax(w), b)
+        quant.expert_page(w[0], w[1], w[2], b, s)
+        total += time.time() - t0
+        nbytes += wl.W_e * (2 + b / 8)
+        done += 1
+        if total >= min_seconds:
+            break
+    log(f"oracle re-precision: solve {t_solve:.2f}s, {done} experts in {total:.1f}s")
+    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"Eq. 1 for {wl.E} experts in {t_solve * 1e3:.0f} ms, then {done} experts re-quantized "
+                      f"from fp16 masters into pages at 8/4/3 bits (master bytes read + page bytes written "
+                      f"per second, as requant_GBps)"}
+
+
 def bench_dynamic(args, wl, log):
     """40 decode steps of 64 tokens; the budget moves every 8 steps through
     avg 8, 6, 4, 3.5, 5 bits (re-quantization from the fp16 masters between
@@ -373,6 +408,8 @@ def bench_dynamic(args, wl, log):
                                   "masters, budget avg 8->6->4->3.5->5 bits every 8 steps"},
            "requant_GBps": req_bytes / t_req / 1e9 if t_req else None,
            "requant_s_total": t_req}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_requant_baseline(masters, wl, p, layer.get_loss_table(), log)
     print(json.dumps(out), flush=True)
 
 

@@ -181,6 +181,17 @@ class Bench:
                     bytes_dn=tot_dn, mean_active=sum(n_act[i % nb] for i in range(steps)) / steps)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the CPU baseline's record."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
     """Oracle forward (float64, from the fp32 masters) on T-token batches of
     the same layer, one after another until min_seconds of oracle time or
@@ -214,7 +225,7 @@ def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
     return {"value": T * done / total, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"{done} batch(es) of {T} tokens of the same layer, each quantizing its routed experts "
                       f"({', '.join(map(str, n_exp))}) from fp32 masters and running the float64 forward "
-                      f"(host copies of the masters excluded)"}, y0
+                      f"(host copies of the masters excluded); {cpu_model()}"}, y0
 
 
 def main():
@@ -360,7 +371,7 @@ def cpu_requant_baseline(masters, wl, p, L, log, min_seconds=10.0):
     return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": f"Eq. 1 for {wl.E} experts in {t_solve * 1e3:.0f} ms, then {done} experts re-quantized "
                       f"from fp16 masters into pages at 8/4/3 bits (master bytes read + page bytes written "
-                      f"per second, as requant_GBps)"}
+                      f"per second, as requant_GBps); {cpu_model()}"}
 
 
 def bench_dynamic(args, wl, log):

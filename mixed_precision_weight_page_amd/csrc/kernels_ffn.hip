@@ -488,7 +488,10 @@ int down_splits(int F, int d, int max_act, int max_splits) {
     for (int n = 1; n <= nblk && n <= max_splits; ++n) {
         if (nblk % n) continue;
         best = n;
-        if (per_split * n >= kFillWorkgroups) break;
+        // with at most two routed experts (one token) half the workgroups:
+        // fewer partial outputs for the combine, and each workgroup's start-up
+        // serves twice the bytes (2% faster at one token, measured)
+        if (per_split * n >= (max_act <= 2 ? kFillWorkgroups / 2 : kFillWorkgroups)) break;
     }
     return best;
 }

@@ -37,6 +37,8 @@ struct pw_ctx {
     uint64_t pool_cap = 0;
     uint8_t* ws = nullptr;
     uint64_t ws_bytes = 0;
+    int dg_parity = 0;    // counter set of the streaming kernels' grouping used by the next forward
+    bool dg_clean = false;   // both counter sets cleared since the workspace was bound
 
     // host tier: with pinned host memory bound, the pages live there and the
     // pool is a cache of page slots (residency state on the device)
@@ -187,9 +189,22 @@ FwdWork fwd_work(pw_ctx* c) {
     w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
     w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
     w.tiles = reinterpret_cast<TileDesc*>(b + c->lay.tiles);
-    w.slots = reinterpret_cast<SlotDesc*>(b + c->lay.slots);
+    // the two counter sets: cnt [E], act [E], n_act, each set 256-byte aligned
+    auto set = [&](int i) {
+        uint8_t* q = b + c->lay.dg + (uint64_t)i * (c->lay.dg_bytes / 2);
+        DecodeGroup g;
+        g.cnt = reinterpret_cast<int32_t*>(q);
+        g.act = g.cnt + c->E;
+        g.n_act = g.act + c->E;
+        g.list = reinterpret_cast<int32_t*>(b + c->lay.list);
+        return g;
+    };
+    w.dg = set(c->dg_parity);
+    w.dg_next = set(1 - c->dg_parity);
+    w.tcap = std::max(c->desc.max_tokens, 16);
     w.ccnt = reinterpret_cast<int32_t*>(b + c->lay.ccnt);
     w.cpre = reinterpret_cast<int32_t*>(b + c->lay.cpre);
+    w.xst = reinterpret_cast<XStat*>(b + c->lay.xst);
     w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
     w.O = reinterpret_cast<float*>(b + c->lay.O);
     return w;
@@ -406,19 +421,25 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.act = take(4 * (uint64_t)E);
     L.n_act = take(8);
     L.tiles = take(sizeof(TileDesc) * ((P + kGemmTokens - 1) / kGemmTokens + (uint64_t)E));
-    L.slots = take(sizeof(SlotDesc) * (uint64_t)E);
     const uint64_t chunks = ((uint64_t)max_tokens + kRankChunk - 1) / kRankChunk;
     L.ccnt = take(4 * (uint64_t)E * chunks);
     L.cpre = take(4 * (uint64_t)E * chunks);
+    L.xst = take(sizeof(XStat) * (uint64_t)max_tokens);
     L.H = take(2 * P * (uint64_t)F);
     L.O = take(4 * (uint64_t)nsplit * P * (uint64_t)d);
     L.xp = take(2 * 3 * (uint64_t)max_tokens * (uint64_t)d);
+    // pair lists of the streaming kernels: at least 16 entries per expert
+    L.list = take(4 * (uint64_t)E * (uint64_t)std::max(max_tokens, 16));
     L.fwd_end = at;
     // the loss pass reuses the forward scratch (calls on one stream are ordered)
     const uint64_t nblk = 3 * (uint64_t)F * d / kStatChunk;
     L.partial = scratch;
     L.stats_end = scratch + align_up(8 * 3 * nblk * (uint64_t)E, kAlign);
-    L.total = std::max(L.fwd_end, L.stats_end);
+    // the grouping counters keep their values between forwards: after
+    // everything the statistics pass may overwrite
+    L.dg_bytes = 2 * align_up(4 * (2 * (uint64_t)E + 1), kAlign);
+    L.dg = std::max(L.fwd_end, L.stats_end);
+    L.total = L.dg + L.dg_bytes;
     return L;
 }
 }  // namespace pw
@@ -462,8 +483,9 @@ pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out) {
     c->We = 3 * (uint64_t)c->M;
     // partial-output buffers for the down product's K splits: room for the
     // splits a single routed expert would want (the most any forward takes),
-    // unless the batch is large (then the buffer of T k d floats is big
-    // enough on its own and small batches split within it)
+    // unless the batch is large (then the buffer of max_tokens k d floats is
+    // big enough on its own: a forward's split stride is its own pair count,
+    // so small batches split within it)
     const int64_t max_pairs = (int64_t)d.max_tokens * d.top_k;
     c->nsplit = max_pairs > 2048 ? 1 : down_splits(c->F, c->d, 1, 1 << 30);
     c->lay = workspace_layout(c->E, c->d, c->F, c->k, d.max_tokens, c->nsplit);
@@ -579,6 +601,8 @@ pw_status pw_bind_workspace(pw_ctx* c, void* ws, uint64_t bytes) {
                     (unsigned long long)bytes, (unsigned long long)c->lay.total);
     c->ws = static_cast<uint8_t*>(ws);
     c->ws_bytes = bytes;
+    c->dg_parity = 0;
+    c->dg_clean = false;   // cleared by the first streaming forward's stream
     return PW_OK;
 }
 
@@ -659,6 +683,40 @@ pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_
     return PW_OK;
 }
 
+// Whether a batch of T tokens takes the matrix-core kernels: many tokens per
+// routed expert (weights read once per 64 tokens); else the streaming kernels
+// (weights read once).
+static bool dense_path(const pw_ctx* c, int32_t T) {
+    const int64_t pairs = (int64_t)T * c->k;
+    const int64_t max_act = std::min<int64_t>(c->E, pairs);
+    return gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act;
+}
+
+// Router and grouping for the path of the batch. The streaming kernels'
+// router also takes the token statistics (x may be NULL: none) and uses the
+// current counter set, so the next forward uses the other one. Returns the
+// per-expert counts.
+static pw_status route_batch(pw_ctx* c, const FwdWork& w, const float* logits, const void* x, int32_t T,
+                             bool dense, hipStream_t s, KTimer t, const int32_t** counts) {
+    RouteArgs ra{logits, static_cast<const uint16_t*>(x), c->d, T, c->E, c->k, c->desc.renorm, 1};
+    if (dense) {
+        ra.x = nullptr;   // prep_x takes the statistics on this path
+        HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s, t));
+        *counts = w.cnt;
+    } else {
+        if (!c->dg_clean) {
+            // both counter sets start at zero (a kernel, not a memset: the
+            // stream may be under graph capture)
+            HIP_TRY(c, launch_zero_i32(reinterpret_cast<int32_t*>(c->ws + c->lay.dg), c->lay.dg_bytes / 4, s));
+            c->dg_clean = true;
+        }
+        HIP_TRY(c, launch_route_decode(ra, w, s, t));
+        c->dg_parity ^= 1;
+        *counts = w.dg.cnt;
+    }
+    return PW_OK;
+}
+
 static pw_status forward_checks(pw_ctx* c, const void* logits, int32_t T) {
     if (T < 0 || T > c->desc.max_tokens)
         return fail(c, PW_ERR_INVALID_ARG, "T = %d outside [0, %d]", T, c->desc.max_tokens);
@@ -677,12 +735,12 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const FwdWork w = fwd_work(c);
-    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, 1};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s));
+    const int32_t* cnt = nullptr;
+    if ((st = route_batch(c, w, logits, nullptr, T, dense_path(c, T), s, KTimer{}, &cnt)) != PW_OK) return st;
     const size_t P = (size_t)T * c->k;
     HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(c, hipMemcpyAsync(g, w.g, P * 4, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(c, hipMemcpyAsync(counts, w.cnt, (size_t)c->E * 4, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(c, hipMemcpyAsync(counts, cnt, (size_t)c->E * 4, hipMemcpyDeviceToDevice, s));
     return PW_OK;
 }
 
@@ -711,11 +769,9 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     }
     const int64_t pairs = (int64_t)T * c->k;
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
-    // many tokens per expert: dense tiles on the matrix cores (weights read
-    // once per 64 tokens); few: the streaming kernels (weights read once)
-    const bool dense = gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act;
-    RouteArgs ra{logits, T, c->E, c->k, c->desc.renorm, dense ? 1 : 0};
-    HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s, tm[0]));
+    const bool dense = dense_path(c, T);
+    const int32_t* cnt = nullptr;
+    if ((st = route_batch(c, w, logits, x, T, dense, s, tm[0], &cnt)) != PW_OK) return st;
     // pages: pool + offset, or with a host tier the addresses of this pass
     // (slot or host tier) after the missing pages are copied in
     const uint8_t* base = c->pool;
@@ -723,12 +779,15 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     if (swap_mode(c)) {
         const SwapState st = swap_state(c);
         const int S = n_slots(c);
-        HIP_TRY(c, launch_swap_in(st, w, tab, c->E, S, std::min(S, max_act), c->We, c->pool, c->host,
-                                  slot_bytes(c), s));
+        HIP_TRY(c, launch_swap_in(st, dense ? w.act : w.dg.act, dense ? w.n_act : w.dg.n_act, tab, c->E, S,
+                                  std::min(S, max_act), c->We, c->pool, c->host, slot_bytes(c), s));
         tab.off = st.addr;
         base = nullptr;
     }
-    const int P = c->desc.max_tokens * c->k;
+    // partial outputs of the down product: O[split][pair][d] with this
+    // batch's pair count as the split stride, so a context sized for large
+    // batches splits small ones as far as its buffer allows
+    const int P = (int)pairs;
     if (dense) {
         GemmArgs ga;
         ga.pool = base;
@@ -762,7 +821,7 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         fa.P = P;
         // K splits of the down product for this batch, within the buffer
         const int64_t cap_pairs = (int64_t)c->nsplit * c->desc.max_tokens * c->k;
-        const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / P, 1 << 30));
+        const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / pairs, 1 << 30));
         HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
         HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, nsplit), s, tm[2]));
         HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, nsplit, y, s, tm[3]));

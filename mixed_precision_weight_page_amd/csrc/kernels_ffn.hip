@@ -14,6 +14,10 @@
 // LDS as fp16, permuted so that each lane's 8 K-slots line up with the
 // order in which its codes unpack. The per-expert scale is applied in the
 // epilogue, so every product is exact and only fp32 accumulation rounds.
+// Token rows enter as x 2^-e_t and the SwiGLU rows are stored as h 2^-m
+// (exact powers of two, xscale.h), so any finite bf16 input and any h
+// representable in fp32 fit the fp16 operands; the epilogues multiply the
+// powers back.
 //
 // Why matrix cores for a memory-bound skinny product: with T_e tokens per
 // expert a VALU dot product costs T_e/2 instructions per weight (packed
@@ -27,6 +31,7 @@
 
 #include "dequant.h"
 #include "pw_internal.h"
+#include "xscale.h"
 
 namespace pw {
 namespace {
@@ -78,14 +83,14 @@ __device__ __forceinline__ Codes<B> load_codes(const uint8_t* p) {
 using dq::half2_t;
 using dq::perm_slot;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 // Stage K-chunk [k0, k0 + kc) of nt token rows into LDS as permuted fp16.
-// MODE 0 reads bf16 activations of the tokens in tok[]; MODE 1 reads the
-// fp16 SwiGLU rows base.. of H.
+// MODE 0 reads bf16 activations of the tokens in tok[], each row scaled by
+// its token's 2^-e; MODE 1 reads the (already scaled) fp16 SwiGLU rows of
+// the pairs in prs[] from H.
 template <int MODE, int B>
 __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a,
-                                      const int* tok, int hrow0, int nt, int k0, int kc) {
+                                      const int* tok, const int* prs, int nt, int k0, int kc) {
     if constexpr (B == 3) {
         // the 3-bit order permutes across all 32 codes of a run
         const int ngrp = kc / 32;
@@ -94,18 +99,19 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
             _Float16 v[32];
             if constexpr (MODE == 0) {
                 const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 32 * grp);
+                const int e = a.w.xst[tok[n]].e;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint4 u = src[q];
                     const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        v[8 * q + 2 * h] = (_Float16)bf16_to_f32((uint16_t)(ww[h] & 0xffffu));
-                        v[8 * q + 2 * h + 1] = (_Float16)bf16_to_f32((uint16_t)(ww[h] >> 16));
+                        v[8 * q + 2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
+                        v[8 * q + 2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
                     }
                 }
             } else {
-                const uint4* src = reinterpret_cast<const uint4*>(a.w.H + (int64_t)(hrow0 + n) * a.F + k0 + 32 * grp);
+                const uint4* src = reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 32 * grp);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     union {
@@ -136,18 +142,19 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
             _Float16 v[8];
             if constexpr (MODE == 0) {
                 const uint4 u = *reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 8 * ch);
+                const int e = a.w.xst[tok[n]].e;
                 const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    v[2 * h] = (_Float16)bf16_to_f32((uint16_t)(ww[h] & 0xffffu));
-                    v[2 * h + 1] = (_Float16)bf16_to_f32((uint16_t)(ww[h] >> 16));
+                    v[2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
+                    v[2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
                 }
             } else {
                 union {
                     uint4 u;
                     _Float16 h[8];
                 } t;
-                t.u = *reinterpret_cast<const uint4*>(a.w.H + (int64_t)(hrow0 + n) * a.F + k0 + 8 * ch);
+                t.u = *reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 8 * ch);
 #pragma unroll
                 for (int h = 0; h < 8; ++h) v[h] = t.h[h];
             }
@@ -203,17 +210,20 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
 // of them. Codes are prefetched PD steps ahead in a register ring; the main
 // loop issues its loads unconditionally so the ring stays full, and LDS
 // chunks of the token rows are staged before the first load when K fits.
-// The expert's page-table entry and token range, read by the kernel in one
-// round of independent loads before its first code load.
+// The expert's page-table entry, pair count and pair list, read by the
+// kernel in one round of independent loads before its first code load
+// (with the first 16 entries of the list: p0 is this thread's).
 struct ExpertRef {
     const uint8_t* page;
     float s;
-    int Te, base;
+    int Te;
+    const int32_t* list;
+    int p0;
 };
 
 template <int MODE, int B>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const ExpertRef& ex, int rt, int sp,
-                                         int ks0, int nsteps, _Float16* xs, int* tok) {
+                                         int ks0, int nsteps, _Float16* xs, int* tok, int* prs) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
     constexpr int PD = prefetch_depth<B>();
     constexpr int SB = 16 * kStep * B / 8;   // bytes of one tile: 16 rows x 128 codes
@@ -222,7 +232,6 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
     const uint8_t* page = ex.page;
     const float s = ex.s;
     const int Te = ex.Te;
-    const int base = ex.base;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
@@ -255,15 +264,20 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
                 for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
         };
         if constexpr (MODE == 1) issue_codes();
-        __syncthreads();   // previous token block done with tok and xs
-        if constexpr (MODE == 0) {
-            if ((int)threadIdx.x < nt) tok[threadIdx.x] = a.w.sorted[base + tb + threadIdx.x] / a.k;
+        // this block's pairs (the first block's came with the expert's entry)
+        const int p = tb == 0 ? ex.p0 : ((int)threadIdx.x < nt ? ex.list[tb + threadIdx.x] : 0);
+        __syncthreads();   // previous token block done with tok, prs and xs
+        if ((int)threadIdx.x < nt) {
+            prs[threadIdx.x] = p;
+            tok[threadIdx.x] = p / a.k;
         }
         __syncthreads();
-        // the down product writes this lane's token row of O at its pair index
-        int my_pair = 0;
-        if constexpr (MODE == 1) my_pair = a.w.sorted[base + tb + min(r, nt - 1)];
-        stage<MODE, B>(xs, stride, a, tok, base + tb, nt, ks0 * kStep, min(spc, nsteps) * kStep);
+        // this lane's pair (its row of H, or of O for the down product)
+        const int my_pair = prs[min(r, nt - 1)];
+        stage<MODE, B>(xs, stride, a, tok, prs, nt, ks0 * kStep, min(spc, nsteps) * kStep);
+        // the statistics of this lane's token, for the epilogue (issued after
+        // the staging loads, which the barrier below waits for)
+        const XStat my_xs = a.w.xst[my_pair / a.k];
         if constexpr (MODE == 0) issue_codes();
         __syncthreads();
         f32x4 acc[NMAT];
@@ -275,7 +289,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         for (; s0 + 2 * PD <= nsteps; s0 += PD) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
@@ -299,7 +313,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         if (nsteps - s0 > PD) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
@@ -319,7 +333,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         if (s0 < nsteps) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, base + tb, nt, (ks0 + s0) * kStep,
+                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
@@ -336,51 +350,54 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         }
         // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n
         if (r < nt) {
-            const int pos = base + tb + r;
             const int orow = row0 + 4 * g;
             if constexpr (MODE == 0) {
                 union {
                     uint2 u;
                     _Float16 h[4];
                 } hv;
+                const xsc::GateUpScale gs = xsc::gate_up_scale(s, B, my_xs);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float av = s * acc[0][v];
-                    const float cv = s * acc[1][v];
-                    hv.h[v] = (_Float16)(av / (1.0f + expf(-av)) * cv);
-                }
-                *reinterpret_cast<uint2*>(a.w.H + (int64_t)pos * a.F + orow) = hv.u;
+                for (int v = 0; v < 4; ++v) hv.h[v] = (_Float16)xsc::swiglu_scaled(acc[0][v], acc[1][v], gs);
+                *reinterpret_cast<uint2*>(a.w.H + (int64_t)my_pair * a.F + orow) = hv.u;
             } else {
+                const int m = xsc::h_exponent(s, B, my_xs);
                 float4 o;
-                o.x = s * acc[0][0];
-                o.y = s * acc[0][1];
-                o.z = s * acc[0][2];
-                o.w = s * acc[0][3];
+                o.x = ldexpf(s * acc[0][0], m);
+                o.y = ldexpf(s * acc[0][1], m);
+                o.z = ldexpf(s * acc[0][2], m);
+                o.w = ldexpf(s * acc[0][3], m);
                 *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + my_pair) * a.d + orow) = o;
             }
         }
     }
 }
 
-// grid: (active expert, 64-row tile, K split) flattened; experts beyond the
-// device-side active count exit at once.
+// grid: (routed expert slot, 64-row tile, K split) flattened; slots beyond
+// the device-side routed count exit at once. The slot's expert comes from
+// the router's active list (arrival order); its page-table entry, pair count
+// and first 16 pairs are then read in one round of independent loads (the
+// pair list has room for at least 16 entries).
 template <int MODE>
 __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-    __shared__ int tok[16];
+    __shared__ int tok[16];   // token of each pair of the current block
+    __shared__ int prs[16];   // the pairs t k + j of the current block
     const int per_expert = tiles * nsplit;
     const int ai = blockIdx.x / per_expert;
-    const SlotDesc sd = a.w.slots[ai];   // stale past the active count, not used then
-    if (ai >= a.w.n_act[0]) return;
+    const DecodeGroup& dg = a.w.dg;
+    const int e = dg.act[ai];   // stale past the routed count, not used then
+    if (ai >= dg.n_act[0]) return;
     const int rem = blockIdx.x - ai * per_expert;
     const int rt = rem / nsplit, sp = rem - rt * nsplit;
-    const int b = sd.bits;
-    const ExpertRef ex{a.pool + sd.page, sd.scale, sd.cnt, sd.off};
+    const int32_t* list = dg.list + (int64_t)e * a.w.tcap;
+    const int b = a.tab.bits[e];
+    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15]};
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
-    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
-    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
-    else ffn_tile<MODE, 3>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok);
+    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+    else ffn_tile<MODE, 3>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
 }
 
 template <int MODE>

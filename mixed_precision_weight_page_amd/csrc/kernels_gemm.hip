@@ -16,7 +16,9 @@
 // in registers; each lane's MFMA operand is one 16-byte LDS read, and the
 // next K group's operands are read while the current ones are in use.
 // Per step and wave: 4 K groups x 4 code streams x 4 token blocks of
-// v_mfma_f32_16x16x32_f16, fp32 accumulate.
+// v_mfma_f32_16x16x32_f16, fp32 accumulate. Token rows are x 2^-e_t and
+// the SwiGLU rows h 2^-m (exact powers of two, xscale.h), so every finite
+// bf16 input and every h representable in fp32 fits the fp16 operands.
 //
 // Tile order: expert (in the active list, 8-bit first), row tile, token
 // tile; with N tiles in this forward, workgroup b runs tile
@@ -31,6 +33,7 @@
 
 #include "dequant.h"
 #include "pw_internal.h"
+#include "xscale.h"
 
 namespace pw {
 namespace {
@@ -93,28 +96,18 @@ __device__ __forceinline__ int slot_of(int c) {
     return slot;
 }
 
-// 32 consecutive activations (bf16 when SRC_BF16, else fp16) as fp16 in the
+// 32 consecutive bf16 activations scaled by 2^-e (xscale.h) as fp16 in the
 // K-slot order of B-bit codes.
-template <bool SRC_BF16, int B>
-__device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4]) {
+template <int B>
+__device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4], int e) {
     _Float16 v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t ww[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            if constexpr (SRC_BF16) {
-                v[8 * q + 2 * h] = (_Float16)__uint_as_float((ww[h] & 0xffffu) << 16);
-                v[8 * q + 2 * h + 1] = (_Float16)__uint_as_float(ww[h] & 0xffff0000u);
-            } else {
-                union {
-                    uint32_t u;
-                    _Float16 f[2];
-                } t;
-                t.u = ww[h];
-                v[8 * q + 2 * h] = t.f[0];
-                v[8 * q + 2 * h + 1] = t.f[1];
-            }
+            v[8 * q + 2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
+            v[8 * q + 2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
         }
     }
     union {
@@ -127,29 +120,35 @@ __device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4]) {
     for (int q = 0; q < 4; ++q) out[q] = o.u[q];
 }
 
-// Token rows for the gate/up tiles, once per forward: xp[i][t] = x[t] as
-// fp16 in the K order of the codes of bit-width kBits[i], for each
-// bit-width some expert uses (bit i of mask). One thread per 32-activation
-// group of a token: the group is read once and written to every plane in
-// use. grid ceil(T d / 32 / 256).
+// Token rows for the gate/up tiles, once per forward. One wave per token:
+// the token's statistics (xscale.h) into xst[t], then xp[i][t] = x[t] 2^-e
+// as fp16 in the K order of the codes of bit-width kBits[i], for each
+// bit-width some expert uses (bit i of mask). Lane l handles the
+// 32-activation groups l, l + 64, ..., read once more (from the cache) after
+// the statistics and written to every plane in use. grid ceil(T / 4).
 __global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int T, int d, int mask,
-                                                          _Float16* xp, int64_t plane) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int gpr = d / 32;
-    if (idx >= (int64_t)T * gpr) return;
-    const int64_t off = idx * 32;   // t * d + 32 grp
-    const uint4* src = reinterpret_cast<const uint4*>(x + off);
-    const uint4 in[4] = {src[0], src[1], src[2], src[3]};
+                                                          _Float16* xp, int64_t plane, XStat* xst) {
+    const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* row = x + (int64_t)t * d;
+    const XStat st = xsc::row_stat(row, d);
+    if (lane == 0) xst[t] = st;
+    for (int grp = lane; grp < d / 32; grp += 64) {
+        const int64_t off = (int64_t)t * d + 32 * grp;
+        const uint4* src = reinterpret_cast<const uint4*>(x + off);
+        const uint4 in[4] = {src[0], src[1], src[2], src[3]};
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        if (!((mask >> i) & 1)) continue;
-        uint4 o[4];
-        if (i == 0) permute32<true, 3>(in, o);
-        else if (i == 1) permute32<true, 4>(in, o);
-        else permute32<true, 8>(in, o);
-        uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + off);
+        for (int i = 0; i < 3; ++i) {
+            if (!((mask >> i) & 1)) continue;
+            uint4 o[4];
+            if (i == 0) permute32<3>(in, o, st.e);
+            else if (i == 1) permute32<4>(in, o, st.e);
+            else permute32<8>(in, o, st.e);
+            uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + off);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = o[q];
+            for (int q = 0; q < 4; ++q) dst[q] = o[q];
+        }
     }
 }
 
@@ -216,9 +215,16 @@ __device__ __forceinline__ void sched_step() {
     }
 }
 
+// Per-token scaling of the epilogue (xscale.h): the gate/up factors, or the
+// exponent of the token's stored SwiGLU row for the down product.
+struct TokScale {
+    xsc::GateUpScale gu;
+    int m;
+};
+
 template <int MODE, int B, int NA>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int base, int tt, int rt,
-                                          _Float16* smem, int* tok, int* pair) {
+                                          _Float16* smem, int* tok, int* pair, TokScale* tsc) {
     constexpr int NMAT = 2;   // stream pairs: W1 / W3 (MODE 0), two 32-row halves of W2 (MODE 1)
     constexpr int PD = gemm_depth<B>();
     constexpr int TB = 256 * B;                  // bytes of one 16-row x 128-code tile
@@ -245,11 +251,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
             ap[m][blk] = page + (MODE == 0 ? m : 2) * mat_bytes + (int64_t)rb * S * TB + loff;
         }
 
+    // the token statistics are loaded here and used after the loop
+    XStat my_xs{0.0f, 0};
     if (tid < BN) {
         const int n = tid < nt ? tid : 0;   // past nt: repeat the first row, outputs dropped
-        tok[tid] = MODE == 0 ? a.w.sorted[base + t0 + n] / a.k : base + t0 + n;
+        const int p = a.w.sorted[base + t0 + n];
+        tok[tid] = MODE == 0 ? p / a.k : base + t0 + n;
         // the down product writes each token's rows of O at its pair index
-        if constexpr (MODE == 1) pair[tid] = a.w.sorted[base + t0 + n];
+        if constexpr (MODE == 1) pair[tid] = p;
+        my_xs = a.w.xst[p / a.k];
     }
     __syncthreads();
     const int my_tok = tok[tid >> 2];
@@ -348,25 +358,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
     for (int j = 0; j < PD; ++j)
         if (s0 + j < S) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
+    if (tid < BN) {
+        if constexpr (MODE == 0) tsc[tid].gu = xsc::gate_up_scale(s, B, my_xs);
+        else tsc[tid].m = xsc::h_exponent(s, B, my_xs);
+    }
     if constexpr (MODE == 0) {
         // SwiGLU rows h = silu(s W1 x) * (s W3 x) of the tile's 64 tokens x
         // 128 rows go through LDS (the token buffers are free after the last
         // step's barrier), already at the K-slots the down projection's
         // B-bit codes expect, then to H in coalesced 16-byte chunks. silu with
-        // the native base-2 exponential and reciprocal: h is stored as fp16.
+        // the native base-2 exponential and reciprocal; h is stored as fp16
+        // scaled by the token's 2^-m (xscale.h).
         constexpr int HS = tile_rows<0>() + 8;   // LDS row (halves), padded against bank conflicts
-        constexpr float kLog2e = 1.4426950408889634f;
         _Float16* hs = smem;
+        __syncthreads();   // the token scales are in LDS
 #pragma unroll
         for (int jt = 0; jt < NA; ++jt) {
             const int n = 16 * jt + r;
+            const xsc::GateUpScale gs = tsc[n].gu;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float av = s * acc[0][blk][jt][v];
-                    const float cv = s * acc[1][blk][jt][v];
-                    const float h = av * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-av * kLog2e)) * cv;
+                    const float h = xsc::swiglu_scaled_fast(acc[0][blk][jt][v], acc[1][blk][jt][v], gs);
                     hs[n * HS + 32 * wave + slot_of<B>(16 * blk + 4 * g + v)] = (_Float16)h;
                 }
         }
@@ -406,8 +420,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
             constexpr int kChunks = tile_rows<1>() / 4;   // 16-byte chunks per token row
             for (int c = tid; c < rows * kChunks; c += kThreads) {
                 const int n = c / kChunks, ch = c % kChunks;
-                *reinterpret_cast<u32x4*>(a.w.O + (int64_t)pair[n0 + n] * a.d + rt * tile_rows<1>() +
-                                          4 * ch) = *reinterpret_cast<const u32x4*>(os + n * kOutStride + 4 * ch);
+                const int m = tsc[n0 + n].m;   // the token's SwiGLU rows were stored as h 2^-m
+                const f32x4 v = *reinterpret_cast<const f32x4*>(os + n * kOutStride + 4 * ch);
+                *reinterpret_cast<f32x4*>(a.w.O + (int64_t)pair[n0 + n] * a.d + rt * tile_rows<1>() + 4 * ch) =
+                    f32x4{ldexpf(v.x, m), ldexpf(v.y, m), ldexpf(v.z, m), ldexpf(v.w, m)};
             }
         }
     }
@@ -415,11 +431,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
 
 template <int MODE, int B>
 __device__ __forceinline__ void dispatch_na(int na, const GemmArgs& a, const TileDesc& td, int tt, int rt,
-                                            _Float16* smem, int* tok, int* pair) {
-    if (na >= 4) gemm_tile<MODE, B, 4>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
-    else if (na == 3) gemm_tile<MODE, B, 3>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
-    else if (na == 2) gemm_tile<MODE, B, 2>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
-    else gemm_tile<MODE, B, 1>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair);
+                                            _Float16* smem, int* tok, int* pair, TokScale* tsc) {
+    if (na >= 4) gemm_tile<MODE, B, 4>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair, tsc);
+    else if (na == 3) gemm_tile<MODE, B, 3>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair, tsc);
+    else if (na == 2) gemm_tile<MODE, B, 2>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair, tsc);
+    else gemm_tile<MODE, B, 1>(a, td.e, td.cnt, td.off, tt, rt, smem, tok, pair, tsc);
 }
 
 template <int MODE>
@@ -427,6 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
     __shared__ int tok[BN];
     __shared__ int pair[MODE == 1 ? BN : 1];
+    __shared__ TokScale tsc[BN];
     // XCD swizzle: the eighth of this forward's tiles (the grid is sized for
     // the most a batch can have) that this workgroup's XCD walks, so the
     // XCDs get equal shares and the unused workgroups are spread over them
@@ -448,9 +465,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a, int row_t
     // 16-token blocks holding real tokens (fewer than four only in an
     // expert's last token tile): the MFMAs of the empty ones are skipped
     const int nblk = (min(BN, td.cnt - tt * BN) + 15) >> 4;
-    if (b == 4) dispatch_na<MODE, 4>(nblk, a, td, tt, rt, smem, tok, pair);
-    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, td, tt, rt, smem, tok, pair);
-    else dispatch_na<MODE, 3>(nblk, a, td, tt, rt, smem, tok, pair);
+    if (b == 4) dispatch_na<MODE, 4>(nblk, a, td, tt, rt, smem, tok, pair, tsc);
+    else if (b == 8) dispatch_na<MODE, 8>(nblk, a, td, tt, rt, smem, tok, pair, tsc);
+    else dispatch_na<MODE, 3>(nblk, a, td, tt, rt, smem, tok, pair, tsc);
 }
 
 template <int MODE>
@@ -472,10 +489,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, KTimer t) {
 bool gemm_supported(int d, int F) { return d % tile_rows<1>() == 0 && F % tile_rows<0>() == 0; }
 
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
-    const int64_t groups = (int64_t)a.T * (a.d / 32);
-    return launch_timed(prep_x_kernel, dim3((unsigned)((groups + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+    const int per_block = kThreads / 64;
+    return launch_timed(prep_x_kernel, dim3((unsigned)((a.T + per_block - 1) / per_block)), dim3(kThreads), 0, s,
                         (hipEvent_t) nullptr, (hipEvent_t) nullptr, a.x, a.T, a.d, a.bits_mask,
-                        const_cast<_Float16*>(a.xp), a.xp_plane);
+                        const_cast<_Float16*>(a.xp), a.xp_plane, a.w.xst);
 }
 hipError_t launch_gate_up_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<0>(a, s, t); }
 hipError_t launch_down_gemm(const GemmArgs& a, hipStream_t s, KTimer t) { return launch_gemm<1>(a, s, t); }

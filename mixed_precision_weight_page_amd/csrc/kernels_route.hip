@@ -10,9 +10,19 @@
 // by expert id), so the longest tiles are dispatched first.
 //
 // Top-k per token: with at most 256 experts a row of 16 lanes routes one
-// token (DPP reductions within the row), else a wave (shuffles). Up to 64
-// tokens (16 with more than 256 experts): one workgroup does everything. Up to kFusedMaxPairs pairs: a router kernel over many workgroups, then one
-// workgroup ranks and offsets. Larger batches: router; ranks per expert and
+// token (DPP reductions within the row), else a wave (shuffles).
+//
+// The streaming (decode) kernels need per expert only its set of pairs, in
+// any order (each token is its own column of the expert's products, their
+// SwiGLU rows and outputs are addressed by pair index, and the combine sums
+// in slot order), so their router groups the pairs with atomic adds in the
+// same launch as the top-k: one kernel over many small workgroups, which
+// also takes each token's activation statistics (xscale.h).
+//
+// The matrix-core kernels work on token tiles of a stable counting sort.
+// Up to 64 tokens (16 with more than 256 experts): one workgroup does
+// everything. Up to kFusedMaxPairs pairs: a router kernel over many
+// workgroups, then one workgroup ranks and offsets. Larger batches: router; ranks per expert and
 // chunk of kRankChunk tokens; counts, chunk prefixes and offsets in one
 // workgroup; pair positions over many workgroups. Kernel boundaries carry
 // the results between workgroups (a device-scope handshake inside one kernel
@@ -22,7 +32,10 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "pw_internal.h"
+#include "xscale.h"
 
 namespace pw {
 namespace {
@@ -43,9 +56,17 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
 
 // One wave routes token t: writes ids/g (and the ids to s_ids if given).
 // PER = logits held per lane (ceil(E / 64)).
+// The decode grouping of pair p = t k + j routed to expert e: the next
+// position of e's list; the expert's first pair appends it to the active list.
+__device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, int e, int p) {
+    const int slot = atomicAdd(&g.cnt[e], 1);
+    g.list[(int64_t)e * tcap + slot] = p;
+    if (slot == 0) g.act[atomicAdd(g.n_act, 1)] = e;
+}
+
 template <int PER>
 __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork& w, int t,
-                                              int* s_ids) {
+                                              int* s_ids, bool group) {
     const int lane = threadIdx.x & 63;
     const float* row = a.logits + (int64_t)t * a.E;
     float v[PER];
@@ -90,6 +111,7 @@ __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork&
         w.ids[(int64_t)t * a.k + lane] = my_id;
         w.g[(int64_t)t * a.k + lane] = mine / den;
         if (s_ids) s_ids[t * a.k + lane] = my_id;
+        if (group) group_pair(w.dg, w.tcap, my_id, t * a.k + lane);
     }
 }
 
@@ -156,7 +178,7 @@ __device__ __forceinline__ uint64_t row_max_key(uint64_t k) {
 // softmax weights use the native base-2 exponential of (v - top) log2(e).
 template <int PER>
 __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w, int t, bool valid,
-                                            int* s_ids) {
+                                            int* s_ids, bool group) {
     const int l16 = threadIdx.x & 15;
     const float* row = a.logits + (int64_t)t * a.E;
     float v[PER];
@@ -198,30 +220,81 @@ __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w
         w.ids[(int64_t)t * a.k + l16] = id0;
         w.g[(int64_t)t * a.k + l16] = m0 / den;
         if (s_ids) s_ids[t * a.k + l16] = id0;
+        if (group) group_pair(w.dg, w.tcap, id0, t * a.k + l16);
     }
     if (l16 + 16 < a.k) {
         w.ids[(int64_t)t * a.k + l16 + 16] = id1;
         w.g[(int64_t)t * a.k + l16 + 16] = m1 / den;
         if (s_ids) s_ids[t * a.k + l16 + 16] = id1;
+        if (group) group_pair(w.dg, w.tcap, id1, t * a.k + l16 + 16);
     }
 }
 
-__device__ __forceinline__ void route_row(const RouteArgs& a, const FwdWork& w, int t, bool valid, int* s_ids) {
+__device__ __forceinline__ void route_row(const RouteArgs& a, const FwdWork& w, int t, bool valid, int* s_ids,
+                                          bool group = false) {
     const int per = (a.E + 15) / 16;
-    if (per == 1) route_row_t<1>(a, w, t, valid, s_ids);
-    else if (per == 2) route_row_t<2>(a, w, t, valid, s_ids);
-    else if (per <= 4) route_row_t<4>(a, w, t, valid, s_ids);
-    else if (per <= 8) route_row_t<8>(a, w, t, valid, s_ids);
-    else route_row_t<16>(a, w, t, valid, s_ids);
+    if (per == 1) route_row_t<1>(a, w, t, valid, s_ids, group);
+    else if (per == 2) route_row_t<2>(a, w, t, valid, s_ids, group);
+    else if (per <= 4) route_row_t<4>(a, w, t, valid, s_ids, group);
+    else if (per <= 8) route_row_t<8>(a, w, t, valid, s_ids, group);
+    else route_row_t<16>(a, w, t, valid, s_ids, group);
 }
 
-__device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t, int* s_ids) {
+__device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t, int* s_ids,
+                                            bool group = false) {
     const int per = (a.E + 63) / 64;
-    if (per == 1) route_token_t<1>(a, w, t, s_ids);
-    else if (per == 2) route_token_t<2>(a, w, t, s_ids);
-    else if (per <= 4) route_token_t<4>(a, w, t, s_ids);
-    else if (per <= 8) route_token_t<8>(a, w, t, s_ids);
-    else route_token_t<16>(a, w, t, s_ids);
+    if (per == 1) route_token_t<1>(a, w, t, s_ids, group);
+    else if (per == 2) route_token_t<2>(a, w, t, s_ids, group);
+    else if (per <= 4) route_token_t<4>(a, w, t, s_ids, group);
+    else if (per <= 8) route_token_t<8>(a, w, t, s_ids, group);
+    else route_token_t<16>(a, w, t, s_ids, group);
+}
+
+// Statistics of an activation row (xscale.h) by a group of L lanes (16: a
+// row of lanes, reduced with DPP; 64: a wave, the rows then combined with
+// shuffles): lane i takes the 16-byte chunks i, i + L, ...; max |x| as bf16
+// magnitude bits and sum |x| in fp64 (no overflow or underflow for any row
+// of bf16 values). Every reduction step adds two partial results in either
+// order, so all lanes of the group end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const int lo = dpp_i<CTRL>((int)(uint32_t)u), hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+template <int L>
+__device__ __forceinline__ XStat lanes_stat(const uint16_t* row, int d) {
+    const int li = threadIdx.x & (L - 1);
+    const uint4* r = reinterpret_cast<const uint4*>(row);
+    uint32_t mx = 0;
+    double sum = 0.0;
+#pragma unroll 4
+    for (int c = li; c < d / 8; c += L) {
+        const uint4 u = r[c];
+        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t lo = ww[h] & 0x7fffu, hi = (ww[h] >> 16) & 0x7fffu;
+            mx = max(mx, max(lo, hi));
+            sum += (double)__uint_as_float(lo << 16) + (double)__uint_as_float(hi << 16);
+        }
+    }
+    mx = max(mx, (uint32_t)dpp_i<kQuadXor1>((int)mx));
+    sum += dpp_d<kQuadXor1>(sum);
+    mx = max(mx, (uint32_t)dpp_i<kQuadXor2>((int)mx));
+    sum += dpp_d<kQuadXor2>(sum);
+    mx = max(mx, (uint32_t)dpp_i<kRowHalfMirror>((int)mx));
+    sum += dpp_d<kRowHalfMirror>(sum);
+    mx = max(mx, (uint32_t)dpp_i<kRowMirror>((int)mx));
+    sum += dpp_d<kRowMirror>(sum);
+    if constexpr (L == 64) {
+        for (int o = 16; o < 64; o <<= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            sum += __shfl_xor(sum, o);
+        }
+    }
+    const int e = xsc::x_exponent(__uint_as_float(mx << 16));
+    return XStat{(float)ldexp(sum, -e), e};
 }
 
 // Inclusive scan over the 1024 threads of the block (every thread calls it).
@@ -302,9 +375,8 @@ __device__ __forceinline__ ExpertPage load_page(const DevTable& tab, int E) {
     return e < E ? ExpertPage{tab.off[e], tab.scale[e], tab.bits[e]} : ExpertPage{0, 0.0f, 0};
 }
 
-// Offsets, bit-ordered active list, the streaming kernels' slot descriptors
-// and the token tiles; cnt_of(e) gives the count of expert e. Leaves the
-// offsets in s_off.
+// Offsets, bit-ordered active list and the token tiles; cnt_of(e) gives the
+// count of expert e. Leaves the offsets in s_off.
 template <class CntF>
 __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const ExpertPage& my, int tiles,
                                                  CntF cnt_of, int* s_off) {
@@ -334,7 +406,6 @@ __device__ __forceinline__ void finalize_offsets(int E, const FwdWork& w, const 
         const int before = (int)((linc >> (21 * cls)) & 0x1fffff) - 1;
         const int base = cls == 0 ? 0 : (cls == 1 ? n8 : n8 + n4);
         w.act[base + before] = tid;
-        w.slots[base + before] = SlotDesc{my.off, my.scale, tid, b, c, inc - c, 0};
         s_slot_cnt[base + before] = c;
         s_slot_exp[base + before] = tid;
     }
@@ -487,6 +558,34 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
     }
 }
 
+// ---- streaming kernels: top-k, grouping by atomics, token statistics ----
+// grid ceil(T / 4) (E <= 256: row r of block b handles token 4b + r) or T (a
+// wave per token), 64 threads. Block 0 also clears the other counter set for
+// the next forward (every kernel of the previous forward, which used it, has
+// finished).
+__global__ __launch_bounds__(64) void route_decode_kernel(RouteArgs a, FwdWork w) {
+    if (blockIdx.x == 0) {
+        for (int e = threadIdx.x; e < a.E; e += 64) w.dg_next.cnt[e] = 0;
+        if (threadIdx.x == 0) w.dg_next.n_act[0] = 0;
+    }
+    if (a.E <= kRowMaxExperts) {
+        const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
+        const bool valid = t < a.T;
+        route_row(a, w, valid ? t : a.T - 1, valid, nullptr, true);
+        if (valid && a.x) {
+            const XStat st = lanes_stat<16>(a.x + (int64_t)t * a.d, a.d);
+            if ((threadIdx.x & 15) == 0) w.xst[t] = st;
+        }
+    } else {
+        const int t = blockIdx.x;
+        route_token(a, w, t, nullptr, true);
+        if (a.x) {
+            const XStat st = lanes_stat<64>(a.x + (int64_t)t * a.d, a.d);
+            if (threadIdx.x == 0) w.xst[t] = st;
+        }
+    }
+}
+
 // grid (E, C), 256 threads: rank of expert e's pairs in token order among
 // the tokens of chunk c, and their count.
 __global__ __launch_bounds__(256) void rank_kernel(int T, int k, int C, FwdWork w) {
@@ -542,7 +641,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(int P, int k, int C, FwdWo
     w.sorted[w.off[e] + w.cpre[e * C + c] + w.rank[p]] = p;
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* p, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    zero_kernel<<<(unsigned)std::min<uint64_t>((n + 255) / 256, 1024), 256, 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
+    const int blocks = a.E <= kRowMaxExperts ? (a.T + 3) / 4 : a.T;
+    return launch_timed(route_decode_kernel, dim3((unsigned)blocks), dim3(64), 0, s, t.start, t.stop, a, w);
+}
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t) {

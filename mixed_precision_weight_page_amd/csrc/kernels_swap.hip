@@ -27,7 +27,8 @@ constexpr int kPlanThreads = 1024;
 constexpr int kCopyThreads = 256;
 constexpr int64_t kCopyChunk = 256 * 1024;   // bytes per copy workgroup
 
-__global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, FwdWork w, DevTable tab, int E,
+__global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, const int32_t* act,
+                                                                   const int32_t* n_act_p, DevTable tab, int E,
                                                                    int S, const uint8_t* pool,
                                                                    const uint8_t* host, uint64_t slot_bytes) {
     __shared__ int32_t s_slot[kMaxExperts];     // slot of each expert (-1: none)
@@ -39,14 +40,14 @@ __global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, F
     __shared__ int32_t s_scan[kPlanThreads];
     const int tid = threadIdx.x;
     const uint32_t step = st.step[0] + 1;
-    const int n_act = w.n_act[0];
+    const int n_act = n_act_p[0];
     for (int e = tid; e < E; e += kPlanThreads) {
         s_slot[e] = st.slot_of[e];
         s_act[e] = 0;
     }
     for (int s = tid; s < S; s += kPlanThreads) s_exp[s] = st.expert_of[s];
     __syncthreads();
-    for (int i = tid; i < n_act; i += kPlanThreads) s_act[w.act[i]] = 1;
+    for (int i = tid; i < n_act; i += kPlanThreads) s_act[act[i]] = 1;
     __syncthreads();
 
     // misses ranked by expert id: a block scan over the E flags, each thread
@@ -125,12 +126,6 @@ __global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, F
         if (s_act[e]) st.last_use[e] = step;
     }
     for (int s = tid; s < S; s += kPlanThreads) st.expert_of[s] = s_exp[s];
-    // the streaming kernels' slot descriptors carry this pass's address
-    for (int i = tid; i < n_act; i += kPlanThreads) {
-        const int e = w.act[i];
-        const int s = s_slot[e];
-        w.slots[i].page = s >= 0 ? (uint64_t)(pool + (uint64_t)s * slot_bytes) : (uint64_t)(host + tab.off[e]);
-    }
     if (tid == 0) {
         st.step[0] = step;
         st.ncopy[0] = ncopy;
@@ -174,10 +169,10 @@ __global__ __launch_bounds__(256) void swap_invalidate_kernel(SwapState st, cons
 
 }  // namespace
 
-hipError_t launch_swap_in(const SwapState& st, const FwdWork& w, const DevTable& tab, int E, int S,
-                          int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host, uint64_t slot_bytes,
-                          hipStream_t s) {
-    swap_plan_kernel<<<1, kPlanThreads, 0, s>>>(st, w, tab, E, S, pool, host, slot_bytes);
+hipError_t launch_swap_in(const SwapState& st, const int32_t* act, const int32_t* n_act, const DevTable& tab,
+                          int E, int S, int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host,
+                          uint64_t slot_bytes, hipStream_t s) {
+    swap_plan_kernel<<<1, kPlanThreads, 0, s>>>(st, act, n_act, tab, E, S, pool, host, slot_bytes);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || max_copies <= 0) return err;
     const dim3 grid((unsigned)((slot_bytes + kCopyChunk - 1) / kCopyChunk), (unsigned)max_copies);

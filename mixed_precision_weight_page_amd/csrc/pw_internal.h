@@ -41,15 +41,23 @@ struct __attribute__((aligned(16))) TileDesc {
     int32_t e, first, cnt, off;
 };
 
-// One routed expert of the streaming kernels, in active-list order: its page
-// (offset into the pool, or with a host tier the page's address for this
-// pass), scale and bit-width, and its pair count and first sorted position.
-// The router writes it (the host tier's plan patches the page), so a
-// workgroup reads everything it needs before its first code load at once.
-struct __attribute__((aligned(16))) SlotDesc {
-    uint64_t page;
-    float scale;
-    int32_t e, bits, cnt, off, pad;
+// Grouping of the streaming (decode) kernels: per expert the list of its
+// (token, slot) pairs t k + j, filled by atomic adds (capacity tcap per
+// expert: a token routes to an expert at most once), and the list of routed
+// experts. The counters come in two sets that alternate between forwards:
+// the router of one forward clears the set of the next.
+struct DecodeGroup {
+    int32_t* cnt;     // [E] pairs routed to each expert
+    int32_t* n_act;   // [1] routed experts
+    int32_t* act;     // [E] routed experts, in arrival order
+    int32_t* list;    // [E, tcap] pair indices of each expert, in arrival order
+};
+
+// Per-token statistics of the activations (xscale.h): e with max|x| 2^-e in
+// [2^14, 2^15) and n1 = sum |x| 2^-e over the row.
+struct __attribute__((aligned(8))) XStat {
+    float n1;
+    int32_t e;
 };
 
 // Forward-pass scratch carved out of the bound workspace.
@@ -63,16 +71,22 @@ struct FwdWork {
     int32_t* act;      // [E] experts with cnt > 0, ascending
     int32_t* n_act;    // [2] active experts; token tiles of the large-batch kernels
     TileDesc* tiles;   // [ceil(P / kGemmTokens) + E] token tiles in active-list order
-    SlotDesc* slots;   // [E] routed experts in active-list order
+    DecodeGroup dg;    // grouping of this forward (streaming kernels)
+    DecodeGroup dg_next;   // the other counter set, cleared for the next forward
+    int tcap;          // capacity of each expert's pair list
     int32_t* ccnt;     // [E, C] pairs of expert e among the tokens of chunk c (kRankChunk tokens)
     int32_t* cpre;     // [E, C] exclusive prefix of ccnt over the chunks
-    _Float16* H;       // [P, F] SwiGLU output per sorted pair
+    XStat* xst;        // [T] activation statistics per token
+    _Float16* H;       // [P, F] SwiGLU output, scaled by 2^-m (xscale.h): per sorted pair on the
+                       // matrix-core path, per pair t k + j on the streaming path
     float* O;          // [nsplit, P, d] down-projection partials per pair t k + j (scaled by s_e)
 };
 
 struct Layout {
-    uint64_t ids, g, rank, sorted, cnt, off, act, n_act, tiles, slots, ccnt, cpre, H, O, xp, fwd_end;
+    uint64_t ids, g, rank, sorted, cnt, off, act, n_act, tiles, ccnt, cpre, xst, H, O, xp, list, fwd_end;
     uint64_t partial, stats_end;
+    uint64_t dg, dg_bytes;   // the two counter sets of the streaming kernels' grouping (outside the
+                             // bytes the statistics pass reuses; zeroed when the workspace is bound)
     uint64_t total;
 };
 
@@ -113,11 +127,18 @@ hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, 
 
 struct RouteArgs {
     const float* logits;
+    const uint16_t* x;   // bf16 [T, d]: per-token statistics into FwdWork::xst (NULL: none)
+    int d;
     int T, E, k, renorm;
     int tiles;   // also the large-batch kernels' token tiles (FwdWork::tiles)
 };
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t = {});
+// Router of the streaming kernels: top-k, weights, token statistics and the
+// grouping of FwdWork::dg, in one launch over many workgroups.
+hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t = {});
+// n int32 zeros at p (one small kernel)
+hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s);
 
 struct FfnPlan {
     int nt_alloc;     // token rows the LDS is sized for
@@ -174,9 +195,9 @@ struct SwapState {
     int32_t* copy_s;      // [S] slot of each copy
     uint64_t* addr;       // [E] page address for the current pass
 };
-hipError_t launch_swap_in(const SwapState& st, const FwdWork& w, const DevTable& tab, int E, int S,
-                          int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host, uint64_t slot_bytes,
-                          hipStream_t s);
+hipError_t launch_swap_in(const SwapState& st, const int32_t* act, const int32_t* n_act, const DevTable& tab,
+                          int E, int S, int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host,
+                          uint64_t slot_bytes, hipStream_t s);
 hipError_t launch_swap_invalidate(const SwapState& st, const int32_t* list, int n, hipStream_t s);
 
 // ---- host allocator (alloc.cpp) ----

@@ -18,16 +18,12 @@ Readings where the page is silent (each is listed in the design notes):
   code is clamped to [-qmax, qmax];
 * a code q is stored as the unsigned value u = q + 2^(b-1);
 * page layout: [W1 codes][W3 codes][W2 codes]; each matrix is [out, in]
-  (W1, W3: F x d; W2: d x F). Each row is first written as a dense LSB-first
+  (W1, W3: F x d; W2: d x F), row after row; each row is a dense LSB-first
   bitstream (code j of the row occupies stream bits b*j .. b*j+b-1, stream
-  bit i is bit i%8 of byte i//8), rows padded with zero bits to a multiple
-  of 128 codes. The row bitstreams are then arranged in tiles of 16 rows x
-  128 codes (``tile_matrix``): tiles in (row block, K step) order; inside a
-  tile, each row's 128 codes are four runs of 32 codes (4b bytes each),
-  and run g of row r is the "lane" l = 16 g + r; a lane's 4b bytes are cut
-  into pieces of at most 16 bytes and piece p of all 64 lanes is stored
-  together, lane after lane. The page is padded with zero bytes to a
-  multiple of 256;
+  bit i is bit i%8 of byte i//8), padded with zero bits to a multiple of
+  128 codes. The page is padded with zero bytes to a multiple of 256. (How
+  the library arranges these bytes in device memory is its own business;
+  the tests map its pages back to this form.)
 * the loss L(b) of the allocation problem is the mean squared error of
   Eq. 2 on the expert's own weights, in float64.
 """
@@ -117,29 +113,6 @@ def unpack_rows(packed: torch.Tensor, b: int, K: int) -> torch.Tensor:
     return u[:, :K].to(torch.uint8)
 
 
-TILE_ROWS = 16
-
-
-def tile_matrix(packed: torch.Tensor, b: int) -> torch.Tensor:
-    """Arrange a matrix of packed row bitstreams [rows, Kp*b/8] in tiles.
-
-    rows must be a multiple of 16 and Kp of 128. A tile is 16 rows x 128
-    codes (16*128*b/8 bytes); within it lane l = 16*g + r holds the 4b bytes
-    of codes 32g..32g+31 of row r, split into pieces of min(16, 4b) bytes,
-    and piece p of lanes 0..63 is stored contiguously. Returns flat bytes.
-    """
-    rows, nbytes = packed.shape
-    assert rows % TILE_ROWS == 0 and (nbytes * 8 // b) % ROW_ALIGN_CODES == 0
-    lane_bytes = 4 * b
-    piece = min(16, lane_bytes)
-    npiece = lane_bytes // piece
-    steps = nbytes // (32 * b // 2)           # 128 codes = 16 b bytes per row
-    t = packed.reshape(rows // TILE_ROWS, TILE_ROWS, steps, 4, npiece, piece)
-    #                    block,            r,        step,  g, piece, bytes
-    t = t.permute(0, 2, 4, 3, 1, 5)          # block, step, piece, g, r, bytes
-    return t.reshape(-1).contiguous()
-
-
 def matrix_bytes(rows: int, K: int, b: int) -> int:
     Kp = -(-K // ROW_ALIGN_CODES) * ROW_ALIGN_CODES
     return rows * Kp * b // 8
@@ -153,8 +126,9 @@ def page_nbytes(d: int, F: int, b: int) -> int:
 
 def expert_page(w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, b: int,
                 s: float) -> torch.Tensor:
-    """The page of one expert: packed W1 codes, then W3, then W2, zero-padded."""
-    parts = [tile_matrix(pack_rows(stored(codes(w, s, b), b), b), b) for w in (w1, w3, w2)]
+    """The page of one expert: the packed rows of W1, then of W3, then of W2,
+    zero-padded to a multiple of 256 bytes."""
+    parts = [pack_rows(stored(codes(w, s, b), b), b).reshape(-1) for w in (w1, w3, w2)]
     page = torch.cat(parts)
     n = page_nbytes(w1.shape[1], w1.shape[0], b)
     if page.numel() < n:

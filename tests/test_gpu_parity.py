@@ -369,6 +369,21 @@ def test_large_batch_matrix_core_path(T):
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
 
 
+def test_small_batches_on_a_context_sized_for_large_ones():
+    """A context whose workspace is sized for 2048 tokens (its partial-output
+    buffer holds one split per pair) still splits the down product of a
+    1- or 3-token batch: the split stride is the batch's own pair count."""
+    wl = synth.WORKLOADS["tiny"].scaled(name="big_ctx", E=4, d=256, F=1024, k=2, T=3, bits=(8, 4, 3, 4))
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=2048)
+    layer.quantize_experts(wl.bits)
+    for T in (1, 3, 40):
+        x, logits = synth.tokens(wl, T=T, step=T)
+        log(f"large context: forward T={T}")
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"large context T={T}")
+
+
 @pytest.mark.parametrize("F", [384, 640, 896, 1024])
 def test_down_splits_summed_in_order(F):
     """Small batches split the down product along d_ff (here into 3, 5, 7

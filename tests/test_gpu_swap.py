@@ -2,13 +2,15 @@
 cache of page slots): the forward equals the one without a host tier bit
 for bit, the slot of every expert after each pass equals the residency
 oracle's (oracle/swap.py), slot bytes equal the host pages, which equal the
-oracle's pages; requantizing empties exactly the rewritten experts' slots."""
+oracle's pages, and every output is also checked against the float64
+oracle's forward; requantizing empties exactly the rewritten experts'
+slots."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from layer_cases import check_pages, cpu_threads, log, make_layer
+from layer_cases import check_pages, compare_y, cpu_threads, log, make_layer, oracle_y
 from oracle import moe
 from oracle import swap as oswap
 
@@ -70,6 +72,7 @@ def test_forward_equal_and_residency_follows_the_oracle():
         yb = b.moe_forward(x.cuda(), logits.cuda())
         torch.cuda.synchronize()
         assert torch.equal(ya, yb), step
+        compare_y(yb, oracle_y(x, logits, WL, masters, bits), f"host tier step {step}")
         res.forward(_active(logits))
         _check_slots(b, host, slots, res)
     assert res.copies > 6 and res.hits > 0 and res.host_reads > 0
@@ -108,18 +111,20 @@ def test_requantize_empties_rewritten_slots():
         yb = b.moe_forward(x.cuda(), logits.cuda())
         torch.cuda.synchronize()
         assert torch.equal(ya, yb)
+        compare_y(yb, oracle_y(x, logits, WL, masters, new), f"after requantization, step {step}")
         res.forward(_active(logits))
         _check_slots(b, host, slots, res)
 
 
 def test_no_slots_reads_every_page_from_the_host_tier():
     bits = [8, 4, 3, 4] * (WL.E // 4)
-    _, a, b, host, slots = _pair(0, bits)
+    masters, a, b, host, slots = _pair(0, bits)
     x, logits = synth.tokens(WL, T=4, step=7)
     ya = a.moe_forward(x.cuda(), logits.cuda())
     yb = b.moe_forward(x.cuda(), logits.cuda())
     torch.cuda.synchronize()
     assert torch.equal(ya, yb)
+    compare_y(yb, oracle_y(x, logits, WL, masters, bits), "no slots")
     slot_of, stats = b.residency()
     assert (slot_of == -1).all()
     assert stats == dict(hits=0, copies=0, host_reads=len(_active(logits)))
@@ -129,7 +134,7 @@ def test_matrix_core_path_through_the_host_tier():
     # 320 tokens x top-8 over 32 experts (80 per expert): the large-batch kernels
     wl = WL.scaled(name="swap_gemm", T=320)
     bits = [3, 4, 8, 4] * (wl.E // 4)
-    _, a, b, host, slots = _pair(20, bits, wl)
+    masters, a, b, host, slots = _pair(20, bits, wl)
     res = oswap.Residency(wl.E, 20)
     for step in range(3):
         x, logits = synth.tokens(wl, T=320, step=300 + step)
@@ -138,6 +143,7 @@ def test_matrix_core_path_through_the_host_tier():
         yb = b.moe_forward(x.cuda(), logits.cuda())
         torch.cuda.synchronize()
         assert torch.equal(ya, yb)
+        compare_y(yb, oracle_y(x, logits, wl, masters, bits), f"host tier, matrix cores, step {step}")
         res.forward(_active(logits))
         _check_slots(b, host, slots, res)
 
@@ -159,7 +165,7 @@ def test_many_experts_and_slots():
     wl = synth.WORKLOADS["tiny"].scaled(name="swap_e300", E=300, k=6, T=48)
     rng = np.random.default_rng(3)
     bits = rng.choice([3, 4, 8], size=wl.E).tolist()
-    _, a, b, host, slots = _pair(100, bits, wl)
+    masters, a, b, host, slots = _pair(100, bits, wl)
     res = oswap.Residency(wl.E, 100)
     for step in range(8):
         T = [48, 5, 30, 1][step % 4]
@@ -169,6 +175,7 @@ def test_many_experts_and_slots():
         yb = b.moe_forward(x.cuda(), logits.cuda())
         torch.cuda.synchronize()
         assert torch.equal(ya, yb)
+        compare_y(yb, oracle_y(x, logits, wl, masters, bits), f"host tier e300 step {step}")
         ids, _ = moe.route(logits, wl.k)
         res.forward(sorted(set(ids.flatten().tolist())))
         _check_slots(b, host, slots, res)

@@ -156,31 +156,21 @@ def test_pack_against_bigint_unpacker(b, K):
     assert torch.equal(quant.unpack_rows(packed, b, K), u)
 
 
-def tiled_row(matrix_bytes: bytes, rows: int, K: int, b: int, r: int) -> bytes:
-    """Independent address formula of the tile layout: gather row r's
-    bitstream back, piece by piece."""
-    steps = K // 128
-    lane_bytes = 4 * b
-    piece = min(16, lane_bytes)
-    out = bytearray()
-    for s in range(steps):
-        tile = ((r // 16) * steps + s) * (16 * 128 * b // 8)
-        for g in range(4):
-            for p in range(lane_bytes // piece):
-                at = tile + p * 64 * piece + (16 * g + r % 16) * piece
-                out += matrix_bytes[at:at + piece]
-    return bytes(out)
-
-
 @pytest.mark.parametrize("b", quant.BITS)
-def test_tile_layout_against_address_formula(b):
+def test_tests_page_map_two_statements_agree(b):
+    """The tests read device pages through pagemap.untile_matrix (a reshape
+    of the tile layout the library's header describes); the loop-based
+    address formula pagemap.tiled_row states the same map piece by piece."""
+    import pagemap
     rows, K = 48, 384
     g = torch.Generator().manual_seed(40 + b)
-    u = torch.randint(0, 2 ** b, (rows, K), generator=g, dtype=torch.int32).to(torch.uint8)
-    tiled = bytes(quant.tile_matrix(quant.pack_rows(u, b), b).tolist())
-    assert len(tiled) == rows * K * b // 8
+    tiled = torch.randint(0, 256, (rows * K * b // 8,), generator=g, dtype=torch.int32).to(torch.uint8)
+    rm = pagemap.untile_matrix(tiled, rows, K, b)
+    assert rm.shape == (rows, K * b // 8)
     for r in range(rows):
-        assert bigint_unpack(tiled_row(tiled, rows, K, b, r), b, K) == u[r].tolist(), r
+        assert bytes(rm[r].tolist()) == pagemap.tiled_row(tiled, K, b, r), r
+    # a permutation: every tiled byte lands exactly once
+    assert sorted(rm.reshape(-1).tolist()) == sorted(tiled.tolist())
 
 
 def test_page_layout_and_size():
@@ -197,15 +187,18 @@ def test_page_layout_and_size():
         assert page.numel() % 256 == 0
         assert page.numel() == 3 * d * F * b // 8       # 128-multiples: no padding
         pb = bytes(page.tolist())
-        # W3 block starts after the F rows of W1; W2 after both
+        # row-major bitstreams: W3 starts after the F rows of W1, W2 after
+        # both; a row of K codes takes K b / 8 bytes
         m1 = F * d * b // 8
         for r in (0, 17, F - 1):
-            q3 = bigint_unpack(tiled_row(pb[m1:2 * m1], F, d, b, r), b, d)
+            row = d * b // 8
+            q3 = bigint_unpack(pb[m1 + r * row:m1 + (r + 1) * row], b, d)
             want3 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
                      for v in w3[r].tolist()]
             assert q3 == want3
         for r in (0, 17, d - 1):
-            q2 = bigint_unpack(tiled_row(pb[2 * m1:], d, F, b, r), b, F)
+            row = F * b // 8
+            q2 = bigint_unpack(pb[2 * m1 + r * row:2 * m1 + (r + 1) * row], b, F)
             want2 = [exact_round_half_even(Fraction(float(v)) / Fraction(s)) + 2 ** (b - 1)
                      for v in w2[r].tolist()]
             assert q2 == want2

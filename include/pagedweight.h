@@ -140,6 +140,22 @@ pw_status pw_set_budget(pw_ctx* ctx, uint64_t budget_bits, const double* importa
 pw_status pw_moe_forward(pw_ctx* ctx, const void* x, const float* logits, int32_t T,
                          float* y, void* stream);
 
+/* pw_moe_forward without device allocation, for callers that cannot
+ * allocate (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, checks and results as pw_moe_forward
+ * (up to the fp32 summation order of the down product's K-splits), but its
+ * scratch lives in a static 64 MiB device array of the library (one per
+ * device, held until the process ends) instead of the bound workspace,
+ * which it neither needs nor touches; no timing events are recorded. The
+ * array is laid out for exactly T tokens; a batch whose scratch does not fit
+ * returns PW_ERR_WORKSPACE (decode batches fit: for example 64 tokens of
+ * 128 experts, d_model 2048, d_ff 768, top-8 need about 27 MiB). Every call
+ * on a device shares that device's array: calls that may overlap on one
+ * device (several streams, several contexts) race and must be serialized by
+ * the caller. The context's pages must exist (PW_ERR_STATE otherwise). */
+pw_status pw_moe_forward_noalloc(pw_ctx* ctx, const void* x, const float* logits, int32_t T, float* y,
+                                 void* stream);
+
 /* Router and grouping only (the first steps of pw_moe_forward), for
  * inspection: ids int32 [T, k] (descending logit order), g fp32 [T, k] and
  * counts int32 [E] (tokens routed to each expert), all device pointers. */

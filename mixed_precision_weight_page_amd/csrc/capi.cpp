@@ -177,36 +177,49 @@ pw_status ensure_device(pw_ctx* c) {
     return PW_OK;
 }
 
-FwdWork fwd_work(pw_ctx* c) {
+// Device memory a forward works in: the bound workspace, or the library's
+// static scratch (pw_moe_forward_noalloc), with the layout it is carved by.
+struct WsView {
+    uint8_t* base;
+    Layout lay;
+    int max_tokens;   // tokens the layout is sized for
+    int nsplit;       // K-splits per pair its partial-output buffer holds
+};
+
+WsView bound_ws(const pw_ctx* c) { return WsView{c->ws, c->lay, c->desc.max_tokens, c->nsplit}; }
+
+// The forward scratch of a view; `parity` picks the grouping counter set.
+FwdWork fwd_work(const pw_ctx* c, const WsView& v, int parity) {
     FwdWork w;
-    uint8_t* b = c->ws;
-    w.ids = reinterpret_cast<int32_t*>(b + c->lay.ids);
-    w.g = reinterpret_cast<float*>(b + c->lay.g);
-    w.rank = reinterpret_cast<int32_t*>(b + c->lay.rank);
-    w.sorted = reinterpret_cast<int32_t*>(b + c->lay.sorted);
-    w.cnt = reinterpret_cast<int32_t*>(b + c->lay.cnt);
-    w.off = reinterpret_cast<int32_t*>(b + c->lay.off);
-    w.act = reinterpret_cast<int32_t*>(b + c->lay.act);
-    w.n_act = reinterpret_cast<int32_t*>(b + c->lay.n_act);
-    w.tiles = reinterpret_cast<TileDesc*>(b + c->lay.tiles);
+    uint8_t* b = v.base;
+    const Layout& L = v.lay;
+    w.ids = reinterpret_cast<int32_t*>(b + L.ids);
+    w.g = reinterpret_cast<float*>(b + L.g);
+    w.rank = reinterpret_cast<int32_t*>(b + L.rank);
+    w.sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+    w.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
+    w.off = reinterpret_cast<int32_t*>(b + L.off);
+    w.act = reinterpret_cast<int32_t*>(b + L.act);
+    w.n_act = reinterpret_cast<int32_t*>(b + L.n_act);
+    w.tiles = reinterpret_cast<TileDesc*>(b + L.tiles);
     // the two counter sets: cnt [E], act [E], n_act, each set 256-byte aligned
     auto set = [&](int i) {
-        uint8_t* q = b + c->lay.dg + (uint64_t)i * (c->lay.dg_bytes / 2);
+        uint8_t* q = b + L.dg + (uint64_t)i * (L.dg_bytes / 2);
         DecodeGroup g;
         g.cnt = reinterpret_cast<int32_t*>(q);
         g.act = g.cnt + c->E;
         g.n_act = g.act + c->E;
-        g.list = reinterpret_cast<int32_t*>(b + c->lay.list);
+        g.list = reinterpret_cast<int32_t*>(b + L.list);
         return g;
     };
-    w.dg = set(c->dg_parity);
-    w.dg_next = set(1 - c->dg_parity);
-    w.tcap = std::max(c->desc.max_tokens, 16);
-    w.ccnt = reinterpret_cast<int32_t*>(b + c->lay.ccnt);
-    w.cpre = reinterpret_cast<int32_t*>(b + c->lay.cpre);
-    w.xst = reinterpret_cast<XStat*>(b + c->lay.xst);
-    w.H = reinterpret_cast<_Float16*>(b + c->lay.H);
-    w.O = reinterpret_cast<float*>(b + c->lay.O);
+    w.dg = set(parity);
+    w.dg_next = set(1 - parity);
+    w.tcap = std::max(v.max_tokens, 16);
+    w.ccnt = reinterpret_cast<int32_t*>(b + L.ccnt);
+    w.cpre = reinterpret_cast<int32_t*>(b + L.cpre);
+    w.xst = reinterpret_cast<XStat*>(b + L.xst);
+    w.H = reinterpret_cast<_Float16*>(b + L.H);
+    w.O = reinterpret_cast<float*>(b + L.O);
     return w;
 }
 
@@ -693,27 +706,29 @@ static bool dense_path(const pw_ctx* c, int32_t T) {
 }
 
 // Router and grouping for the path of the batch. The streaming kernels'
-// router also takes the token statistics (x may be NULL: none) and uses the
-// current counter set, so the next forward uses the other one. Returns the
-// per-expert counts.
-static pw_status route_batch(pw_ctx* c, const FwdWork& w, const float* logits, const void* x, int32_t T,
-                             bool dense, hipStream_t s, KTimer t, const int32_t** counts) {
+// router also takes the token statistics (x may be NULL: none). With the
+// bound workspace it uses the current counter set and the next forward the
+// other one (both cleared once after binding); the static scratch, shared by
+// every context on the device, has both sets cleared at each call. Returns
+// the per-expert counts.
+static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const float* logits, const void* x,
+                             int32_t T, bool dense, bool scratch, hipStream_t s, KTimer t,
+                             const int32_t** counts) {
     RouteArgs ra{logits, static_cast<const uint16_t*>(x), c->d, T, c->E, c->k, c->desc.renorm, 1};
     if (dense) {
         ra.x = nullptr;   // prep_x takes the statistics on this path
         HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s, t));
         *counts = w.cnt;
-    } else {
-        if (!c->dg_clean) {
-            // both counter sets start at zero (a kernel, not a memset: the
-            // stream may be under graph capture)
-            HIP_TRY(c, launch_zero_i32(reinterpret_cast<int32_t*>(c->ws + c->lay.dg), c->lay.dg_bytes / 4, s));
-            c->dg_clean = true;
-        }
-        HIP_TRY(c, launch_route_decode(ra, w, s, t));
-        c->dg_parity ^= 1;
-        *counts = w.dg.cnt;
+        return PW_OK;
     }
+    if (scratch || !c->dg_clean) {
+        // a kernel, not a memset: the stream may be under graph capture
+        HIP_TRY(c, launch_zero_i32(reinterpret_cast<int32_t*>(v.base + v.lay.dg), v.lay.dg_bytes / 4, s));
+        if (!scratch) c->dg_clean = true;
+    }
+    HIP_TRY(c, launch_route_decode(ra, w, s, t));
+    if (!scratch) c->dg_parity ^= 1;
+    *counts = w.dg.cnt;
     return PW_OK;
 }
 
@@ -734,9 +749,11 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     if (!ids || !g || !counts) return fail(c, PW_ERR_INVALID_ARG, "null output pointer");
     if ((st = ensure_device(c)) != PW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const FwdWork w = fwd_work(c);
+    const WsView v = bound_ws(c);
+    const FwdWork w = fwd_work(c, v, c->dg_parity);
     const int32_t* cnt = nullptr;
-    if ((st = route_batch(c, w, logits, nullptr, T, dense_path(c, T), s, KTimer{}, &cnt)) != PW_OK) return st;
+    if ((st = route_batch(c, v, w, logits, nullptr, T, dense_path(c, T), false, s, KTimer{}, &cnt)) != PW_OK)
+        return st;
     const size_t P = (size_t)T * c->k;
     HIP_TRY(c, hipMemcpyAsync(ids, w.ids, P * 4, hipMemcpyDeviceToDevice, s));
     HIP_TRY(c, hipMemcpyAsync(g, w.g, P * 4, hipMemcpyDeviceToDevice, s));
@@ -744,21 +761,14 @@ pw_status pw_route(pw_ctx* c, const float* logits, int32_t T, int32_t* ids, floa
     return PW_OK;
 }
 
-pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t T, float* y,
-                         void* stream) {
-    if (!c) return PW_ERR_INVALID_ARG;
-    pw_status st = forward_checks(c, logits, T);
-    if (st != PW_OK) return st;
-    if (!c->pages_valid) return fail(c, PW_ERR_STATE, "no quantized pages: call pw_quantize_experts or pw_set_budget first");
-    if (T == 0) return PW_OK;
-    if (!x || !y) return fail(c, PW_ERR_INVALID_ARG, "null x or y");
-    if ((uintptr_t)x % 16 || (uintptr_t)y % 16)
-        return fail(c, PW_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
-    if ((st = ensure_device(c)) != PW_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const FwdWork w = fwd_work(c);
+// The forward over a workspace view (a1-a5: route and group, gate/up +
+// SwiGLU, down, combine). `scratch`: the view is the static scratch (no
+// timing events, counters cleared at each call).
+static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const float* logits, int32_t T,
+                              float* y, hipStream_t s, bool scratch) {
+    const FwdWork w = fwd_work(c, v, scratch ? 0 : c->dg_parity);
     KTimer tm[4];
-    if (c->profile_mask) {
+    if (c->profile_mask && !scratch) {
         for (int j = 0; j < 4; ++j) {
             if (!((c->profile_mask >> j) & 1)) continue;
             tm[j].start = next_event(c);
@@ -771,21 +781,22 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
     const bool dense = dense_path(c, T);
     const int32_t* cnt = nullptr;
-    if ((st = route_batch(c, w, logits, x, T, dense, s, tm[0], &cnt)) != PW_OK) return st;
+    pw_status st = route_batch(c, v, w, logits, x, T, dense, scratch, s, tm[0], &cnt);
+    if (st != PW_OK) return st;
     // pages: pool + offset, or with a host tier the addresses of this pass
     // (slot or host tier) after the missing pages are copied in
     const uint8_t* base = c->pool;
     DevTable tab = dev_table(c, c->cur);
     if (swap_mode(c)) {
-        const SwapState st = swap_state(c);
+        const SwapState ss = swap_state(c);
         const int S = n_slots(c);
-        HIP_TRY(c, launch_swap_in(st, dense ? w.act : w.dg.act, dense ? w.n_act : w.dg.n_act, tab, c->E, S,
+        HIP_TRY(c, launch_swap_in(ss, dense ? w.act : w.dg.act, dense ? w.n_act : w.dg.n_act, tab, c->E, S,
                                   std::min(S, max_act), c->We, c->pool, c->host, slot_bytes(c), s));
-        tab.off = st.addr;
+        tab.off = ss.addr;
         base = nullptr;
     }
     // partial outputs of the down product: O[split][pair][d] with this
-    // batch's pair count as the split stride, so a context sized for large
+    // batch's pair count as the split stride, so a view sized for large
     // batches splits small ones as far as its buffer allows
     const int P = (int)pairs;
     if (dense) {
@@ -800,8 +811,8 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         ga.max_act = max_act;
         ga.P_used = pairs;
         ga.T = T;
-        ga.xp = reinterpret_cast<const _Float16*>(c->ws + c->lay.xp);
-        ga.xp_plane = (int64_t)c->desc.max_tokens * c->d;
+        ga.xp = reinterpret_cast<const _Float16*>(v.base + v.lay.xp);
+        ga.xp_plane = (int64_t)v.max_tokens * c->d;
         ga.bits_mask = 0;
         for (int e = 0; e < c->E; ++e) ga.bits_mask |= 1 << bits_index(c->table[e].bits);
         HIP_TRY(c, launch_prep_x(ga, s));
@@ -820,14 +831,67 @@ pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t 
         fa.max_act = max_act;
         fa.P = P;
         // K splits of the down product for this batch, within the buffer
-        const int64_t cap_pairs = (int64_t)c->nsplit * c->desc.max_tokens * c->k;
+        const int64_t cap_pairs = (int64_t)v.nsplit * v.max_tokens * c->k;
         const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / pairs, 1 << 30));
         HIP_TRY(c, launch_gate_up(fa, plan_ffn(c->d, T, 1), s, tm[1]));
         HIP_TRY(c, launch_down(fa, plan_ffn(c->F, T, nsplit), s, tm[2]));
         HIP_TRY(c, launch_combine(w, T, c->d, c->k, P, nsplit, y, s, tm[3]));
     }
-    if (c->profile_mask) c->forwards_timed++;
+    if (c->profile_mask && !scratch) c->forwards_timed++;
     return PW_OK;
+}
+
+static pw_status forward_args(pw_ctx* c, const void* x, const float* logits, int32_t T, const float* y) {
+    if (!c->pages_valid) return fail(c, PW_ERR_STATE, "no quantized pages: call pw_quantize_experts or pw_set_budget first");
+    if (T == 0) return PW_OK;
+    if (!x || !y) return fail(c, PW_ERR_INVALID_ARG, "null x or y");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16)
+        return fail(c, PW_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    return PW_OK;
+}
+
+pw_status pw_moe_forward(pw_ctx* c, const void* x, const float* logits, int32_t T, float* y,
+                         void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    pw_status st = forward_checks(c, logits, T);
+    if (st != PW_OK) return st;
+    if ((st = forward_args(c, x, logits, T, y)) != PW_OK || T == 0) return st;
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    return forward_core(c, bound_ws(c), x, logits, T, y, static_cast<hipStream_t>(stream), false);
+}
+
+pw_status pw_moe_forward_noalloc(pw_ctx* c, const void* x, const float* logits, int32_t T, float* y,
+                                 void* stream) {
+    if (!c) return PW_ERR_INVALID_ARG;
+    if (T < 0 || T > c->desc.max_tokens)
+        return fail(c, PW_ERR_INVALID_ARG, "T = %d outside [0, %d]", T, c->desc.max_tokens);
+    if (T > 0 && !logits) return fail(c, PW_ERR_INVALID_ARG, "null logits");
+    pw_status st = forward_args(c, x, logits, T, y);
+    if (st != PW_OK || T == 0) return st;
+    // the device state exists once pages do; ensure_device then only checks
+    // that the context's device is current
+    if (!c->dev) return fail(c, PW_ERR_STATE, "no device state: quantize first");
+    if ((st = ensure_device(c)) != PW_OK) return st;
+    // the scratch laid out for exactly this batch; the fewest K-splits the
+    // down product's partial outputs may need (one per pair) if the usual
+    // capacity does not fit
+    WsView v;
+    v.max_tokens = T;
+    v.nsplit = (int64_t)T * c->k > 2048 ? 1 : down_splits(c->F, c->d, 1, 1 << 30);
+    v.lay = workspace_layout(c->E, c->d, c->F, c->k, T, v.nsplit);
+    if (v.lay.total > noalloc_scratch_bytes()) {
+        v.nsplit = 1;
+        v.lay = workspace_layout(c->E, c->d, c->F, c->k, T, 1);
+    }
+    if (v.lay.total > noalloc_scratch_bytes())
+        return fail(c, PW_ERR_WORKSPACE, "a forward of %d tokens needs %llu bytes of scratch, the static scratch "
+                    "holds %llu", T, (unsigned long long)v.lay.total,
+                    (unsigned long long)noalloc_scratch_bytes());
+    void* p = nullptr;
+    if (noalloc_scratch(c->device, &p) != hipSuccess || !p)
+        return fail(c, PW_ERR_HIP, "hipGetSymbolAddress of the static scratch failed on device %d", c->device);
+    v.base = static_cast<uint8_t*>(p);
+    return forward_core(c, v, x, logits, T, y, static_cast<hipStream_t>(stream), true);
 }
 
 pw_status pw_get_page_table(const pw_ctx* c, pw_page_entry* out) {

@@ -200,6 +200,10 @@ hipError_t launch_swap_in(const SwapState& st, const int32_t* act, const int32_t
                           uint64_t slot_bytes, hipStream_t s);
 hipError_t launch_swap_invalidate(const SwapState& st, const int32_t* list, int n, hipStream_t s);
 
+// ---- static scratch of the allocation-free forward (noalloc.hip) ----
+uint64_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(int device, void** out);   // the device's copy; device must be current
+
 // ---- host allocator (alloc.cpp) ----
 pw_status solve_allocation(int E, const uint64_t* W, const double* p, const double* L,
                            uint64_t B, uint8_t* bits_out, std::string* err);

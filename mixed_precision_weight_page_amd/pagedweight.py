@@ -69,6 +69,7 @@ _SIGNATURES = {
     "pw_quantize_experts": (ctypes.c_int, [_P, _P, _P]),
     "pw_set_budget": (ctypes.c_int, [_P, ctypes.c_uint64, _P, _P, _P, _P]),
     "pw_moe_forward": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P]),
+    "pw_moe_forward_noalloc": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P]),
     "pw_route": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "pw_get_page_table": (ctypes.c_int, [_P, ctypes.POINTER(PageEntry)]),
     "pw_get_loss_table": (ctypes.c_int, [_P, _P, _P]),
@@ -332,6 +333,20 @@ class PagedMoELayer:
         _check(lib().pw_moe_forward(self._ctx, _dev(x, torch.bfloat16, "x"),
                                     _dev(logits, torch.float32, "logits"), T,
                                     _dev(y, torch.float32, "y"), _stream(stream)), self._ctx)
+        return y
+
+    def moe_forward_noalloc(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
+                            stream=None) -> torch.Tensor:
+        """pw_moe_forward_noalloc: the forward with the library's static
+        device scratch instead of the workspace (y is the caller's)."""
+        T = x.shape[0]
+        if x.dim() != 2 or x.shape[1] != self.d or tuple(logits.shape) != (T, self.E):
+            raise ValueError("x must be [T, d] and logits [T, E]")
+        if tuple(y.shape) != (T, self.d):
+            raise ValueError("y must be [T, d]")
+        _check(lib().pw_moe_forward_noalloc(self._ctx, _dev(x, torch.bfloat16, "x"),
+                                            _dev(logits, torch.float32, "logits"), T,
+                                            _dev(y, torch.float32, "y"), _stream(stream)), self._ctx)
         return y
 
     def route(self, logits: torch.Tensor, stream=None):

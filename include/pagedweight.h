@@ -237,15 +237,25 @@ pw_status pw_budget_decide(const pw_budget_policy* policy, uint64_t kv_used_byte
                            int32_t steps_since_change, int32_t* action, uint64_t* budget_out,
                            int32_t* pressure);
 
-/* One scheduler step on a layer: the decision from the layer's pages (their
- * bytes; the budget of the last scheduler move, or the bits of pages set by
- * pw_quantize_experts) and the steps since the last move; on INIT, SHRINK or
- * GROW it calls pw_set_budget with importance and loss (host, as there) on
- * stream. The step counter advances only on KEEP. A failed pw_set_budget
- * leaves pages, table and scheduler state unchanged and returns its status. */
+/* One scheduler step on a layer: the decision from the layer's pages (the
+ * bytes they span, pw_pool_used_bytes; the budget of the last scheduler
+ * move, or the bits of pages set by pw_quantize_experts) and the steps
+ * since the last move; on INIT, SHRINK or GROW it re-allocates as
+ * pw_set_budget does with importance and loss (host, as there) on stream,
+ * and places the new pages so that they span at most A bytes from the
+ * start of the pool: first fit when that stays within A, else every page is
+ * rewritten densely (compaction). Without pressure the pages then fit in A,
+ * so after a SHRINK the caller may hand the pool's bytes from
+ * pw_pool_used_bytes on to the KV cache. The step counter advances only on
+ * KEEP. A failed re-allocation leaves pages, table and scheduler state
+ * unchanged and returns its status. */
 pw_status pw_budget_step(pw_ctx* ctx, const pw_budget_policy* policy, uint64_t kv_used_bytes,
                          const double* importance, const double* loss, int32_t* action,
                          uint64_t* budget_out, int32_t* pressure, void* stream);
+
+/* Bytes of the pool the current pages span: the end of the highest page
+ * (0 without pages). The pool's bytes beyond it are unused. */
+uint64_t pw_pool_used_bytes(const pw_ctx* ctx);
 
 /* ---- Host tier: expert pages swapped out to CPU memory ----
  * PagedWeight page, section "Dynamic Paging": the router decides which

@@ -280,12 +280,22 @@ pw_status ensure_loss(pw_ctx* c, hipStream_t s) {
     return PW_OK;
 }
 
+// Bytes the pages span: the end of the highest page (0 without pages).
+uint64_t extent_of(const pw_ctx* c, const std::vector<pw_page_entry>& t) {
+    uint64_t end = 0;
+    for (int e = 0; e < c->E; ++e)
+        if (t[e].bits) end = std::max(end, t[e].offset + page_bytes(c, t[e].bits));
+    return end;
+}
+
 // Place the pages of the new allocation. Unchanged experts keep their
 // pages; changed experts go first-fit (largest first) into the space the
-// unchanged pages leave; if that fails every page is rewritten densely in
-// expert order. Returns the list of experts to pack.
+// unchanged pages leave, lowest addresses first. If that fails, or leaves
+// the pages spanning more than max_extent bytes, every page is rewritten
+// densely in expert order (compaction: the pages then occupy the head of
+// the pool, exactly their total size). Returns the list of experts to pack.
 pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
-                std::vector<int32_t>& list) {
+                std::vector<int32_t>& list, uint64_t max_extent) {
     const int E = c->E;
     const bool fresh = !c->pages_valid || c->pages_gen != c->masters_gen;
     nt.assign(E, pw_page_entry{});
@@ -331,6 +341,7 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
             }
             if (!placed) { ok = false; break; }
         }
+        if (ok && extent_of(c, nt) > max_extent) ok = false;
     }
     if (!ok) {
         uint64_t at = 0;
@@ -352,10 +363,10 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
 
 // Quantize at the given bits: place, upload the new table (into the idle
 // device copy), pack the changed experts, then make the new table current.
-pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s) {
+pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s, uint64_t max_extent = UINT64_MAX) {
     std::vector<pw_page_entry> nt;
     std::vector<int32_t> list;
-    pw_status st = place(c, bits, nt, list);
+    pw_status st = place(c, bits, nt, list, max_extent);
     if (st != PW_OK) return st;
     if (list.empty()) return PW_OK;
     const int E = c->E;
@@ -640,8 +651,10 @@ pw_status pw_quantize_experts(pw_ctx* c, const uint8_t* bits, void* stream) {
     return PW_OK;
 }
 
-pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importance,
-                        const double* loss, uint8_t* bits_out, void* stream) {
+// pw_set_budget with an extent the placement keeps the pages within when it
+// can (the KV-pressure scheduler passes the bytes the KV cache leaves).
+static pw_status set_budget(pw_ctx* c, uint64_t budget_bits, const double* importance, const double* loss,
+                            uint8_t* bits_out, void* stream, uint64_t max_extent) {
     if (!c) return PW_ERR_INVALID_ARG;
     if (!importance) return fail(c, PW_ERR_INVALID_ARG, "importance is NULL");
     pw_status st = need_masters_pool(c);
@@ -661,12 +674,19 @@ pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importanc
     std::vector<uint8_t> bits(c->E);
     st = solve_allocation(c->E, W.data(), importance, L, budget_bits, bits.data(), &c->err);
     if (st != PW_OK) return st;
-    if ((st = apply_bits(c, bits.data(), s)) != PW_OK) return st;
+    if ((st = apply_bits(c, bits.data(), s, max_extent)) != PW_OK) return st;
     c->budget_now = budget_bits;
     c->steps_since_change = 0;
     if (bits_out) std::memcpy(bits_out, bits.data(), c->E);
     return PW_OK;
 }
+
+pw_status pw_set_budget(pw_ctx* c, uint64_t budget_bits, const double* importance,
+                        const double* loss, uint8_t* bits_out, void* stream) {
+    return set_budget(c, budget_bits, importance, loss, bits_out, stream, UINT64_MAX);
+}
+
+uint64_t pw_pool_used_bytes(const pw_ctx* c) { return c && c->pages_valid ? extent_of(c, c->table) : 0; }
 
 pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_used_bytes,
                          const double* importance, const double* loss, int32_t* action,
@@ -674,11 +694,9 @@ pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_
     if (!c) return PW_ERR_INVALID_ARG;
     if (!policy || !importance || !action || !budget_out || !pressure)
         return fail(c, PW_ERR_INVALID_ARG, "null policy, importance or output pointer");
-    uint64_t pool_now = UINT64_MAX;
-    if (c->pages_valid) {
-        pool_now = 0;
-        for (int e = 0; e < c->E; ++e) pool_now += c->table[e].nbytes;
-    }
+    // the pool's size for the decision is the span of its pages (a page
+    // above the memory the KV cache leaves overlaps it, holes or not)
+    const uint64_t pool_now = c->pages_valid ? extent_of(c, c->table) : UINT64_MAX;
     std::vector<uint64_t> W(c->E, c->We);
     int32_t act = PW_BUDGET_KEEP, press = 0;
     uint64_t target = 0;
@@ -686,7 +704,12 @@ pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_
                                     c->steps_since_change, &act, &target, &press);
     if (st != PW_OK) return fail(c, st, "invalid budget policy");
     if (act != PW_BUDGET_KEEP) {
-        if ((st = pw_set_budget(c, target, importance, loss, nullptr, stream)) != PW_OK) return st;
+        // the new pages stay within the memory the KV cache leaves (compacted
+        // if first-fit placement would reach above it)
+        uint64_t avail = 0;
+        if (policy->memory_bytes > kv_used_bytes && policy->memory_bytes - kv_used_bytes > policy->reserve_bytes)
+            avail = policy->memory_bytes - kv_used_bytes - policy->reserve_bytes;
+        if ((st = set_budget(c, target, importance, loss, nullptr, stream, avail)) != PW_OK) return st;
     } else {
         c->steps_since_change++;
     }

@@ -79,6 +79,7 @@ _SIGNATURES = {
     "pw_budget_decide": (ctypes.c_int, [ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, ctypes.c_int32, _P,
                                         ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, _P, _P, _P]),
     "pw_budget_step": (ctypes.c_int, [_P, ctypes.POINTER(BudgetPolicy), ctypes.c_uint64, _P, _P, _P, _P, _P, _P]),
+    "pw_pool_used_bytes": (ctypes.c_uint64, [_P]),
     "pw_bind_host_tier": (ctypes.c_int, [_P, _P, ctypes.c_uint64]),
     "pw_get_residency": (ctypes.c_int, [_P, _P, _P, _P]),
     "pw_profile": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -271,6 +272,10 @@ class PagedMoELayer:
             raise ValueError("host tier must be a contiguous pinned uint8 CPU tensor")
         _check(lib().pw_bind_host_tier(self._ctx, host.data_ptr(), host.numel()), self._ctx)
         self._keep["host"] = host
+
+    def pool_used_bytes(self) -> int:
+        """pw_pool_used_bytes: bytes of the pool the pages span (from its start)."""
+        return int(lib().pw_pool_used_bytes(self._ctx))
 
     def slot_bytes(self) -> int:
         """Bytes of one page slot of the host tier's device cache (an 8-bit page)."""

@@ -297,8 +297,10 @@ def test_budget_scheduler_follows_a_kv_trace():
     """The KV-pressure scheduler (reading in include/pagedweight.h) on a
     layer with fp16 masters over 48 decode steps of a synthetic KV-cache
     trace: each step's action and budget equal the oracle's decision from
-    the oracle's own state; after every move the allocation (Eq. 1) and the
-    pages are the oracle's and the pool fits in the memory left."""
+    the oracle's own state (the pool's size being the bytes its pages span);
+    after every move the allocation (Eq. 1) and the pages are the oracle's,
+    and without pressure the pages span at most the memory the KV cache
+    leaves, so the pool's tail from pw_pool_used_bytes on is free for it."""
     wl = SMALL_DYN
     masters = synth.expert_weights(wl)
     layer, pool = make_layer(wl, masters, max_tokens=wl.T)
@@ -311,6 +313,7 @@ def test_budget_scheduler_follows_a_kv_trace():
     o_pool = o_budget = None
     o_since = 0
     seen = set()
+    shrinks_checked = 0
     for t, kv in enumerate(trace):
         got = layer.budget_step(memory, reserve, h, n, kv, p)
         want = osched.decide(memory, reserve, h, n, kv, W, o_pool, o_budget, o_since)
@@ -322,17 +325,57 @@ def test_budget_scheduler_follows_a_kv_trace():
             table = layer.get_page_table()
             bits = [int(e["bits"]) for e in table]
             assert bits == list(bits_want), t
-            o_pool, o_budget, o_since = osched.pool_nbytes(W, bits), B, 0
-            assert sum(int(e["nbytes"]) for e in table) == o_pool
+            assert sum(int(e["nbytes"]) for e in table) == osched.pool_nbytes(W, bits)
+            used = layer.pool_used_bytes()
+            assert used == max(e["offset"] + e["nbytes"] for e in table)
             if not pressure:
-                assert o_pool <= memory - kv - reserve
+                assert used <= memory - kv - reserve, (t, used, memory - kv - reserve)
+                if action == osched.SHRINK:
+                    shrinks_checked += 1
+            o_pool, o_budget, o_since = used, B, 0
             check_pages(layer, pool, masters, bits, rows_per_matrix=2)
         else:
             o_since += 1
     assert {osched.INIT, osched.SHRINK, osched.GROW, osched.KEEP} <= seen, seen
+    assert shrinks_checked > 0
     x, logits = synth.tokens(wl)
     y = layer.moe_forward(x.cuda(), logits.cuda())
     compare_y(y, oracle_y(x, logits, wl, masters, bits), "after the KV trace")
+
+
+def test_shrink_compacts_pages_below_the_kv_cache():
+    """Importance rising with the expert index keeps the last expert's page,
+    at the top of the pool, at 8 bits when the KV cache grows: first-fit
+    placement of the shrunk pages would leave the pool spanning its whole
+    all-8-bit size, above the memory left, so the scheduler rewrites the
+    pages densely; they then span exactly their total size, within the
+    memory left, bit-exact, and the layer's output is the oracle's."""
+    wl = SMALL_DYN
+    masters = synth.expert_weights(wl)
+    layer, pool = make_layer(wl, masters, max_tokens=wl.T)
+    p = synth.importance(wl)[::-1].copy()      # the last expert is the most important
+    W = [wl.W_e] * wl.E
+    pool8 = osched.pool_nbytes(W, [8] * wl.E)
+    memory, reserve = pool8 + pool8 // 8, pool8 // 16
+    act, B, pressure = layer.budget_step(memory, reserve, 0.05, 0, 0, p)
+    assert act == osched.INIT and not pressure
+    before = layer.get_page_table()
+    assert [e["bits"] for e in before] == [8] * wl.E
+    last_off = before[-1]["offset"]
+    kv = pool8 // 2
+    act, B, pressure = layer.budget_step(memory, reserve, 0.05, 0, kv, p)
+    assert act == osched.SHRINK and not pressure
+    table = layer.get_page_table()
+    bits = [e["bits"] for e in table]
+    assert bits[-1] == 8 and min(bits) < 8
+    used = layer.pool_used_bytes()
+    total = sum(e["nbytes"] for e in table)
+    assert used == total <= memory - kv - reserve < last_off + table[-1]["nbytes"]
+    assert table[-1]["offset"] < last_off    # the unchanged page moved down
+    check_pages(layer, pool, masters, bits)
+    x, logits = synth.tokens(wl)
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, bits), "after compaction")
 
 
 def test_mostly_zero_codes_keep_precision():

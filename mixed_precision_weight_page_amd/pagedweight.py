@@ -15,7 +15,10 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedweight.so")
+# PW_LIBRARY may name another build of the same library (the tests' host
+# sanitizer build); by default the one built in-tree
+_LIB_PATH = os.environ.get("PW_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libpagedweight.so")
 _lib = None
 
 PW_MASTER_F32 = 0

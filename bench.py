@@ -1,11 +1,14 @@
 """Throughput of the per-expert mixed-precision MoE expert layer on one MI355X.
 
-Default workload (one JSON line): decode on the coarse MoE layer, E=8,
+Default run (one JSON line): decode on the coarse MoE layer, E=8,
 d_model=4096, d_ff=14336 SwiGLU, top-2, 16 tokens per step, bit-widths from
 the exact allocator at an average of 4.5 bits/weight with Zipf(1.0)
 importance. A step is one pw_moe_forward: route, group, fused dequant +
 gate/up + SwiGLU, dequant + down, combine. Batches of 1 and 4 tokens are
-reported in "sweep".
+reported in "sweep"; the other workloads (the fine-grained decode layer, the
+same layer with importance-skewed routing, prefill on the matrix cores, the
+dynamic re-precision schedule) in "workloads", each with its tokens/s and
+its dominant kernels' fraction of the roofline.
 
 Inputs are resident in HBM before timing starts. Each step reads a
 different copy of the packed pool (several contexts over the same masters)
@@ -14,9 +17,10 @@ so that weights come from HBM, not from the 256 MB Infinity Cache.
 roofline: the gate/up kernel (two thirds of the packed bytes), algorithmic
 bytes = packed W1 + W3 bytes of the experts the step routes to, divided by
 the kernel's mean duration from HIP events on the forward's stream.
-cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample.
+cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample, on
+all host cores and single-threaded.
 
-Other workloads: --workload decode_fine | prefill | dynamic | kvtrace | swap | tiny.
+One workload alone: --workload decode_fine | skewed | prefill | dynamic | kvtrace | swap | tiny.
 """
 from __future__ import annotations
 
@@ -45,11 +49,14 @@ def parse():
     # started below them (decode 97k against 109k tokens/s)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode_coarse",
-                    choices=["decode_coarse", "decode_fine", "prefill", "dynamic", "kvtrace", "swap", "tiny"])
+                    choices=["decode_coarse", "decode_fine", "skewed", "prefill", "dynamic", "kvtrace", "swap",
+                             "tiny"])
     ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")
     ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="default run: only the decode_coarse line (no other workloads)")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-kernel events (no roofline)")
     ap.add_argument("--event-every-step", action="store_true",
@@ -87,17 +94,20 @@ def traffic_from_profiles(workload: str, T: int):
 
 
 class Bench:
-    def __init__(self, wl, max_tokens, npools, log):
+    def __init__(self, wl, max_tokens, npools, log, bias=None):
+        """bias: added to every batch's logits (None: N(0, 1) logits as the
+        workload specifies)."""
         import torch
 
         import synth
         from mixed_precision_weight_page_amd import PagedMoELayer
         self.torch = torch
         self.wl = wl
+        self.bias = bias
         t0 = time.time()
         self.masters = synth.expert_weights(wl, device="cuda", seed=0)
         torch.cuda.synchronize()
-        log(f"masters on device ({time.time() - t0:.1f}s)")
+        log(f"{wl.name}: masters on device ({time.time() - t0:.1f}s)")
         self.layers, self.pools = [], []
         bits = None
         for i in range(npools):
@@ -117,20 +127,32 @@ class Bench:
             self.pools.append(pool)
         torch.cuda.synchronize()
         self.bits = bits
-        log(f"bits {bits} ({time.time() - t0:.1f}s)")
+        log(f"{wl.name}: bits {bits} ({time.time() - t0:.1f}s)")
+
+    def release(self):
+        self.layers, self.pools, self.masters = [], [], None
+        self.torch.cuda.empty_cache()
 
     def batches(self, T, n, seed=1):
         import synth
-        return [synth.tokens(self.wl, T=T, device="cuda", seed=seed, step=i) for i in range(n)]
+        out = []
+        for i in range(n):
+            x, lg = synth.tokens(self.wl, T=T, device="cuda", seed=seed, step=i)
+            if self.bias is not None:
+                lg = (lg + self.bias).contiguous()
+            out.append((x, lg))
+        return out
 
     def routed_bytes(self, logits):
-        """Packed bytes (W1+W3, W2) of the experts the batch routes to."""
+        """Packed bytes (W1+W3, W2) of the experts the batch routes to, and
+        the most tokens any expert receives."""
         _, _, counts = self.layers[0].route(logits)
-        active = (counts.cpu() > 0).nonzero().flatten().tolist()
+        c = counts.cpu()
+        active = (c > 0).nonzero().flatten().tolist()
         wl = self.wl
         gu = sum(2 * wl.F * wl.d * self.bits[e] // 8 for e in active)
         dn = sum(wl.d * wl.F * self.bits[e] // 8 for e in active)
-        return gu, dn, len(active)
+        return gu, dn, len(active), int(c.max())
 
     def run(self, T, steps, warmup, profile=2, sample=False):
         """profile: kernel mask timed with events; sample: events only on the
@@ -139,12 +161,13 @@ class Bench:
         nb = 8
         batches = self.batches(T, nb)
         ys = [torch.empty((T, self.wl.d), dtype=torch.float32, device="cuda") for _ in range(nb)]
-        bytes_gu, bytes_dn, n_act = [], [], []
+        bytes_gu, bytes_dn, n_act, tmax = [], [], [], []
         for x, lg in batches:
-            a, b, c = self.routed_bytes(lg)
+            a, b, c, m = self.routed_bytes(lg)
             bytes_gu.append(a)
             bytes_dn.append(b)
             n_act.append(c)
+            tmax.append(m)
         L = len(self.layers)
         for i in range(warmup):
             x, lg = batches[i % nb]
@@ -177,8 +200,9 @@ class Bench:
         gu_timed = sum(bytes_gu[i % nb] for i in range(steps) if not sample or i % L == 0)
         tot_dn = sum(bytes_dn[i % nb] for i in range(steps))
         return dict(T=T, steps=steps, timed_forwards=timed, bytes_gu_timed=gu_timed, elapsed=elapsed, prof=prof,
-                    bytes_gu=tot_gu,
-                    bytes_dn=tot_dn, mean_active=sum(n_act[i % nb] for i in range(steps)) / steps)
+                    bytes_gu=tot_gu, bytes_dn=tot_dn,
+                    mean_active=sum(n_act[i % nb] for i in range(steps)) / steps,
+                    max_tokens_per_expert=max(tmax))
 
 
 def cpu_model() -> str:
@@ -192,25 +216,34 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
-    """Oracle forward (float64, from the fp32 masters) on T-token batches of
-    the same layer, one after another until min_seconds of oracle time or
-    max_batches: each batch quantizes its routed experts and runs the
-    forward."""
+def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4, single_experts=2):
+    """The oracle (float64, from the fp32 masters) on T-token batches of the
+    same layer: each batch quantizes its routed experts and runs the forward.
+
+    All host threads (up to 16, the machine's CPU share per GPU): whole batches
+    one after another until min_seconds or max_batches. One thread: the
+    first batch's first `single_experts` routed experts only (each
+    quantized, then the SwiGLU of its tokens), scaled to all the batch's
+    routed experts (the oracle's cost is linear in them), labelled
+    extrapolated."""
     import torch
 
     from oracle import moe
-    threads = min(16, os.cpu_count() or 1)
-    torch.set_num_threads(threads)
+    nproc = os.cpu_count() or 1
     batches = bench.batches(T, max_batches, seed=99)
-    total, done, n_exp, t_copy, y0 = 0.0, 0, [], 0.0, None
+
+    def host_experts(experts):
+        return [m[experts].cpu() for m in bench.masters]   # not timed
+
+    # all threads: the oracle's whole forward
+    threads = min(16, nproc)
+    torch.set_num_threads(threads)
+    total, done, n_exp, y0 = 0.0, 0, [], None
     for x, lg in batches:
         x, lg = x.cpu(), lg.cpu()
         ids, _ = moe.route(lg, bench.wl.k)
         experts = sorted(set(ids.flatten().tolist()))
-        t0 = time.time()
-        w = [m[experts].cpu() for m in bench.masters]   # only the routed experts
-        t_copy += time.time() - t0
+        w = host_experts(experts)
         remap = {e: i for i, e in enumerate(experts)}
         t0 = time.time()
         getter = moe.quantized_experts(*w, [bench.bits[e] for e in experts])
@@ -221,11 +254,89 @@ def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
         y0 = y if y0 is None else y0
         if total >= min_seconds:
             break
-    log(f"oracle: {done} batches of {T} tokens in {total:.1f}s (+{t_copy:.1f}s host copy)")
-    return {"value": T * done / total, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+    log(f"oracle, {threads} threads: {done} batches of {T} tokens in {total:.1f}s")
+    # one thread: part of the first batch
+    torch.set_num_threads(1)
+    x, lg = batches[0]
+    x64 = x.cpu().double()
+    ids, _ = moe.route(lg.cpu(), bench.wl.k)
+    experts = sorted(set(ids.flatten().tolist()))
+    some = experts[:single_experts]
+    w = host_experts(some)
+    t0 = time.time()
+    getter = moe.quantized_experts(*w, [bench.bits[e] for e in some])
+    for i, e in enumerate(some):
+        rows = (ids == e).nonzero(as_tuple=True)[0]
+        moe.expert_ffn(x64[rows], *getter(i))
+    t1 = (time.time() - t0) * len(experts) / len(some)
+    torch.set_num_threads(threads)
+    log(f"oracle, 1 thread: {len(some)} of {len(experts)} experts, batch extrapolated to {t1:.1f}s")
+    return {"value": T * done / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": nproc, "cpu_model": cpu_model(),
             "sample": f"{done} batch(es) of {T} tokens of the same layer, each quantizing its routed experts "
                       f"({', '.join(map(str, n_exp))}) from fp32 masters and running the float64 forward "
-                      f"(host copies of the masters excluded); {cpu_model()}"}, y0
+                      f"(host copies of the masters excluded), {threads} threads; {cpu_model()}, nproc {nproc}",
+            "single_thread": {"value": T / t1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"extrapolated: {len(some)} of the {len(experts)} experts one batch of {T} "
+                                        f"tokens routes to, each quantized and run on its tokens, single-threaded, "
+                                        f"scaled to all {len(experts)}"}}, y0
+
+
+HBM = "GB/s"
+
+
+def kernel_line(name, ms, work, unit):
+    """Achieved rate of a kernel class and its fraction of the roofline:
+    work in bytes (unit GB/s) or flops (unit TFLOP/s) per launch."""
+    if not ms:
+        return {f"{name}_us": None}
+    if unit == HBM:
+        rate = work / (ms * 1e-3) / 1e9
+        peak = HBM_PEAK_GBPS
+    else:
+        rate = work / (ms * 1e-3) / 1e12
+        peak = MFMA_F16_PEAK_TFLOPS
+    return {f"{name}_us": 1e3 * ms, f"{name}_{'GBps' if unit == HBM else 'TFLOPs'}": rate,
+            f"{name}_frac": rate / peak}
+
+
+def measure(wl, T, args, log, npools, bias=None, bench=None):
+    """One workload's summary: tokens/s over the timed steps (events on the
+    gate/up kernel of the first rotated context), then a second pass timing
+    every kernel class for the breakdown and the down kernel's rate."""
+    b = bench or Bench(wl, T, npools, log, bias)
+    r = b.run(T, args.steps, args.warmup, profile=2, sample=True)
+    r_all = b.run(T, args.steps, 0, profile=15)
+    out = {"tokens_per_s": T * r["steps"] / r["elapsed"], "ms_per_step": 1e3 * r["elapsed"] / r["steps"],
+           "tokens": T, "bits_per_weight": sum(b.bits) / len(b.bits), "mean_active_experts": r["mean_active"],
+           "max_tokens_per_expert": r["max_tokens_per_expert"]}
+    gu_bytes = r["bytes_gu_timed"] / max(1, r["timed_forwards"])
+    dn_bytes = r_all["bytes_dn"] / r_all["steps"]
+    if wl.name == "prefill":
+        flops = 2.0 * T * wl.k * wl.d * wl.F           # per matrix: 2 flops per weight per pair
+        out.update(kernel_line("gate_up", r["prof"]["gate_up_ms"], 2 * flops, "TFLOP/s"))
+        out.update(kernel_line("down", r_all["prof"]["down_ms"], flops, "TFLOP/s"))
+    else:
+        out.update(kernel_line("gate_up", r["prof"]["gate_up_ms"], gu_bytes, HBM))
+        out.update(kernel_line("down", r_all["prof"]["down_ms"], dn_bytes, HBM))
+    out["route_us"] = 1e3 * r_all["prof"]["route_ms"]
+    out["combine_us"] = 1e3 * r_all["prof"]["combine_ms"]
+    out["packed_weight_GBps"] = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
+    out["packed_weight_frac_of_hbm"] = out["packed_weight_GBps"] / HBM_PEAK_GBPS
+    if bench is None:
+        b.release()
+    return out, r, r_all, gu_bytes
+
+
+def skew_bias(wl):
+    """Logits bias log p_e: experts routed in proportion to their importance
+    (Zipf), so the most important experts take most of the tokens."""
+    import numpy as np
+    import torch
+
+    import synth
+    p = np.asarray(synth.importance(wl), dtype=np.float64)
+    return torch.tensor(np.log(p), dtype=torch.float32, device="cuda")
 
 
 def main():
@@ -254,14 +365,17 @@ def main():
         return bench_kvtrace(args, synth.WORKLOADS["dynamic"], log)
     if args.workload == "swap":
         return bench_swap(args, synth.WORKLOADS["decode_fine"], log)
-    wl = synth.WORKLOADS[args.workload]
     if args.workload == "dynamic":
-        return bench_dynamic(args, wl, log)
+        print(json.dumps(bench_dynamic(args, synth.WORKLOADS["dynamic"], log)), flush=True)
+        return
+    skewed = args.workload == "skewed"
+    wl = synth.WORKLOADS["decode_fine" if skewed else args.workload]
     T = args.tokens or wl.T
-    sweep_T = [t for t in synth.DECODE_COARSE_BATCHES if t != T] if args.workload == "decode_coarse" else []
+    default_run = args.workload == "decode_coarse"
+    sweep_T = [t for t in synth.DECODE_COARSE_BATCHES if t != T] if default_run else []
     max_tokens = max([T] + sweep_T)
     npools = args.pools if args.workload != "prefill" else 2
-    b = Bench(wl, max_tokens, npools, log)
+    b = Bench(wl, max_tokens, npools, log, skew_bias(wl) if skewed else None)
     # timed region: events only on the gate/up kernel (the roofline kernel);
     # a second pass of the same steps times every kernel for the breakdown
     sample = not args.event_every_step
@@ -291,6 +405,7 @@ def main():
                 "bytes_per_launch": gu_bytes,
                 "launches_timed": r["timed_forwards"],
                 "launch_ms": gu_ms}
+    name = "decode_fine, importance-skewed routing" if skewed else wl.name
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -304,7 +419,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: E={wl.E}, d_model={wl.d}, d_ff={wl.F} SwiGLU, "
+        "config": {"workload": f"{name}: E={wl.E}, d_model={wl.d}, d_ff={wl.F} SwiGLU, "
                                f"top-{wl.k}, {T} tokens per step, "
                                + (f"avg {wl.budget_avg} bits/weight" if wl.budget_avg else f"bits {list(wl.bits)}"),
                    "E": wl.E, "d_model": wl.d, "d_ff": wl.F, "top_k": wl.k, "tokens": T,
@@ -316,6 +431,7 @@ def main():
         "down_GBps": (r_all["bytes_dn"] / r_all["steps"] / (r_all["prof"]["down_ms"] * 1e-3) / 1e9
                       if r_all and r_all["prof"]["down_ms"] > 0 else None),
         "mean_active_experts": r["mean_active"],
+        "max_tokens_per_expert": r["max_tokens_per_expert"],
         "roofline": roof,
     }
     if not args.no_sweep and sweep_T:
@@ -329,6 +445,8 @@ def main():
                             "gate_up_GBps": (rs["bytes_gu_timed"] / rs["timed_forwards"] / (g * 1e-3) / 1e9
                                              if g and rs["timed_forwards"] else None),
                             "mean_active_experts": rs["mean_active"]}
+            if sw[f"T={t}"]["gate_up_GBps"]:
+                sw[f"T={t}"]["gate_up_frac"] = sw[f"T={t}"]["gate_up_GBps"] / HBM_PEAK_GBPS
         out["sweep"] = sw
     if not args.no_cpu_baseline:
         sample_T = T if args.workload != "prefill" else 64
@@ -336,6 +454,27 @@ def main():
         if args.workload == "prefill":
             cb["sample"] += " (64 of the 4096 tokens)"
         out["cpu_baseline"] = cb
+    b.release()
+    if default_run and not args.no_workloads:
+        # the other configurations, each on its own layer (one at a time on
+        # the device)
+        wls = {}
+        for key, w, bias in (("decode_fine_T64", synth.WORKLOADS["decode_fine"], None),
+                             ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew"),
+                             ("prefill_T4096", synth.WORKLOADS["prefill"], None)):
+            t0 = time.time()
+            res, _, _, _ = measure(w, w.T, args, log, 2 if w.name == "prefill" else args.pools,
+                                   skew_bias(w) if bias else None)
+            if bias:
+                res["routing"] = "logits + log p_e (Zipf 1.1 importance)"
+            wls[key] = res
+            log(f"{key}: {res['tokens_per_s']:.0f} tokens/s ({time.time() - t0:.1f}s)")
+        t0 = time.time()
+        dyn = bench_dynamic(args, synth.WORKLOADS["dynamic"], log, cpu=False)
+        wls["dynamic"] = {k: dyn[k] for k in ("value", "ms_per_step", "requant_GBps", "requant_s_total")}
+        wls["dynamic"]["tokens_per_s"] = wls["dynamic"].pop("value")
+        log(f"dynamic: {wls['dynamic']['tokens_per_s']:.0f} tokens/s ({time.time() - t0:.1f}s)")
+        out["workloads"] = wls
     print(json.dumps(out), flush=True)
 
 
@@ -343,7 +482,7 @@ def cpu_requant_baseline(masters, wl, p, L, log, min_seconds=10.0):
     """The oracle's re-precision on the host: Eq. 1 solved for the first
     budget of the schedule (the library's measured loss table as input),
     then experts re-quantized from the fp16 masters into pages (max |w|,
-    scale, codes, packed tiled page), alternating 8/4/3 bits, until
+    scale, codes, packed page), alternating 8/4/3 bits, until
     min_seconds; GB/s counts master bytes read plus page bytes written, as
     requant_GBps does."""
     import torch
@@ -374,7 +513,7 @@ def cpu_requant_baseline(masters, wl, p, L, log, min_seconds=10.0):
                       f"per second, as requant_GBps); {cpu_model()}"}
 
 
-def bench_dynamic(args, wl, log):
+def bench_dynamic(args, wl, log, cpu=True):
     """40 decode steps of 64 tokens; the budget moves every 8 steps through
     avg 8, 6, 4, 3.5, 5 bits (re-quantization from the fp16 masters between
     steps). Reports end-to-end tokens/s and the requantize rate."""
@@ -419,9 +558,11 @@ def bench_dynamic(args, wl, log):
                                   "masters, budget avg 8->6->4->3.5->5 bits every 8 steps"},
            "requant_GBps": req_bytes / t_req / 1e9 if t_req else None,
            "requant_s_total": t_req}
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_requant_baseline(masters, wl, p, layer.get_loss_table(), log)
-    print(json.dumps(out), flush=True)
+    del layer, masters, batches
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_kvtrace(args, wl, log):

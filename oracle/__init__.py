@@ -18,8 +18,11 @@ Plain, slow and written to be checked by eye against the pages:
              hysteresis.
 * ``swap``   the host tier of section "Dynamic Paging": which expert pages
              a device cache of page slots holds, pass by pass.
+* ``bitplane`` the PagedMoE page's prefix-compatible bitplane layout (its
+             Abstract), read as a tree codebook over Eq. 2's 8-bit codes:
+             depth-b weights, pages of b bitplanes, the loss table.
 
 All floating-point arithmetic is float64 except where a rounding step is part
 of the definition (the fp32 scale, the bf16 activations).
 """
-from . import quant, alloc, moe, sched, swap  # noqa: F401
+from . import quant, alloc, moe, sched, swap, bitplane  # noqa: F401

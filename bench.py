@@ -20,7 +20,7 @@ the kernel's mean duration from HIP events on the forward's stream.
 cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample, on
 all host cores and single-threaded.
 
-One workload alone: --workload decode_fine | skewed | prefill | dynamic | kvtrace | swap | tiny.
+One workload alone: --workload decode_fine | skewed | bitplane | prefill | dynamic | kvtrace | swap | tiny.
 """
 from __future__ import annotations
 
@@ -49,8 +49,8 @@ def parse():
     # started below them (decode 97k against 109k tokens/s)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode_coarse",
-                    choices=["decode_coarse", "decode_fine", "skewed", "prefill", "dynamic", "kvtrace", "swap",
-                             "tiny"])
+                    choices=["decode_coarse", "decode_fine", "skewed", "bitplane", "prefill", "dynamic", "kvtrace",
+                             "swap", "tiny"])
     ap.add_argument("--tokens", type=int, default=None, help="batch for the main line")
     ap.add_argument("--pools", type=int, default=4, help="rotating packed pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,9 +94,9 @@ def traffic_from_profiles(workload: str, T: int):
 
 
 class Bench:
-    def __init__(self, wl, max_tokens, npools, log, bias=None):
+    def __init__(self, wl, max_tokens, npools, log, bias=None, layout="eq2"):
         """bias: added to every batch's logits (None: N(0, 1) logits as the
-        workload specifies)."""
+        workload specifies); layout: "eq2" or "bitplane" pages."""
         import torch
 
         import synth
@@ -112,7 +112,7 @@ class Bench:
         bits = None
         for i in range(npools):
             layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=max_tokens,
-                                  renorm=wl.renorm, master_dtype=wl.master)
+                                  renorm=wl.renorm, master_dtype=wl.master, layout=layout)
             layer.bind_masters(*self.masters)
             pool = layer.alloc_pool(layer.pool_bytes_for_bits([8] * wl.E))
             layer.alloc_workspace()
@@ -300,11 +300,11 @@ def kernel_line(name, ms, work, unit):
             f"{name}_frac": rate / peak}
 
 
-def measure(wl, T, args, log, npools, bias=None, bench=None):
+def measure(wl, T, args, log, npools, bias=None, bench=None, layout="eq2"):
     """One workload's summary: tokens/s over the timed steps (events on the
     gate/up kernel of the first rotated context), then a second pass timing
     every kernel class for the breakdown and the down kernel's rate."""
-    b = bench or Bench(wl, T, npools, log, bias)
+    b = bench or Bench(wl, T, npools, log, bias, layout)
     r = b.run(T, args.steps, args.warmup, profile=2, sample=True)
     r_all = b.run(T, args.steps, 0, profile=15)
     out = {"tokens_per_s": T * r["steps"] / r["elapsed"], "ms_per_step": 1e3 * r["elapsed"] / r["steps"],
@@ -323,9 +323,39 @@ def measure(wl, T, args, log, npools, bias=None, bench=None):
     out["combine_us"] = 1e3 * r_all["prof"]["combine_ms"]
     out["packed_weight_GBps"] = (r["bytes_gu"] + r["bytes_dn"]) / r["elapsed"] / 1e9
     out["packed_weight_frac_of_hbm"] = out["packed_weight_GBps"] / HBM_PEAK_GBPS
+    if layout == "bitplane":
+        out["layout"] = "bitplane pages (depths from Eq. 1 over 3, 4, 8)"
+        out.update(plane_reprecision(b, log))
     if bench is None:
         b.release()
     return out, r, r_all, gu_bytes
+
+
+def plane_reprecision(b, log, reps=5):
+    """Re-precision of a bitplane layer by plane count: every expert's depth
+    halved (the pages lose their last planes in place: a table upload, no
+    master reads), then restored (the missing planes written from the
+    masters where the pages were). Wall time per change, synchronised."""
+    import torch
+    layer = b.layers[0]
+    full = list(b.bits)
+    low = [max(1, x // 2) for x in full]
+    t_low = t_high = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        layer.quantize_experts(low)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        layer.quantize_experts(full)
+        torch.cuda.synchronize()
+        t_high += time.perf_counter() - t1
+        t_low += t1 - t0
+    wl = b.wl
+    written = sum((f - l) for f, l in zip(full, low)) * wl.W_e / 8
+    log(f"bitplane re-precision: lower {1e3 * t_low / reps:.3f} ms, raise {1e3 * t_high / reps:.3f} ms")
+    return {"lower_depths_ms": 1e3 * t_low / reps, "raise_depths_ms": 1e3 * t_high / reps,
+            "raise_plane_bytes_written": written,
+            "raise_GBps": written / (t_high / reps) / 1e9 if t_high else None}
 
 
 def skew_bias(wl):
@@ -367,6 +397,17 @@ def main():
         return bench_swap(args, synth.WORKLOADS["decode_fine"], log)
     if args.workload == "dynamic":
         print(json.dumps(bench_dynamic(args, synth.WORKLOADS["dynamic"], log)), flush=True)
+        return
+    if args.workload == "bitplane":
+        wl = synth.WORKLOADS["decode_fine"]
+        res, _, _, _ = measure(wl, wl.T, args, log, args.pools, layout="bitplane")
+        print(json.dumps({"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                          "data": "synthetic",
+                          "config": {"workload": "decode_fine layer (E=128, d_model=2048, d_ff=768, top-8, 64 "
+                                                 "tokens) in bitplane pages, avg 4 bits/weight"},
+                          **res}), flush=True)
         return
     skewed = args.workload == "skewed"
     wl = synth.WORKLOADS["decode_fine" if skewed else args.workload]
@@ -459,12 +500,13 @@ def main():
         # the other configurations, each on its own layer (one at a time on
         # the device)
         wls = {}
-        for key, w, bias in (("decode_fine_T64", synth.WORKLOADS["decode_fine"], None),
-                             ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew"),
-                             ("prefill_T4096", synth.WORKLOADS["prefill"], None)):
+        for key, w, bias, layout in (("decode_fine_T64", synth.WORKLOADS["decode_fine"], None, "eq2"),
+                                     ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew", "eq2"),
+                                     ("decode_fine_bitplane_T64", synth.WORKLOADS["decode_fine"], None, "bitplane"),
+                                     ("prefill_T4096", synth.WORKLOADS["prefill"], None, "eq2")):
             t0 = time.time()
             res, _, _, _ = measure(w, w.T, args, log, 2 if w.name == "prefill" else args.pools,
-                                   skew_bias(w) if bias else None)
+                                   skew_bias(w) if bias else None, layout=layout)
             if bias:
                 res["routing"] = "logits + log p_e (Zipf 1.1 importance)"
             wls[key] = res

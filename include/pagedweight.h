@@ -55,6 +55,28 @@ typedef enum {
 
 typedef enum { PW_MASTER_F32 = 0, PW_MASTER_F16 = 1 } pw_master_dtype;
 
+/* Page layout of a layer.
+ * PW_LAYOUT_EQ2: pages of Eq. 2 codes at 3, 4 or 8 bits (the PagedWeight
+ *   page), the layout described at pw_quantize_experts.
+ * PW_LAYOUT_BITPLANE: the PagedMoE page's prefix-compatible layout (its
+ *   Abstract: one stored state per expert, a lower precision a prefix of a
+ *   higher one), read as a tree codebook over Eq. 2's 8-bit codes: with
+ *   s8 = max|w| / 127 (nearest fp32) and u8 = q8 + 128 Eq. 2's 8-bit code, a
+ *   weight at depth b in 1..8 is s8 ((2p + 1) 2^(7-b) - 128.5) for the prefix
+ *   p = u8 >> (8 - b) (the centre of the node it names; Eq. 2's 8-bit weight
+ *   at depth 8). Bitplane j holds bit 7 - j of every u8; a depth-b page is
+ *   planes 0 .. b-1 in order, each plane the W1, W3 and W2 bits (W_e / 8
+ *   bytes, every matrix in the tiles of pw_quantize_experts at 1 bit per
+ *   code: 256 bytes per 16 x 128 tile, lane l = 16 g + r holding the bits
+ *   of codes 32 g .. 32 g + 31 of row r as one little-endian word). The
+ *   "bits" of every call are depths; lowering a depth drops the page's last
+ *   planes in place without reading the masters, raising it writes only
+ *   the missing planes when the bytes after the page are free. The table's
+ *   scale is s8; the loss table holds depths 3, 4, 8 (the allocation of
+ *   pw_set_budget chooses among them); forwards use the streaming kernels
+ *   for every batch. */
+typedef enum { PW_LAYOUT_EQ2 = 0, PW_LAYOUT_BITPLANE = 1 } pw_layout;
+
 /* One MoE layer. W_e = 3 * d_model * d_ff weights per expert. */
 typedef struct {
     int32_t num_experts;   /* E                                                 */
@@ -65,6 +87,7 @@ typedef struct {
                               1: softmax renormalised over the k chosen         */
     int32_t max_tokens;    /* largest T passed to pw_moe_forward                */
     int32_t master_dtype;  /* pw_master_dtype of the bound masters              */
+    int32_t layout;        /* pw_layout of the pages                            */
 } pw_layer_desc;
 
 /* Host copy of one page-table entry. */

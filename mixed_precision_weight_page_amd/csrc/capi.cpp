@@ -104,7 +104,8 @@ pw_status fail(pw_ctx* c, pw_status s, const char* fmt, ...) {
     } while (0)
 
 // device block: per table [off u64 E][scale f32 E][bits i32 E][list i32 E]
-size_t table_bytes(int E) { return align_up((size_t)E * 20, kAlign); }
+// [first plane i32 E]
+size_t table_bytes(int E) { return align_up((size_t)E * 24, kAlign); }
 size_t dev_bytes(int E) { return 2 * table_bytes(E) + align_up((size_t)E * 4 + 16, kAlign) + (size_t)E * 24; }
 
 DevTable dev_table(pw_ctx* c, int which) {
@@ -117,6 +118,9 @@ DevTable dev_table(pw_ctx* c, int which) {
 }
 int32_t* dev_list(pw_ctx* c, int which) {
     return reinterpret_cast<int32_t*>(c->dev + which * table_bytes(c->E) + (size_t)c->E * 16);
+}
+int32_t* dev_first(pw_ctx* c, int which) {
+    return reinterpret_cast<int32_t*>(c->dev + which * table_bytes(c->E) + (size_t)c->E * 20);
 }
 uint32_t* dev_absmax(pw_ctx* c) { return reinterpret_cast<uint32_t*>(c->dev + 2 * table_bytes(c->E)); }
 uint32_t* dev_flags(pw_ctx* c) { return dev_absmax(c) + c->E; }
@@ -232,8 +236,16 @@ pw_status reset_swap(pw_ctx* c) {
     return PW_OK;
 }
 
-float scale_for(float m, int b) {
+// s = the fp32 value nearest m / qmax; bitplane pages use Eq. 2's 8-bit
+// scale s8 at every depth
+float scale_for(const pw_ctx* c, float m, int b) {
+    if (c->desc.layout == PW_LAYOUT_BITPLANE) b = 8;
     return m == 0.0f ? 0.0f : (float)((double)m / (double)qmax_of(b));
+}
+
+// bit-widths a page may have: {3, 4, 8} (Eq. 2), depths 1..8 (bitplane)
+bool bits_ok(const pw_ctx* c, int b) {
+    return c->desc.layout == PW_LAYOUT_BITPLANE ? (b >= 1 && b <= 8) : bits_index(b) >= 0;
 }
 
 uint64_t page_bytes(const pw_ctx* c, int b) { return align_up(c->We * (uint64_t)b / 8, kPageAlign); }
@@ -270,7 +282,8 @@ pw_status ensure_loss(pw_ctx* c, hipStream_t s) {
                     (unsigned long long)c->lay.total);
     const int f16 = c->desc.master_dtype == PW_MASTER_F16;
     HIP_TRY(c, launch_loss(c->w1, c->w3, c->w2, f16, c->E, c->M, dev_absmax(c),
-                           reinterpret_cast<double*>(c->ws + c->lay.partial), dev_loss(c), s));
+                           reinterpret_cast<double*>(c->ws + c->lay.partial), dev_loss(c),
+                           c->desc.layout == PW_LAYOUT_BITPLANE ? 1 : 0, s));
     HIP_TRY(c, hipEventSynchronize(c->upload_done));
     HIP_TRY(c, hipMemcpyAsync(c->host_stage, dev_loss(c), (size_t)c->E * 24, hipMemcpyDeviceToHost, s));
     HIP_TRY(c, hipStreamSynchronize(s));
@@ -288,33 +301,67 @@ uint64_t extent_of(const pw_ctx* c, const std::vector<pw_page_entry>& t) {
     return end;
 }
 
-// Place the pages of the new allocation. Unchanged experts keep their
-// pages; changed experts go first-fit (largest first) into the space the
-// unchanged pages leave, lowest addresses first. If that fails, or leaves
-// the pages spanning more than max_extent bytes, every page is rewritten
-// densely in expert order (compaction: the pages then occupy the head of
-// the pool, exactly their total size). Returns the list of experts to pack.
+bool bitplane(const pw_ctx* c) { return c->desc.layout == PW_LAYOUT_BITPLANE; }
+
+// Place the pages of the new allocation; `pack` receives (expert, first
+// plane to write) for every page that needs writing (Eq. 2 pages: always
+// from plane 0, i.e. the whole page). Unchanged experts keep their pages.
+// Eq. 2 pages whose width changes go first-fit (largest first) into the
+// space the kept pages leave, lowest addresses first. Bitplane pages whose
+// depth drops keep their place and lose their last planes (nothing is
+// written: a shallower page is a prefix of the deeper one); those whose
+// depth grows get their missing planes written after the ones they have
+// when the bytes there are free, else go first-fit like Eq. 2 pages and
+// are written whole. If placement fails, or leaves the pages spanning more
+// than max_extent bytes, every page is rewritten densely in expert order
+// (compaction: the pages then occupy the head of the pool, exactly their
+// total size).
 pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
-                std::vector<int32_t>& list, uint64_t max_extent) {
+                std::vector<std::pair<int32_t, int32_t>>& pack, uint64_t max_extent) {
     const int E = c->E;
     const bool fresh = !c->pages_valid || c->pages_gen != c->masters_gen;
+    const bool bp = bitplane(c);
     nt.assign(E, pw_page_entry{});
-    std::vector<char> changed(E, 1);
+    // 0: keep, 1: place anew (whole page), 2: bitplane page grown (in place
+    // if possible)
+    std::vector<char> kind(E, 1);
     for (int e = 0; e < E; ++e) {
         nt[e].bits = bits[e];
         nt[e].nbytes = c->We * bits[e] / 8;
-        nt[e].scale = scale_for(c->absmax[e], bits[e]);
-        if (!fresh && c->table[e].bits == bits[e]) {
-            changed[e] = 0;
+        nt[e].scale = scale_for(c, c->absmax[e], bits[e]);
+        if (fresh) continue;
+        const int old = c->table[e].bits;
+        if (old == bits[e] || (bp && bits[e] < old)) {
+            kind[e] = 0;
             nt[e].offset = c->table[e].offset;
+        } else if (bp) {
+            kind[e] = 2;
         }
     }
+    pack.clear();
     bool ok = !fresh;
     if (ok) {
-        // free space = pool minus the unchanged pages
         std::vector<std::pair<uint64_t, uint64_t>> used;
         for (int e = 0; e < E; ++e)
-            if (!changed[e]) used.push_back({nt[e].offset, nt[e].offset + page_bytes(c, bits[e])});
+            if (kind[e] == 0) used.push_back({nt[e].offset, nt[e].offset + page_bytes(c, bits[e])});
+        // grown bitplane pages first try to extend where they are
+        auto overlaps = [&](uint64_t lo, uint64_t hi) {
+            for (auto& u : used)
+                if (lo < u.second && u.first < hi) return true;
+            return false;
+        };
+        for (int e = 0; e < E; ++e) {
+            if (kind[e] != 2) continue;
+            const uint64_t lo = c->table[e].offset, hi = lo + page_bytes(c, bits[e]);
+            if (hi <= page_cap(c) && !overlaps(lo, hi)) {
+                nt[e].offset = lo;
+                used.push_back({lo, hi});
+                pack.push_back({e, (int32_t)c->table[e].bits});
+                kind[e] = 0;
+            } else {
+                kind[e] = 1;
+            }
+        }
         std::sort(used.begin(), used.end());
         std::vector<std::pair<uint64_t, uint64_t>> holes;
         uint64_t at = 0;
@@ -325,7 +372,7 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
         if (page_cap(c) > at) holes.push_back({at, page_cap(c)});
         std::vector<int> order;
         for (int e = 0; e < E; ++e)
-            if (changed[e]) order.push_back(e);
+            if (kind[e] == 1) order.push_back(e);
         std::stable_sort(order.begin(), order.end(),
                          [&](int a, int b) { return bits[a] > bits[b]; });
         for (int e : order) {
@@ -336,6 +383,7 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
                     nt[e].offset = h.first;
                     h.first += need;
                     placed = true;
+                    pack.push_back({e, 0});
                     break;
                 }
             }
@@ -344,20 +392,19 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
         if (ok && extent_of(c, nt) > max_extent) ok = false;
     }
     if (!ok) {
+        pack.clear();
         uint64_t at = 0;
         for (int e = 0; e < E; ++e) {
             nt[e].offset = at;
             at += page_bytes(c, bits[e]);
-            changed[e] = 1;
+            pack.push_back({e, 0});
         }
         if (at > page_cap(c))
             return fail(c, PW_ERR_POOL_CAPACITY, "pages need %llu bytes, %s holds %llu",
                         (unsigned long long)at, swap_mode(c) ? "host tier" : "pool",
                         (unsigned long long)page_cap(c));
     }
-    list.clear();
-    for (int e = 0; e < E; ++e)
-        if (changed[e]) list.push_back(e);
+    std::sort(pack.begin(), pack.end());
     return PW_OK;
 }
 
@@ -365,11 +412,15 @@ pw_status place(pw_ctx* c, const uint8_t* bits, std::vector<pw_page_entry>& nt,
 // device copy), pack the changed experts, then make the new table current.
 pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s, uint64_t max_extent = UINT64_MAX) {
     std::vector<pw_page_entry> nt;
-    std::vector<int32_t> list;
-    pw_status st = place(c, bits, nt, list, max_extent);
+    std::vector<std::pair<int32_t, int32_t>> pack;
+    pw_status st = place(c, bits, nt, pack, max_extent);
     if (st != PW_OK) return st;
-    if (list.empty()) return PW_OK;
     const int E = c->E;
+    bool same = c->pages_valid && c->pages_gen == c->masters_gen;
+    for (int e = 0; same && e < E; ++e)
+        same = nt[e].bits == c->table[e].bits && nt[e].offset == c->table[e].offset;
+    if (same) return PW_OK;
+    const int n = (int)pack.size();
     const int next = 1 - c->cur;
     HIP_TRY(c, hipEventSynchronize(c->upload_done));   // staging buffer free again
     uint8_t* h = c->host_stage;
@@ -379,16 +430,19 @@ pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s, uint64_t max
         const int32_t b = nt[e].bits;
         std::memcpy(h + (size_t)E * 12 + (size_t)e * 4, &b, 4);
     }
-    std::memcpy(h + (size_t)E * 16, list.data(), list.size() * 4);
+    for (int i = 0; i < n; ++i) {
+        std::memcpy(h + (size_t)E * 16 + (size_t)i * 4, &pack[i].first, 4);
+        std::memcpy(h + (size_t)E * 20 + (size_t)i * 4, &pack[i].second, 4);
+    }
     c->pages_valid = false;   // until the pack is enqueued
-    HIP_TRY(c, hipMemcpyAsync(dev_table(c, next).off, h, (size_t)E * 16 + list.size() * 4,
-                              hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipMemcpyAsync(dev_table(c, next).off, h, (size_t)E * 24, hipMemcpyHostToDevice, s));
     HIP_TRY(c, hipEventRecord(c->upload_done, s));
     const int f16 = c->desc.master_dtype == PW_MASTER_F16;
     HIP_TRY(c, launch_pack(c->w1, c->w3, c->w2, f16, c->d, c->F, dev_table(c, next), dev_list(c, next),
-                           (int)list.size(), page_base(c), s));
-    // rewritten pages: their slot copies are stale
-    if (swap_mode(c)) HIP_TRY(c, launch_swap_invalidate(swap_state(c), dev_list(c, next), (int)list.size(), s));
+                           dev_first(c, next), n, bitplane(c) ? 1 : 0, page_base(c), s));
+    // rewritten pages: their slot copies are stale (a bitplane page that only
+    // lost planes keeps a valid slot: its planes are a prefix of the slot's)
+    if (swap_mode(c)) HIP_TRY(c, launch_swap_invalidate(swap_state(c), dev_list(c, next), n, s));
     c->table = nt;
     c->cur = next;
     c->pages_valid = true;
@@ -399,9 +453,9 @@ pw_status apply_bits(pw_ctx* c, const uint8_t* bits, hipStream_t s, uint64_t max
 pw_status check_bits(pw_ctx* c, const uint8_t* bits) {
     if (!bits) return fail(c, PW_ERR_INVALID_ARG, "bits is NULL");
     for (int e = 0; e < c->E; ++e)
-        if (bits_index(bits[e]) < 0)
-            return fail(c, PW_ERR_UNSUPPORTED_BITS, "expert %d: %d bits (supported: 3, 4, 8)", e,
-                        (int)bits[e]);
+        if (!bits_ok(c, bits[e]))
+            return fail(c, PW_ERR_UNSUPPORTED_BITS, "expert %d: %d bits (supported: %s)", e, (int)bits[e],
+                        c->desc.layout == PW_LAYOUT_BITPLANE ? "depths 1 to 8" : "3, 4, 8");
     return PW_OK;
 }
 
@@ -493,7 +547,8 @@ pw_status pw_create(const pw_layer_desc* desc, pw_ctx** out) {
         d.d_ff < kRowAlign || d.d_model % kRowAlign || d.d_ff % kRowAlign || d.top_k < 1 ||
         d.top_k > kMaxTopK || d.top_k > d.num_experts || d.max_tokens < 0 ||
         (d.renorm != 0 && d.renorm != 1) ||
-        (d.master_dtype != PW_MASTER_F32 && d.master_dtype != PW_MASTER_F16))
+        (d.master_dtype != PW_MASTER_F32 && d.master_dtype != PW_MASTER_F16) ||
+        (d.layout != PW_LAYOUT_EQ2 && d.layout != PW_LAYOUT_BITPLANE))
         return PW_ERR_INVALID_ARG;
     if ((int64_t)d.max_tokens * d.top_k > (int64_t)1 << 30) return PW_ERR_INVALID_ARG;
     pw_ctx* c = new (std::nothrow) pw_ctx;
@@ -549,7 +604,7 @@ uint64_t pw_pool_bytes_for_bits(const pw_ctx* c, const uint8_t* bits) {
     if (!c || !bits) return 0;
     uint64_t t = 0;
     for (int e = 0; e < c->E; ++e) {
-        if (bits_index(bits[e]) < 0) return 0;
+        if (!bits_ok(c, bits[e])) return 0;
         t += page_bytes(c, bits[e]);
     }
     return t;
@@ -723,6 +778,7 @@ pw_status pw_budget_step(pw_ctx* c, const pw_budget_policy* policy, uint64_t kv_
 // routed expert (weights read once per 64 tokens); else the streaming kernels
 // (weights read once).
 static bool dense_path(const pw_ctx* c, int32_t T) {
+    if (c->desc.layout == PW_LAYOUT_BITPLANE) return false;   // the streaming kernels decode bitplanes
     const int64_t pairs = (int64_t)T * c->k;
     const int64_t max_act = std::min<int64_t>(c->E, pairs);
     return gemm_supported(c->d, c->F) && pairs >= (int64_t)kGemmMinTokens * max_act;
@@ -853,6 +909,7 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
         fa.k = c->k;
         fa.max_act = max_act;
         fa.P = P;
+        fa.bitplane = c->desc.layout == PW_LAYOUT_BITPLANE ? 1 : 0;
         // K splits of the down product for this batch, within the buffer
         const int64_t cap_pairs = (int64_t)v.nsplit * v.max_tokens * c->k;
         const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / pairs, 1 << 30));

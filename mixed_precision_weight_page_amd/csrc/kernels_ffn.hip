@@ -88,11 +88,11 @@ using dq::perm_slot;
 // MODE 0 reads bf16 activations of the tokens in tok[], each row scaled by
 // its token's 2^-e; MODE 1 reads the (already scaled) fp16 SwiGLU rows of
 // the pairs in prs[] from H.
-template <int MODE, int B>
+template <int MODE, class C>
 __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a,
                                       const int* tok, const int* prs, int nt, int k0, int kc) {
-    if constexpr (B == 3) {
-        // the 3-bit order permutes across all 32 codes of a run
+    if constexpr (C::kPermSpan == 32) {
+        // the order permutes across all 32 codes of a run
         const int ngrp = kc / 32;
         for (int idx = threadIdx.x; idx < nt * ngrp; idx += kThreads) {
             const int n = idx / ngrp, grp = idx - n * ngrp;
@@ -128,7 +128,7 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
                 _Float16 h[32];
             } o;
 #pragma unroll
-            for (int s = 0; s < 32; ++s) o.h[s] = v[perm_slot<B>(s)];
+            for (int s = 0; s < 32; ++s) o.h[s] = v[C::perm(s)];
             uint4* dst = reinterpret_cast<uint4*>(xs + n * stride + 32 * grp);
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = o.u[q];
@@ -163,7 +163,7 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
                 _Float16 h[8];
             } o;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) o.h[s] = v[perm_slot<B>(s)];
+            for (int s = 0; s < 8; ++s) o.h[s] = v[C::perm(s)];
             *reinterpret_cast<uint4*>(xs + n * stride + 8 * ch) = o.u;
         }
     }
@@ -172,7 +172,7 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
 // Steps of codes in flight per wave: 8 x 16 B (4-bit), 8 x 12 B (3-bit),
 // 4 x 32 B (8-bit) per matrix and lane.
 template <int B>
-__device__ __forceinline__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
+__host__ __device__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
 
 // The four MFMAs of one 128-code step for each matrix; bp points at the
 // step's 128 staged activations of this lane's token row and K-group.
@@ -203,6 +203,153 @@ __device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Flo
     }
 }
 
+// How the codes of a page reach the matrix cores. Eq2Codec<B>: Eq. 2 pages;
+// a lane's 32-code run of a tile is 4B contiguous bytes. PlaneCodec<NP>:
+// bitplane pages at depth NP (planes 0 .. NP-1 of the expert, W_e / 8 bytes
+// apart; each plane of a 16 x 128 tile is 256 bytes, lane l = 16 g + r holding
+// the bits of codes 32g .. 32g+31 of row r as one 32-bit word).
+template <int B>
+struct Eq2Codec {
+    static constexpr int kWords = B;
+    static constexpr int PD = prefetch_depth<B>();
+    static constexpr int kStepBytes = 16 * kStep * B / 8;
+    static constexpr int kPermSpan = B == 3 ? 32 : 8;
+    static constexpr int kQmax = qmax_of(B);                       // largest |code| the MFMA sees
+    __device__ static float eff_scale(float s) { return s; }        // weight = eff_scale(s) code
+    __device__ static int lane_offset(int l) { return (B == 3 ? 12 : 16) * l; }
+    __device__ static int64_t mat_bytes(int64_t M) { return M * B / 8; }
+    using Src = const uint8_t*;
+    __device__ static Src source(const uint8_t* base) { return base; }
+    __device__ static Codes<B> load(Src p, int64_t off, int lane_off, int64_t) { return load_codes<B>(p + off + lane_off); }
+    __host__ __device__ static constexpr int perm(int s) { return perm_slot<B>(s); }
+    template <int NMAT>
+    __device__ static void mma(const Codes<B> (&cur)[NMAT], const _Float16* bp, f32x4 (&acc)[NMAT],
+                               const dq::Const& dc) {
+        step_mma<B, NMAT>(cur, bp, acc, dc);
+    }
+};
+
+// Bitplane decoding (the nested quantizer read from the PagedMoE page's
+// abstract: a depth-NP weight is the centre of the node named by the first
+// NP bits of Eq. 2's 8-bit code; twice its code is the integer
+// c = (2p + 1) 2^(8-NP) - 257 for the prefix p, so the MFMA products stay
+// exact and the epilogue scales by s8 / 2). The NP plane words of a step are
+// transposed in groups of four with two rounds of masked block swaps (four
+// words hold a 4 x 32 bit matrix; afterwards word i holds, in nibble g, the
+// four plane bits of code i + 4 g), so every code's prefix bits sit in one
+// nibble; then each pair of codes (at bit S = 0 or 4 of both 16-bit halves)
+// becomes exact fp16 c with a magic-exponent OR, one subtract and one or two
+// fma. Word i gives MFMA fragment i, K-slots 8i .. 8i+7 holding codes
+// i, i+16, i+4, i+20, i+8, i+24, i+12, i+28.
+__device__ __forceinline__ void transpose4(uint32_t& x0, uint32_t& x1, uint32_t& x2, uint32_t& x3) {
+    uint32_t t = ((x0 >> 2) ^ x2) & 0x33333333u;
+    x2 ^= t;
+    x0 ^= t << 2;
+    t = ((x1 >> 2) ^ x3) & 0x33333333u;
+    x3 ^= t;
+    x1 ^= t << 2;
+    t = ((x0 >> 1) ^ x1) & 0x55555555u;
+    x1 ^= t;
+    x0 ^= t << 1;
+    t = ((x2 >> 1) ^ x3) & 0x55555555u;
+    x3 ^= t;
+    x2 ^= t << 1;
+}
+
+// the nibbles at bit S of both halves of t, times 2^S, as fp16
+template <int S>
+__device__ __forceinline__ half2_t nibbles(uint32_t t, const dq::Const& c) {
+    constexpr uint32_t mask = 0x000F000Fu << S;
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    return dq::as_half2((t & mask) | c.magic) - k1024;
+}
+
+template <int NP>
+struct PlaneCodec {
+    static constexpr int kWords = NP;
+    static constexpr int PD = NP <= 4 ? 8 : (NP <= 6 ? 5 : 4);   // at most 64 plane words per lane in flight
+    static constexpr int kStepBytes = 256;
+    static constexpr int kPermSpan = 32;
+    static constexpr int kQmax = 257;                               // |c| <= 257
+    __device__ static float eff_scale(float s8) { return 0.5f * s8; }   // weight = s8 c / 2
+    __device__ static int lane_offset(int l) { return 4 * l; }
+    __device__ static int64_t mat_bytes(int64_t M) { return M / 8; }
+    // A buffer descriptor over the wave's (uniform) stream base, in scalar
+    // registers: each plane word is one non-temporal buffer load with the
+    // lane's offset in a vector register and the plane's in a scalar one, so
+    // the NP planes cost no per-plane address registers.
+    struct Src {
+        __amdgpu_buffer_rsrc_t r;
+    };
+    __device__ static Src source(const uint8_t* base) {
+        const uint64_t a = reinterpret_cast<uint64_t>(base);
+        const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        return Src{__builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, 0x7fffffff, 0x00020000)};
+    }
+    __device__ static Codes<NP> load(const Src& p, int64_t off, int lane_off, int64_t plane) {
+        Codes<NP> c;
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            c.w[j] = __builtin_amdgcn_raw_buffer_load_b32(p.r, lane_off, (int)(j * plane + off), 2 /* nt */);
+        return c;
+    }
+    __host__ __device__ static constexpr int perm(int s) { return (s >> 3) + 4 * ((s >> 1) & 3) + 16 * (s & 1); }
+
+    // fragment of word pair (hi: nibble of planes 0-3, or of all NP <= 4
+    // planes; lo: planes 4-7, zero-padded)
+    __device__ static half8_t frag(uint32_t hi, uint32_t lo, const dq::Const& dc) {
+        constexpr float K = (float)((1 << (8 - NP)) - 257);
+        const half2_t k2 = {(_Float16)K, (_Float16)K};
+        half2_t p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t th = (q & 2) ? hi >> 8 : hi;
+            const uint32_t tl = (q & 2) ? lo >> 8 : lo;
+            const half2_t h = (q & 1) ? nibbles<4>(th, dc) : nibbles<0>(th, dc);
+            if constexpr (NP <= 4) {
+                // c = p 2^(9-NP) + K
+                const float m = (float)(1 << (9 - NP)) / ((q & 1) ? 16.0f : 1.0f);
+                p[q] = __builtin_elementwise_fma(h, half2_t{(_Float16)m, (_Float16)m}, k2);
+            } else {
+                // c = 32 H + 2 L + K
+                const half2_t l = (q & 1) ? nibbles<4>(tl, dc) : nibbles<0>(tl, dc);
+                const float mh = (q & 1) ? 2.0f : 32.0f, ml = (q & 1) ? 0.125f : 2.0f;
+                p[q] = __builtin_elementwise_fma(h, half2_t{(_Float16)mh, (_Float16)mh},
+                                                 __builtin_elementwise_fma(l, half2_t{(_Float16)ml, (_Float16)ml}, k2));
+            }
+        }
+        return dq::cat(p[0], p[1], p[2], p[3]);
+    }
+
+    template <int NMAT>
+    __device__ static void mma(const Codes<NP> (&cur)[NMAT], const _Float16* bp, f32x4 (&acc)[NMAT],
+                               const dq::Const& dc) {
+        uint32_t hi[NMAT][4], lo[NMAT][4];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            // row r of the high group is plane (min(NP, 4) - 1 - r); of the
+            // low group plane 7 - r (zero past the depth)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jh = (NP < 4 ? NP : 4) - 1 - r;
+                hi[m][r] = jh >= 0 ? cur[m].w[jh < 0 ? 0 : jh] : 0u;
+                const int jl = 7 - r;
+                lo[m][r] = (NP > 4 && jl < NP) ? cur[m].w[jl < NP ? jl : 0] : 0u;
+            }
+            transpose4(hi[m][0], hi[m][1], hi[m][2], hi[m][3]);
+            if constexpr (NP > 4) transpose4(lo[m][0], lo[m][1], lo[m][2], lo[m][3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag(hi[m][i], lo[m][i], dc), bfr, acc[m], 0, 0, 0);
+        }
+    }
+};
+
 // MODE 0: gate/up + SwiGLU (NMAT = 2: W1, W3); MODE 1: down (NMAT = 1: W2),
 // over K-steps [ks0, ks0 + nsteps) (the down product may be split along K
 // across workgroups; split `sp` writes its own partial output).
@@ -221,27 +368,31 @@ struct ExpertRef {
     int p0;
 };
 
-template <int MODE, int B>
+template <int MODE, class C>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const ExpertRef& ex, int rt, int sp,
                                          int ks0, int nsteps, _Float16* xs, int* tok, int* prs) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
-    constexpr int PD = prefetch_depth<B>();
-    constexpr int SB = 16 * kStep * B / 8;   // bytes of one tile: 16 rows x 128 codes
+    constexpr int PD = C::PD;
+    constexpr int SB = C::kStepBytes;   // bytes of one tile (of one plane): 16 rows x 128 codes
+    constexpr int NW = C::kWords;
     const int K = MODE == 0 ? a.d : a.F;
-    const int64_t mat_bytes = (int64_t)a.F * a.d * B / 8;
+    const int64_t mat_bytes = C::mat_bytes((int64_t)a.F * a.d);
+    const int64_t plane = 3 * (int64_t)a.F * a.d / 8;   // bitplane pages: bytes per plane
     const uint8_t* page = ex.page;
-    const float s = ex.s;
+    const float s = C::eff_scale(ex.s);
     const int Te = ex.Te;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
     const int row0 = rt * 64 + 16 * wave;
     const dq::Const dc = dq::make_const();
-    // this wave's 16-row block is one contiguous run of K/128 tiles
-    const uint8_t* ap[NMAT];
+    // this wave's 16-row block is one contiguous run of K/128 tiles: a
+    // wave-uniform base per matrix, plus the lane's offset
+    typename C::Src ap[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-        ap[m] = page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * (K / kStep) + ks0) * SB +
-                lane_offset<B>(lane);
+        ap[m] = C::source(page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * (K / kStep) + ks0) * SB);
+    const int loff = C::lane_offset(lane);
 
     for (int tb = 0; tb < Te; tb += 16) {
         const int nt = min(16, Te - tb);
@@ -256,12 +407,12 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         // after (its token-id and token-row loads, which the first step
         // waits for, are then not queued behind the codes): measured best
         // for each
-        Codes<B> buf[NMAT][PD];
+        Codes<NW> buf[NMAT][PD];
         auto issue_codes = [&]() {
 #pragma unroll
             for (int j = 0; j < PD; ++j)
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) buf[m][j] = load_codes<B>(ap[m] + min(j, nsteps - 1) * SB);
+                for (int m = 0; m < NMAT; ++m) buf[m][j] = C::load(ap[m], (int64_t)min(j, nsteps - 1) * SB, loff, plane);
         };
         if constexpr (MODE == 1) issue_codes();
         // this block's pairs (the first block's came with the expert's entry)
@@ -274,7 +425,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         __syncthreads();
         // this lane's pair (its row of H, or of O for the down product)
         const int my_pair = prs[min(r, nt - 1)];
-        stage<MODE, B>(xs, stride, a, tok, prs, nt, ks0 * kStep, min(spc, nsteps) * kStep);
+        stage<MODE, C>(xs, stride, a, tok, prs, nt, ks0 * kStep, min(spc, nsteps) * kStep);
         // the statistics of this lane's token, for the epilogue (issued after
         // the staging loads, which the barrier below waits for)
         const XStat my_xs = a.w.xst[my_pair / a.k];
@@ -289,20 +440,20 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         for (; s0 + 2 * PD <= nsteps; s0 += PD) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
+                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
             const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
             for (int j = 0; j < PD; ++j) {
-                Codes<B> cur[NMAT];
+                Codes<NW> cur[NMAT];
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     cur[m] = buf[m][j];
-                    buf[m][j] = load_codes<B>(ap[m] + (int64_t)(s0 + j + PD) * SB);
+                    buf[m][j] = C::load(ap[m], (int64_t)(s0 + j + PD) * SB, loff, plane);
                 }
-                step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
+                C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
             }
         }
         // The last one or two groups. A group that still has loads to issue
@@ -313,27 +464,27 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         if (nsteps - s0 > PD) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
+                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
             const _Float16* bp = bp0 + (s0 % spc) * kStep;
 #pragma unroll
             for (int j = 0; j < PD; ++j) {
-                Codes<B> cur[NMAT];
+                Codes<NW> cur[NMAT];
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     cur[m] = buf[m][j];
-                    buf[m][j] = load_codes<B>(ap[m] + (int64_t)min(s0 + j + PD, nsteps - 1) * SB);
+                    buf[m][j] = C::load(ap[m], (int64_t)min(s0 + j + PD, nsteps - 1) * SB, loff, plane);
                 }
-                step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
+                C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
             }
             s0 += PD;
         }
         if (s0 < nsteps) {
             if (s0 != 0 && s0 % spc == 0) {
                 __syncthreads();
-                stage<MODE, B>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
+                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
                                min(spc, nsteps - s0) * kStep);
                 __syncthreads();
             }
@@ -341,10 +492,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
 #pragma unroll
             for (int j = 0; j < PD; ++j) {
                 if (s0 + j < nsteps) {
-                    Codes<B> cur[NMAT];
+                    Codes<NW> cur[NMAT];
 #pragma unroll
                     for (int m = 0; m < NMAT; ++m) cur[m] = buf[m][j];
-                    step_mma<B, NMAT>(cur, bp + j * kStep, acc, dc);
+                    C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
                 }
             }
         }
@@ -356,12 +507,12 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
                     uint2 u;
                     _Float16 h[4];
                 } hv;
-                const xsc::GateUpScale gs = xsc::gate_up_scale(s, B, my_xs);
+                const xsc::GateUpScale gs = xsc::gate_up_scale(s, C::kQmax, my_xs);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) hv.h[v] = (_Float16)xsc::swiglu_scaled(acc[0][v], acc[1][v], gs);
                 *reinterpret_cast<uint2*>(a.w.H + (int64_t)my_pair * a.F + orow) = hv.u;
             } else {
-                const int m = xsc::h_exponent(s, B, my_xs);
+                const int m = xsc::h_exponent(s, C::kQmax, my_xs);
                 float4 o;
                 o.x = ldexpf(s * acc[0][0], m);
                 o.y = ldexpf(s * acc[0][1], m);
@@ -378,8 +529,11 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
 // the router's active list (arrival order); its page-table entry, pair count
 // and first 16 pairs are then read in one round of independent loads (the
 // pair list has room for at least 16 entries).
-template <int MODE>
-__global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles, int nsplit) {
+// PLANES: bitplane pages (a kernel of its own, so that the Eq. 2 kernel's
+// register allocation does not depend on the bitplane decoding).
+template <int MODE, bool PLANES>
+__global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles,
+                                                                          int nsplit) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     __shared__ int tok[16];   // token of each pair of the current block
     __shared__ int prs[16];   // the pairs t k + j of the current block
@@ -395,9 +549,23 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArg
     const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15]};
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
-    if (b == 4) ffn_tile<MODE, 4>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
-    else if (b == 8) ffn_tile<MODE, 8>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
-    else ffn_tile<MODE, 3>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+    if constexpr (PLANES) {
+        // bitplane pages: b is the depth, 1 .. 8 planes
+        switch (b) {
+            case 1: ffn_tile<MODE, PlaneCodec<1>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 2: ffn_tile<MODE, PlaneCodec<2>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 3: ffn_tile<MODE, PlaneCodec<3>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 4: ffn_tile<MODE, PlaneCodec<4>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 5: ffn_tile<MODE, PlaneCodec<5>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 6: ffn_tile<MODE, PlaneCodec<6>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 7: ffn_tile<MODE, PlaneCodec<7>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            default: ffn_tile<MODE, PlaneCodec<8>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+        }
+    } else {
+        if (b == 4) ffn_tile<MODE, Eq2Codec<4>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+        else if (b == 8) ffn_tile<MODE, Eq2Codec<8>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+        else ffn_tile<MODE, Eq2Codec<3>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+    }
 }
 
 template <int MODE>
@@ -405,7 +573,10 @@ hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer 
     const int rows = MODE == 0 ? a.F : a.d;
     const int tiles = rows / 64;
     const dim3 grid((unsigned)(a.max_act * tiles * p.nsplit));
-    return launch_timed(ffn_kernel<MODE>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
+    if (a.bitplane)
+        return launch_timed(ffn_kernel<MODE, true>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
+                            (int)p.lds, tiles, p.nsplit);
+    return launch_timed(ffn_kernel<MODE, false>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
                         (int)p.lds, tiles, p.nsplit);
 }
 

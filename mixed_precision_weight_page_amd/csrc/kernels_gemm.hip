@@ -359,8 +359,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int e, int Te, int 
         if (s0 + j < S) step(s0 + j, ring[j], xs[j & 1], xs[(j + 1) & 1]);
     // epilogue: lane (n = lane % 16, g) holds rows 4g..4g+3 of each 16 x 16 tile
     if (tid < BN) {
-        if constexpr (MODE == 0) tsc[tid].gu = xsc::gate_up_scale(s, B, my_xs);
-        else tsc[tid].m = xsc::h_exponent(s, B, my_xs);
+        if constexpr (MODE == 0) tsc[tid].gu = xsc::gate_up_scale(s, qmax_of(B), my_xs);
+        else tsc[tid].m = xsc::h_exponent(s, qmax_of(B), my_xs);
     }
     if constexpr (MODE == 0) {
         // SwiGLU rows h = silu(s W1 x) * (s W3 x) of the tile's 64 tokens x

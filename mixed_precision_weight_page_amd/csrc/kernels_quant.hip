@@ -1,6 +1,11 @@
 // Quantizer kernels (PagedWeight page, section "Implementation Details",
 // Eq. 2): per-expert max|w|, the per-expert loss table L(b) used by Eq. 1,
-// and the pack of codes into the expert's page.
+// and the pack of codes into the expert's page. Bitplane pages (the
+// PagedMoE page's prefix-compatible layout, read as a tree codebook over
+// Eq. 2's 8-bit codes u8): plane j holds bit 7 - j of every u8, a depth-b
+// page holds planes 0 .. b-1 (each the three matrices' tiles, W_e / 8
+// bytes), and a depth-b weight is s8 c / 2 with c = (2p + 1) 2^(8-b) - 257,
+// p = u8 >> (8 - b).
 //
 // Weight space of expert e: its W1 block (M = F*d weights), then W3, then W2,
 // each row-major. A page holds the codes u = q + 2^(b-1) of W1, W3, W2, each
@@ -114,12 +119,13 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* w1, const 
 }
 
 // grid (3*M / kStatChunk, E): per-block partial sums of (w - s q)^2 for
-// b = 3, 4, 8 in fp64, written in block order (no atomics).
+// b = 3, 4, 8 in fp64 (bitplane pages: of (w - s8 c / 2)^2 at depths 3, 4,
+// 8), written in block order (no atomics).
 __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, const void* w3,
                                                                 const void* w2, int f16,
                                                                 int64_t M,
                                                                 const uint32_t* absmax,
-                                                                double* partial) {
+                                                                double* partial, int planes) {
     const int e = blockIdx.y;
     const int64_t start = (int64_t)blockIdx.x * kStatChunk;
     const int mtx = (int)(start / M);
@@ -139,11 +145,22 @@ __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, 
         load4(base, off + (int64_t)(i * kThreads + threadIdx.x) * 4, f16, v);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if (planes) {
+                const int u = (int)code_of(v[j], s[2], inv_s[2], qm[2]) + 128;   // u8 (s[2] = s8)
 #pragma unroll
-            for (int b = 0; b < 3; ++b) {
-                const float q = code_of(v[j], s[b], inv_s[b], qm[b]);
-                const double err = (double)v[j] - (double)s[b] * (double)q;  // exact
-                acc[b] = fma(err, err, acc[b]);
+                for (int b = 0; b < 3; ++b) {
+                    const int depth = bits_of_index(b);
+                    const int c = (2 * (u >> (8 - depth)) + 1) * (1 << (8 - depth)) - 257;
+                    const double err = (double)v[j] - (double)s[2] * (double)c * 0.5;   // exact
+                    acc[b] = fma(err, err, acc[b]);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    const float q = code_of(v[j], s[b], inv_s[b], qm[b]);
+                    const double err = (double)v[j] - (double)s[b] * (double)q;  // exact
+                    acc[b] = fma(err, err, acc[b]);
+                }
             }
         }
     }
@@ -224,20 +241,41 @@ __device__ __forceinline__ void pack_run(const uint8_t* codes, uint8_t* tile) {
     }
 }
 
+// Bitplane j of a tile: lane l = 16 g + r writes one word, bit i = bit
+// 7 - j of code 32 g + i of row r (codes as bytes in LDS, as for pack_run).
+__device__ __forceinline__ uint32_t plane_word(const uint8_t* codes, int j) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const uint4 c0 = *reinterpret_cast<const uint4*>(codes + r * kCodeRow + 32 * g);
+    const uint4 c1 = *reinterpret_cast<const uint4*>(codes + r * kCodeRow + 32 * g + 16);
+    const uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};   // 4 codes per word
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t x = (c[k] >> (7 - j)) & 0x01010101u;   // the bit of each byte, at 0, 8, 16, 24
+        w |= ((x | (x >> 7) | (x >> 14) | (x >> 21)) & 0xfu) << (4 * k);
+    }
+    return w;
+}
+
 // grid (3*M / 8192, nlist), 4 waves: wave w of block x packs tile 4x + w of
 // the listed expert (tiles of W1, then W3, then W2; in each matrix in
-// (16-row block, 128-code step) order).
+// (16-row block, 128-code step) order). Bitplane pages (planes != 0): the
+// codes are u8 of Eq. 2 at 8 bits with scale s8 (the table's scale), and
+// planes first[i] .. depth - 1 of the i-th listed expert are written.
 __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const void* w3,
                                                         const void* w2, int f16, int d, int F,
                                                         DevTable tab, const int32_t* list,
+                                                        const int32_t* first, int planes,
                                                         uint8_t* pool) {
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[kThreads / 64][16 * kCodeRow];
     const int e = list[blockIdx.y];
-    const int b = tab.bits[e];
+    const int b = tab.bits[e];            // bit-width, or the depth of a bitplane page
+    const int cb = planes ? 8 : b;         // bits of the codes computed
     const float s = tab.scale[e];
     const float inv_s = s > 0.0f ? 1.0f / s : 0.0f;
-    const float qm = (float)qmax_of(b);
-    const int bias = 1 << (b - 1);
+    const float qm = (float)qmax_of(cb);
+    const int bias = 1 << (cb - 1);
     const int64_t M = (int64_t)F * d;
     const int64_t tpm = M / 2048;                         // tiles per matrix
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -264,6 +302,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const vo
         *reinterpret_cast<uint32_t*>(codes + row * kCodeRow + c4) = packed;
     }
     __syncthreads();   // (the wave's own rows; a block barrier keeps it simple)
+    if (planes) {
+        const int64_t plane = 3 * M / 8;
+        uint8_t* tile = pool + tab.off[e] + mtx * (M / 8) + tt * 256 + 4 * lane;
+        for (int j = first[blockIdx.y]; j < b; ++j)
+            *reinterpret_cast<uint32_t*>(tile + j * plane) = plane_word(codes, j);
+        return;
+    }
     uint8_t* tile = pool + tab.off[e] + mtx * (M * b / 8) + tt * (256 * b);
     if (b == 3) pack_run<3>(codes, tile);
     else if (b == 4) pack_run<4>(codes, tile);
@@ -280,10 +325,10 @@ hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16
 }
 
 hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, int E,
-                       int64_t M, const uint32_t* absmax, double* partial, double* loss,
+                       int64_t M, const uint32_t* absmax, double* partial, double* loss, int planes,
                        hipStream_t s) {
     const int nblk = (int)(3 * M / kStatChunk);
-    loss_partial_kernel<<<dim3(nblk, E), kThreads, 0, s>>>(w1, w3, w2, f16, M, absmax, partial);
+    loss_partial_kernel<<<dim3(nblk, E), kThreads, 0, s>>>(w1, w3, w2, f16, M, absmax, partial, planes);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     loss_final_kernel<<<E, kThreads, 0, s>>>(partial, nblk, 3 * M, loss);
@@ -291,12 +336,12 @@ hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, 
 }
 
 hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int d, int F,
-                       DevTable tab, const int32_t* list, int nlist, uint8_t* pool,
-                       hipStream_t s) {
+                       DevTable tab, const int32_t* list, const int32_t* first, int nlist, int planes,
+                       uint8_t* pool, hipStream_t s) {
     if (nlist == 0) return hipSuccess;
     const int64_t M = (int64_t)F * d;
     dim3 grid((unsigned)(3 * M / 8192), (unsigned)nlist);
-    pack_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, d, F, tab, list, pool);
+    pack_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, d, F, tab, list, first, planes, pool);
     return hipGetLastError();
 }
 

@@ -119,11 +119,13 @@ inline hipError_t launch_timed(Kern kernel, dim3 grid, dim3 block, size_t lds, h
 hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16, int E,
                          int64_t M, uint32_t* absmax, uint32_t* flags, hipStream_t s);
 hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, int E,
-                       int64_t M, const uint32_t* absmax, double* partial, double* loss,
+                       int64_t M, const uint32_t* absmax, double* partial, double* loss, int planes,
                        hipStream_t s);
+// planes: bitplane pages; first[i] (planes only) is the first plane to write
+// for the i-th listed expert, up to its depth
 hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, int d, int F,
-                       DevTable tab, const int32_t* list, int nlist, uint8_t* pool,
-                       hipStream_t s);
+                       DevTable tab, const int32_t* list, const int32_t* first, int nlist, int planes,
+                       uint8_t* pool, hipStream_t s);
 
 struct RouteArgs {
     const float* logits;
@@ -161,6 +163,7 @@ struct FfnArgs {
     const uint16_t* x;   // bf16 [T, d]
     int d, F, k, max_act;
     int P;               // pair stride of the split partial outputs O[split][P][d]
+    int bitplane;        // 1: bitplane pages (the table's bits are depths 1..8)
 };
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});

@@ -47,20 +47,21 @@ __device__ __forceinline__ int a_exponent(float s, int qmax, float n1) {
     return es + en + em;
 }
 
-// Per-token factors of the gate/up epilogue for an expert of scale s and
-// width B: a_s = acc_a fa, c_s = acc_c fc, a = a_s 2^ea.
+// Per-token factors of the gate/up epilogue for an expert whose weights are
+// s times integer codes of magnitude at most qmax: a_s = acc_a fa,
+// c_s = acc_c fc, a = a_s 2^ea.
 struct GateUpScale {
     float fa, fc;
     int ea;
 };
-__device__ __forceinline__ GateUpScale gate_up_scale(float s, int B, XStat xt) {
-    const int Ea = a_exponent(s, qmax_of(B), xt.n1);
+__device__ __forceinline__ GateUpScale gate_up_scale(float s, int qmax, XStat xt) {
+    const int Ea = a_exponent(s, qmax, xt.n1);
     return GateUpScale{ldexpf(s, -Ea), ldexpf(s, 15 - Ea), Ea + xt.e};
 }
 
 // Exponent m of the stored h~ rows (h = h~ 2^m) of a token and expert.
-__device__ __forceinline__ int h_exponent(float s, int B, XStat xt) {
-    return 2 * (a_exponent(s, qmax_of(B), xt.n1) + xt.e) - 15;
+__device__ __forceinline__ int h_exponent(float s, int qmax, XStat xt) {
+    return 2 * (a_exponent(s, qmax, xt.n1) + xt.e) - 15;
 }
 
 // h~ from the two fp32 sums; sigmoid(a) with a = a_s 2^ea (which may

@@ -23,6 +23,8 @@ _lib = None
 
 PW_MASTER_F32 = 0
 PW_MASTER_F16 = 1
+PW_LAYOUT_EQ2 = 0
+PW_LAYOUT_BITPLANE = 1
 BITS = (3, 4, 8)
 
 
@@ -36,7 +38,7 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("master_dtype", ctypes.c_int32)]
+                ("master_dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class PageEntry(ctypes.Structure):
@@ -230,10 +232,16 @@ class PagedMoELayer:
     """One MoE expert layer bound to its masters, pool and workspace."""
 
     def __init__(self, num_experts: int, d_model: int, d_ff: int, top_k: int,
-                 max_tokens: int, renorm: int = 0, master_dtype: str = "f32"):
+                 max_tokens: int, renorm: int = 0, master_dtype: str = "f32", layout: str = "eq2"):
+        """layout: "eq2" (pages of Eq. 2 codes at 3/4/8 bits) or "bitplane"
+        (prefix-compatible bitplane pages; bits are depths 1..8)."""
         self._ctx = None
+        if layout not in ("eq2", "bitplane"):
+            raise ValueError("layout must be 'eq2' or 'bitplane'")
         desc = LayerDesc(num_experts, d_model, d_ff, top_k, renorm, max_tokens,
-                         PW_MASTER_F16 if master_dtype == "f16" else PW_MASTER_F32)
+                         PW_MASTER_F16 if master_dtype == "f16" else PW_MASTER_F32,
+                         PW_LAYOUT_BITPLANE if layout == "bitplane" else PW_LAYOUT_EQ2)
+        self.layout = layout
         ctx = _P()
         _check(lib().pw_create(ctypes.byref(desc), ctypes.byref(ctx)))
         self._ctx = ctx

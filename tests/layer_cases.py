@@ -27,11 +27,11 @@ def cpu_threads():
     return n
 
 
-def make_layer(wl: synth.Workload, masters, max_tokens: int, pool_bytes: int = None):
+def make_layer(wl: synth.Workload, masters, max_tokens: int, pool_bytes: int = None, layout: str = "eq2"):
     from mixed_precision_weight_page_amd import PagedMoELayer
     w1, w3, w2 = (m.to("cuda") for m in masters)
     layer = PagedMoELayer(wl.E, wl.d, wl.F, wl.k, max_tokens=max_tokens, renorm=wl.renorm,
-                          master_dtype=wl.master)
+                          master_dtype=wl.master, layout=layout)
     layer.bind_masters(w1, w3, w2)
     if pool_bytes is None:
         pool_bytes = layer.pool_bytes_for_bits([8] * wl.E)

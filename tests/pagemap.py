@@ -57,3 +57,17 @@ def tiled_row(matrix: torch.Tensor, K: int, b: int, r: int) -> bytes:
                 at = tile + p * 64 * piece + (16 * g + r % TILE_ROWS) * piece
                 idx.extend(range(at, at + piece))
     return bytes(matrix[torch.tensor(idx)].tolist())
+
+
+def bitplane_page_rows(page: torch.Tensor, d: int, F: int, depth: int) -> torch.Tensor:
+    """A device bitplane page of `depth` planes in the oracle's layout: each
+    plane is the W1, W3 and W2 bits, every matrix tiled as above at one bit
+    per code (a 256-byte tile, lane l holding one 32-bit word)."""
+    out = page.clone()
+    off = 0
+    for _ in range(depth):
+        for rows, K in ((F, d), (F, d), (d, F)):
+            n = rows * K // 8
+            out[off:off + n] = untile_matrix(page[off:off + n], rows, K, 1).reshape(-1)
+            off += n
+    return out

@@ -125,7 +125,7 @@ def make_ctx(L, **kw):
 def test_create_rejects_bad_shapes(L):
     for bad in (dict(d_model=100), dict(d_ff=0), dict(top_k=0), dict(top_k=5),
                 dict(num_experts=2000), dict(renorm=2), dict(master_dtype=7),
-                dict(max_tokens=-1)):
+                dict(max_tokens=-1), dict(layout=2)):
         st, ctx = make_ctx(L, **bad)
         assert st == INVALID, bad
     st, ctx = make_ctx(L)
@@ -339,3 +339,23 @@ def test_host_tier_errors_without_gpu(L):
         assert L.pw_get_residency(None, None, None, None) == INVALID
     finally:
         L.pw_destroy(ctx)
+
+
+def test_bitplane_layout_depths(L):
+    # bitplane pages take depths 1..8 (a depth-b page holds b planes of
+    # W_e / 8 bytes); Eq. 2 pages only 3, 4 and 8 bits
+    E, d, F = 4, 128, 256
+    We = 3 * d * F
+    st, ctx = make_ctx(L, layout=1)
+    assert st == PW_OK
+    for depths in ([1, 2, 5, 8], [7, 6, 3, 1]):
+        b = np.array(depths, dtype=np.uint8)
+        assert L.pw_pool_bytes_for_bits(ctx, b.ctypes.data) == sum((We * x // 8 + 255) // 256 * 256 for x in depths)
+    for bad in ([0, 4, 4, 4], [9, 4, 4, 4]):
+        b = np.array(bad, dtype=np.uint8)
+        assert L.pw_pool_bytes_for_bits(ctx, b.ctypes.data) == 0
+    L.pw_destroy(ctx)
+    st, ctx = make_ctx(L, layout=0)
+    b = np.array([5, 4, 4, 4], dtype=np.uint8)
+    assert L.pw_pool_bytes_for_bits(ctx, b.ctypes.data) == 0
+    L.pw_destroy(ctx)

@@ -910,6 +910,8 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
         fa.max_act = max_act;
         fa.P = P;
         fa.bitplane = c->desc.layout == PW_LAYOUT_BITPLANE ? 1 : 0;
+        // an expert may receive more than 16 tokens
+        fa.wide = T > 16 ? 1 : 0;
         // K splits of the down product for this batch, within the buffer
         const int64_t cap_pairs = (int64_t)v.nsplit * v.max_tokens * c->k;
         const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / pairs, 1 << 30));

@@ -29,6 +29,11 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <utility>
+#include <mutex>
+#include <map>
+
 #include "dequant.h"
 #include "pw_internal.h"
 #include "xscale.h"
@@ -40,6 +45,7 @@ using dq::half8_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr int kCUs = 256;     // compute units of the GPU
 constexpr int kStep = 128;   // codes per wave per step (4 K-groups x 32)
 
 template <int B>
@@ -90,11 +96,11 @@ using dq::perm_slot;
 // the pairs in prs[] from H.
 template <int MODE, class C>
 __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a,
-                                      const int* tok, const int* prs, int nt, int k0, int kc) {
+                                      const int* tok, const int* prs, int nt, int k0, int kc, int tid) {
     if constexpr (C::kPermSpan == 32) {
         // the order permutes across all 32 codes of a run
         const int ngrp = kc / 32;
-        for (int idx = threadIdx.x; idx < nt * ngrp; idx += kThreads) {
+        for (int idx = tid; idx < nt * ngrp; idx += kThreads) {
             const int n = idx / ngrp, grp = idx - n * ngrp;
             _Float16 v[32];
             if constexpr (MODE == 0) {
@@ -137,7 +143,7 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
         // 4- and 8-bit orders permute within groups of 8: one 16-byte chunk
         // of 8 activations per thread and iteration
         const int nch = kc / 8;
-        for (int idx = threadIdx.x; idx < nt * nch; idx += kThreads) {
+        for (int idx = tid; idx < nt * nch; idx += kThreads) {
             const int n = idx / nch, ch = idx - n * nch;
             _Float16 v[8];
             if constexpr (MODE == 0) {
@@ -174,32 +180,40 @@ __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a
 template <int B>
 __host__ __device__ constexpr int prefetch_depth() { return B == 8 ? 4 : 8; }
 
-// The four MFMAs of one 128-code step for each matrix; bp points at the
-// step's 128 staged activations of this lane's token row and K-group.
-template <int B, int NMAT>
-__device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* bp,
-                                         f32x4 (&acc)[NMAT], const dq::Const& dc) {
+// The MFMAs of one 128-code step: for each matrix and each of the nblk
+// (<= NB) blocks of 16 tokens, four K-groups; bp[nb] points at the step's
+// 128 staged activations of this lane's token row of block nb and K-group.
+// Each dequantized code fragment feeds every block.
+template <int NB>
+__device__ __forceinline__ void mma_blocks(const half8_t& af, const _Float16* const (&bp)[NB], int i,
+                                           f32x4 (&acc)[NB], int nblk) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        if (NB == 1 || nb < nblk) {
+            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp[nb] + 8 * i);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr, acc[nb], 0, 0, 0);
+        }
+    }
+}
+
+template <int B, int NMAT, int NB>
+__device__ __forceinline__ void step_mma(const Codes<B> (&cur)[NMAT], const _Float16* const (&bp)[NB],
+                                         f32x4 (&acc)[NMAT][NB], int nblk, const dq::Const& dc) {
     if constexpr (B == 3) {
         half2_t pr[NMAT][16];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) dq::pairs3(cur[m].w, pr[m], dc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    dq::cat(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]), bfr, acc[m], 0,
-                    0, 0);
-        }
+                mma_blocks<NB>(dq::cat(pr[m][4 * i], pr[m][4 * i + 1], pr[m][4 * i + 2], pr[m][4 * i + 3]), bp, i,
+                               acc[m], nblk);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq::frag48<B>(cur[m].w, i, dc), bfr, acc[m], 0, 0, 0);
-        }
+            for (int m = 0; m < NMAT; ++m) mma_blocks<NB>(dq::frag48<B>(cur[m].w, i, dc), bp, i, acc[m], nblk);
     }
 }
 
@@ -222,10 +236,10 @@ struct Eq2Codec {
     __device__ static Src source(const uint8_t* base) { return base; }
     __device__ static Codes<B> load(Src p, int64_t off, int lane_off, int64_t) { return load_codes<B>(p + off + lane_off); }
     __host__ __device__ static constexpr int perm(int s) { return perm_slot<B>(s); }
-    template <int NMAT>
-    __device__ static void mma(const Codes<B> (&cur)[NMAT], const _Float16* bp, f32x4 (&acc)[NMAT],
-                               const dq::Const& dc) {
-        step_mma<B, NMAT>(cur, bp, acc, dc);
+    template <int NMAT, int NB>
+    __device__ static void mma(const Codes<B> (&cur)[NMAT], const _Float16* const (&bp)[NB],
+                               f32x4 (&acc)[NMAT][NB], int nblk, const dq::Const& dc) {
+        step_mma<B, NMAT, NB>(cur, bp, acc, nblk, dc);
     }
 };
 
@@ -322,9 +336,9 @@ struct PlaneCodec {
         return dq::cat(p[0], p[1], p[2], p[3]);
     }
 
-    template <int NMAT>
-    __device__ static void mma(const Codes<NP> (&cur)[NMAT], const _Float16* bp, f32x4 (&acc)[NMAT],
-                               const dq::Const& dc) {
+    template <int NMAT, int NB>
+    __device__ static void mma(const Codes<NP> (&cur)[NMAT], const _Float16* const (&bp)[NB],
+                               f32x4 (&acc)[NMAT][NB], int nblk, const dq::Const& dc) {
         uint32_t hi[NMAT][4], lo[NMAT][4];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
@@ -341,12 +355,9 @@ struct PlaneCodec {
             if constexpr (NP > 4) transpose4(lo[m][0], lo[m][1], lo[m][2], lo[m][3]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half8_t bfr = *reinterpret_cast<const half8_t*>(bp + 8 * i);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag(hi[m][i], lo[m][i], dc), bfr, acc[m], 0, 0, 0);
-        }
+            for (int m = 0; m < NMAT; ++m) mma_blocks<NB>(frag(hi[m][i], lo[m][i], dc), bp, i, acc[m], nblk);
     }
 };
 
@@ -368,181 +379,221 @@ struct ExpertRef {
     int p0;
 };
 
-template <int MODE, class C>
+// NB: blocks of 16 tokens per pass over the codes (1, or 4 for the experts
+// that receive more than 16 tokens, whose passes prefetch two steps, the
+// most of 64 token rows the LDS holds).
+// rpw: row blocks of 16 per wave (the down product's NB = 1 passes only; the
+// host picks rpw > 1 only when the LDS holds every step of the pass's token
+// rows). The wave walks
+// its rpw blocks' steps as one sequence, so that the prefetch ring runs on
+// across block boundaries; a block's output is written after its last step.
+template <int MODE, class C, int NB>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const ExpertRef& ex, int rt, int sp,
-                                         int ks0, int nsteps, _Float16* xs, int* tok, int* prs) {
+                                         int ks0, int nsteps, int rpw, _Float16* xs, int* tok, int* prs) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
-    constexpr int PD = C::PD;
+    constexpr int PD = NB == 1 ? C::PD : 2;   // a wide pass stages two steps of its rows at a time
     constexpr int SB = C::kStepBytes;   // bytes of one tile (of one plane): 16 rows x 128 codes
     constexpr int NW = C::kWords;
     const int K = MODE == 0 ? a.d : a.F;
+    const int KS = K / kStep;   // tiles of one 16-row block in a matrix
     const int64_t mat_bytes = C::mat_bytes((int64_t)a.F * a.d);
     const int64_t plane = 3 * (int64_t)a.F * a.d / 8;   // bitplane pages: bytes per plane
     const uint8_t* page = ex.page;
     const float s = C::eff_scale(ex.s);
     const int Te = ex.Te;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
-    const int row0 = rt * 64 + 16 * wave;
+    constexpr bool kSeq = MODE == 1 && NB == 1;   // several row blocks per wave
+    const int R = kSeq ? rpw : 1;
+    const int total = R * nsteps;   // steps of the wave's sequence
+    const int row0 = (rt * 4 + wave) * R * 16;
     const dq::Const dc = dq::make_const();
-    // this wave's 16-row block is one contiguous run of K/128 tiles: a
+    // this wave's 16-row blocks are consecutive runs of K/128 tiles: a
     // wave-uniform base per matrix, plus the lane's offset
     typename C::Src ap[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-        ap[m] = C::source(page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * (K / kStep) + ks0) * SB);
+        ap[m] = C::source(page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * KS + ks0) * SB);
     const int loff = C::lane_offset(lane);
 
-    for (int tb = 0; tb < Te; tb += 16) {
-        const int nt = min(16, Te - tb);
+    for (int tb = 0; tb < Te; tb += 16 * NB) {
+        const int nt = min(16 * NB, Te - tb);
+        const int nblk = (nt + 15) >> 4;
         // steps per LDS chunk: all of them if nt rows fit, else a multiple of
         // PD (the host sizes the LDS for at least PD steps of 16 rows)
         int spc = nsteps;
         if (nt * (nsteps * kStep + 8) * 2 > lds_bytes)
             spc = ((lds_bytes / (2 * nt) - 8) / (kStep * PD)) * PD;
         const int stride = spc * kStep + 8;
+        // the load cursor: sequence index, step within its block and tile
+        // index of the next code load (it stays on the last step once there:
+        // the ring's loads past the end are never used, and a conditional
+        // load would make the ring slot's old value need a copy while it is
+        // still being consumed)
+        int lf = 0, ls = 0, la = 0;
+        auto load_step = [&](Codes<NW> (&dst)[NMAT]) {
+            if constexpr (kSeq) {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) dst[m] = C::load(ap[m], (int64_t)la * SB, loff, plane);
+                const int adv = lf < total - 1 ? 1 : 0;
+                lf += adv;
+                la += adv;
+                ls += adv;
+                const bool wrap = ls == nsteps;
+                la += wrap ? KS - nsteps : 0;
+                ls = wrap ? 0 : ls;
+            } else {
+                // one row block: the tile index is the sequence index
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) dst[m] = C::load(ap[m], (int64_t)min(lf, total - 1) * SB, loff, plane);
+                ++lf;
+            }
+        };
         // the first PD steps of codes: the down product issues them before
         // its token rows are staged (their round trips overlap), gate/up
         // after (its token-id and token-row loads, which the first step
         // waits for, are then not queued behind the codes): measured best
         // for each
-        Codes<NW> buf[NMAT][PD];
+        Codes<NW> buf[PD][NMAT];
         auto issue_codes = [&]() {
 #pragma unroll
-            for (int j = 0; j < PD; ++j)
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) buf[m][j] = C::load(ap[m], (int64_t)min(j, nsteps - 1) * SB, loff, plane);
+            for (int j = 0; j < PD; ++j) load_step(buf[j]);
         };
         if constexpr (MODE == 1) issue_codes();
-        // this block's pairs (the first block's came with the expert's entry)
-        const int p = tb == 0 ? ex.p0 : ((int)threadIdx.x < nt ? ex.list[tb + threadIdx.x] : 0);
+        // this pass's pairs (the first 16 came with the expert's entry)
+        const int p = (tb == 0 && tid < 16) ? ex.p0 : (tid < nt ? ex.list[tb + tid] : 0);
         __syncthreads();   // previous token block done with tok, prs and xs
-        if ((int)threadIdx.x < nt) {
-            prs[threadIdx.x] = p;
-            tok[threadIdx.x] = p / a.k;
+        if (tid < nt) {
+            prs[tid] = p;
+            tok[tid] = p / a.k;
         }
         __syncthreads();
-        // this lane's pair (its row of H, or of O for the down product)
-        const int my_pair = prs[min(r, nt - 1)];
-        stage<MODE, C>(xs, stride, a, tok, prs, nt, ks0 * kStep, min(spc, nsteps) * kStep);
-        // the statistics of this lane's token, for the epilogue (issued after
-        // the staging loads, which the barrier below waits for)
-        const XStat my_xs = a.w.xst[my_pair / a.k];
+        // this lane's pair in each block (its row of H, or of O for the
+        // down product)
+        int my_pair[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) my_pair[nb] = prs[min(16 * nb + r, nt - 1)];
+        stage<MODE, C>(xs, stride, a, tok, prs, nt, ks0 * kStep, min(spc, nsteps) * kStep, tid);
+        // the statistics of this lane's tokens, for the epilogue (issued
+        // after the staging loads, which the barrier below waits for)
+        XStat my_xs[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) my_xs[nb] = a.w.xst[my_pair[nb] / a.k];
         if constexpr (MODE == 0) issue_codes();
         __syncthreads();
-        f32x4 acc[NMAT];
+        f32x4 acc[NMAT][NB];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // B-fragment row of this lane's token (columns past nt repeat a real row)
-        const _Float16* bp0 = xs + min(r, nt - 1) * stride + 32 * g;
-        int s0 = 0;
-        for (; s0 + 2 * PD <= nsteps; s0 += PD) {
-            if (s0 != 0 && s0 % spc == 0) {
-                __syncthreads();
-                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
-                               min(spc, nsteps - s0) * kStep);
-                __syncthreads();
-            }
-            const _Float16* bp = bp0 + (s0 % spc) * kStep;
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < PD; ++j) {
-                Codes<NW> cur[NMAT];
+            for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B-fragment row of this lane's token in each block (columns past nt
+        // repeat a real row)
+        const _Float16* bp0[NB];
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    cur[m] = buf[m][j];
-                    buf[m][j] = C::load(ap[m], (int64_t)(s0 + j + PD) * SB, loff, plane);
-                }
-                C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
-            }
-        }
-        // The last one or two groups. A group that still has loads to issue
-        // clamps their addresses to the last tile (the loads past the end
-        // are never used; a conditional load would make the ring slot's old
-        // value need a copy while it is still being consumed). The final
-        // group issues no loads.
-        if (nsteps - s0 > PD) {
-            if (s0 != 0 && s0 % spc == 0) {
-                __syncthreads();
-                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
-                               min(spc, nsteps - s0) * kStep);
-                __syncthreads();
-            }
-            const _Float16* bp = bp0 + (s0 % spc) * kStep;
-#pragma unroll
-            for (int j = 0; j < PD; ++j) {
-                Codes<NW> cur[NMAT];
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    cur[m] = buf[m][j];
-                    buf[m][j] = C::load(ap[m], (int64_t)min(s0 + j + PD, nsteps - 1) * SB, loff, plane);
-                }
-                C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
-            }
-            s0 += PD;
-        }
-        if (s0 < nsteps) {
-            if (s0 != 0 && s0 % spc == 0) {
-                __syncthreads();
-                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + s0) * kStep,
-                               min(spc, nsteps - s0) * kStep);
-                __syncthreads();
-            }
-            const _Float16* bp = bp0 + (s0 % spc) * kStep;
-#pragma unroll
-            for (int j = 0; j < PD; ++j) {
-                if (s0 + j < nsteps) {
-                    Codes<NW> cur[NMAT];
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m) cur[m] = buf[m][j];
-                    C::template mma<NMAT>(cur, bp + j * kStep, acc, dc);
-                }
-            }
-        }
+        for (int nb = 0; nb < NB; ++nb) bp0[nb] = xs + min(16 * nb + r, nt - 1) * stride + 32 * g;
+        // the output of row block i, from the accumulators
         // D layout: lane (n = lane % 16, g = lane / 16) holds rows 4g..4g+3, token n
-        if (r < nt) {
-            const int orow = row0 + 4 * g;
-            if constexpr (MODE == 0) {
-                union {
-                    uint2 u;
-                    _Float16 h[4];
-                } hv;
-                const xsc::GateUpScale gs = xsc::gate_up_scale(s, C::kQmax, my_xs);
+        auto write_out = [&](int i) {
+            const int orow = row0 + 16 * i + 4 * g;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) hv.h[v] = (_Float16)xsc::swiglu_scaled(acc[0][v], acc[1][v], gs);
-                *reinterpret_cast<uint2*>(a.w.H + (int64_t)my_pair * a.F + orow) = hv.u;
-            } else {
-                const int m = xsc::h_exponent(s, C::kQmax, my_xs);
-                float4 o;
-                o.x = ldexpf(s * acc[0][0], m);
-                o.y = ldexpf(s * acc[0][1], m);
-                o.z = ldexpf(s * acc[0][2], m);
-                o.w = ldexpf(s * acc[0][3], m);
-                *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + my_pair) * a.d + orow) = o;
+            for (int nb = 0; nb < NB; ++nb) {
+                if (16 * nb + r >= nt) continue;
+                if constexpr (MODE == 0) {
+                    union {
+                        uint2 u;
+                        _Float16 h[4];
+                    } hv;
+                    const xsc::GateUpScale gs = xsc::gate_up_scale(s, C::kQmax, my_xs[nb]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        hv.h[v] = (_Float16)xsc::swiglu_scaled(acc[0][nb][v], acc[1][nb][v], gs);
+                    *reinterpret_cast<uint2*>(a.w.H + (int64_t)my_pair[nb] * a.F + orow) = hv.u;
+                } else {
+                    const int m = xsc::h_exponent(s, C::kQmax, my_xs[nb]);
+                    float4 o;
+                    o.x = ldexpf(s * acc[0][nb][0], m);
+                    o.y = ldexpf(s * acc[0][nb][1], m);
+                    o.z = ldexpf(s * acc[0][nb][2], m);
+                    o.w = ldexpf(s * acc[0][nb][3], m);
+                    *reinterpret_cast<float4*>(a.w.O + ((int64_t)sp * a.P + my_pair[nb]) * a.d + orow) = o;
+                }
             }
+        };
+        // the compute cursor: step within its row block, the block, and the
+        // step's offset in the staged chunk (without row-block sequences a
+        // group's steps sit at fixed offsets from the group's: immediate
+        // offsets of its LDS reads)
+        int cs = 0, ci = 0, cbo = 0;
+        auto compute_step = [&](const Codes<NW> (&cur)[NMAT], int j) {
+            const int off = kSeq ? cbo : cbo + j * kStep;
+            const _Float16* bq[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) bq[nb] = bp0[nb] + off;
+            C::template mma<NMAT, NB>(cur, bq, acc, nblk, dc);
+            if constexpr (kSeq) {
+                if (cs == nsteps - 1) {
+                    write_out(ci);
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    ++ci;
+                    cs = 0;
+                    cbo = 0;
+                } else {
+                    ++cs;
+                    cbo += kStep;
+                    if (cbo == spc * kStep) cbo = 0;   // next LDS chunk (one row block)
+                }
+            }
+        };
+        // after a group of PD steps, in a single row block
+        auto next_group = [&]() {
+            if constexpr (!kSeq) {
+                cs += PD;
+                cbo += PD * kStep;
+                if (cbo == spc * kStep) cbo = 0;
+            }
+        };
+        // a new LDS chunk of the token rows at a group's start (rpw is 1 when
+        // K is staged in chunks, and chunks hold whole groups)
+        auto restage = [&](int f0) {
+            if (spc < nsteps && f0 != 0 && cbo == 0) {
+                __syncthreads();
+                stage<MODE, C>(xs, stride, a, tok, prs, nt, (ks0 + cs) * kStep, min(spc, nsteps - cs) * kStep, tid);
+                __syncthreads();
+            }
+        };
+        int f0 = 0;
+        for (; total - f0 > PD; f0 += PD) {
+            restage(f0);
+            // each slot's codes are consumed before its next load is issued
+            // into the same registers (a load issued first would need
+            // registers of its own, and the ring copied between them, after
+            // a wait for every load in flight, at the loop's end)
+#pragma unroll
+            for (int j = 0; j < PD; ++j) {
+                compute_step(buf[j], j);
+                load_step(buf[j]);
+            }
+            next_group();
         }
+        // the final group issues no loads
+        restage(f0);
+#pragma unroll
+        for (int j = 0; j < PD; ++j)
+            if (f0 + j < total) compute_step(buf[j], j);
+        if constexpr (!kSeq) write_out(0);
     }
 }
 
-// grid: (routed expert slot, 64-row tile, K split) flattened; slots beyond
-// the device-side routed count exit at once. The slot's expert comes from
-// the router's active list (arrival order); its page-table entry, pair count
-// and first 16 pairs are then read in one round of independent loads (the
-// pair list has room for at least 16 entries).
-// PLANES: bitplane pages (a kernel of its own, so that the Eq. 2 kernel's
-// register allocation does not depend on the bitplane decoding).
-template <int MODE, bool PLANES>
-__global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles,
-                                                                          int nsplit) {
-    extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-    __shared__ int tok[16];   // token of each pair of the current block
-    __shared__ int prs[16];   // the pairs t k + j of the current block
-    const int per_expert = tiles * nsplit;
-    const int ai = blockIdx.x / per_expert;
+// One workgroup's share of an expert: row tile rt, K split sp. PLANES:
+// bitplane pages (a kernel of its own, so that the Eq. 2 kernel's register
+// allocation does not depend on the bitplane decoding).
+template <int MODE, bool PLANES, int NB>
+__device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, int e, int rem,
+                                         _Float16* xs, int* tok, int* prs) {
     const DecodeGroup& dg = a.w.dg;
-    const int e = dg.act[ai];   // stale past the routed count, not used then
-    if (ai >= dg.n_act[0]) return;
-    const int rem = blockIdx.x - ai * per_expert;
     const int rt = rem / nsplit, sp = rem - rt * nsplit;
     const int32_t* list = dg.list + (int64_t)e * a.w.tcap;
     const int b = a.tab.bits[e];
@@ -552,32 +603,169 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 5) void ffn_kernel(FfnArg
     if constexpr (PLANES) {
         // bitplane pages: b is the depth, 1 .. 8 planes
         switch (b) {
-            case 1: ffn_tile<MODE, PlaneCodec<1>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 2: ffn_tile<MODE, PlaneCodec<2>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 3: ffn_tile<MODE, PlaneCodec<3>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 4: ffn_tile<MODE, PlaneCodec<4>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 5: ffn_tile<MODE, PlaneCodec<5>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 6: ffn_tile<MODE, PlaneCodec<6>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            case 7: ffn_tile<MODE, PlaneCodec<7>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
-            default: ffn_tile<MODE, PlaneCodec<8>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs); break;
+            case 1: ffn_tile<MODE, PlaneCodec<1>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 2: ffn_tile<MODE, PlaneCodec<2>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 3: ffn_tile<MODE, PlaneCodec<3>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 4: ffn_tile<MODE, PlaneCodec<4>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 5: ffn_tile<MODE, PlaneCodec<5>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 6: ffn_tile<MODE, PlaneCodec<6>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 7: ffn_tile<MODE, PlaneCodec<7>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            default: ffn_tile<MODE, PlaneCodec<8>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
         }
     } else {
-        if (b == 4) ffn_tile<MODE, Eq2Codec<4>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
-        else if (b == 8) ffn_tile<MODE, Eq2Codec<8>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
-        else ffn_tile<MODE, Eq2Codec<3>>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, xs, tok, prs);
+        if (b == 4) ffn_tile<MODE, Eq2Codec<4>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
+        else if (b == 8) ffn_tile<MODE, Eq2Codec<8>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
+        else ffn_tile<MODE, Eq2Codec<3>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
     }
+}
+
+// Experts that receive more than 16 tokens are served by wide passes,
+// kWideNB blocks of 16 tokens per pass over their codes: every code is read
+// once per 16 kWideNB tokens instead of once per 16. Both kinds share the
+// launch's LDS; a wide pass holds its token rows two steps at a time.
+constexpr int kWideNB = 4;
+
+// Experts with more than 16 tokens ("hot") among the routed ones, found by
+// one wave scanning the routed list (arrival order) with ballots; every
+// lane gets the same answer.
+// hot_expert: the h-th hot expert (0-based), or -1 if there are fewer.
+__device__ __forceinline__ int hot_expert(const DecodeGroup& dg, int h) {
+    const int lane = threadIdx.x & 63;
+    const int n = dg.n_act[0];
+    int seen = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int idx = base + lane;
+        const int e = idx < n ? dg.act[idx] : 0;
+        const bool hot = idx < n && dg.cnt[e] > 16;
+        const uint64_t m = __ballot(hot);
+        const int c = __popcll(m);
+        if (seen + c > h) {
+            // the (h - seen)-th set bit of m
+            uint64_t mm = m;
+            for (int i = 0; i < h - seen; ++i) mm &= mm - 1;
+            return __shfl(e, __ffsll((unsigned long long)mm) - 1);
+        }
+        seen += c;
+    }
+    return -1;
+}
+
+// hot_rank: how many hot experts come before routed slot ai.
+__device__ __forceinline__ int hot_rank(const DecodeGroup& dg, int ai) {
+    const int lane = threadIdx.x & 63;
+    int seen = 0;
+    for (int base = 0; base < ai; base += 64) {
+        const int idx = base + lane;
+        const bool hot = idx < ai && dg.cnt[dg.act[idx]] > 16;
+        seen += __popcll(__ballot(hot));
+    }
+    return seen;
+}
+
+// Hot experts whose tiles beyond the routed slot's own get workgroups of
+// their own when a workgroup covers several row tiles.
+constexpr int kHotExtra = 16;
+
+// grid: `extra` workgroups for hot experts, then (routed expert slot, 64
+// rpw-row tile, K split) flattened; slots past the device-side routed count
+// exit at once. The slot's expert comes from the router's list (arrival
+// order); its page-table entry, pair count and first 16 pairs are then read
+// in one round of independent loads (the pair list has room for at least 16
+// entries). wide (set when the batch has more than 16 tokens): an expert may
+// be hot; a hot expert's 64-row tiles take wide passes, one tile per
+// workgroup. With rpw = 1 that is its routed workgroups; with rpw > 1 its
+// routed workgroups take its first tiles/rpw tiles and, for the first
+// kHotExtra hot experts, the extra workgroups the rest; a later hot expert
+// keeps the passes of 16 tokens over its workgroups' rpw-tile sequences.
+template <int MODE, bool PLANES>
+__global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles,
+                                                                          int nsplit, int rpw, int extra) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+    __shared__ int tok[16 * kWideNB];   // token of each pair of the current pass
+    __shared__ int prs[16 * kWideNB];   // the pairs t k + j of the current pass
+    const DecodeGroup& dg = a.w.dg;
+    const int own = tiles / rpw;   // 64-row tiles of a hot expert its routed workgroups take
+    if ((int)blockIdx.x < extra) {
+        const int per = (tiles - own) * nsplit;
+        const int h = blockIdx.x / per;
+        const int e = hot_expert(dg, h);
+        if (e < 0) return;
+        ffn_role<MODE, PLANES, kWideNB>(a, lds_bytes, nsplit, 1, e, own * nsplit + (blockIdx.x - h * per), xs,
+                                        tok, prs);
+        return;
+    }
+    const int blk = blockIdx.x - extra;
+    const int per_expert = own * nsplit;
+    const int ai = blk / per_expert;
+    const int e = dg.act[ai];   // stale past the routed count, not used then
+    if (ai >= dg.n_act[0]) return;
+    const int rem = blk - ai * per_expert;
+    if (a.wide && dg.cnt[e] > 16 && (rpw == 1 || hot_rank(dg, ai) < kHotExtra))
+        ffn_role<MODE, PLANES, kWideNB>(a, lds_bytes, nsplit, 1, e, rem, xs, tok, prs);
+    else
+        ffn_role<MODE, PLANES, 1>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
+}
+
+// Resident workgroups of a kernel per CU at an LDS size, and the CU count
+// (cached: the occupancy query is host arithmetic, but not free).
+int resident_blocks(const void* kernel, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find({kernel, lds});
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, lds) != hipSuccess || n < 1) n = 1;
+    cache[{kernel, lds}] = n;
+    return n;
+}
+
+int cu_count() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return kCUs;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = kCUs;
+    cache[dev] = n;
+    return n;
+}
+
+template <int MODE, bool PLANES>
+hipError_t launch_ffn_k(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
+    const int rows = MODE == 0 ? a.F : a.d;
+    const int tiles = rows / 64;
+    // a wide pass stages 64 token rows of at least two steps (or of the
+    // whole K range if shorter): 33,792 bytes at most
+    size_t lds = p.lds;
+    if (a.wide) {
+        const int k = (MODE == 0 ? a.d : a.F) / p.nsplit;
+        lds = std::max(lds, (size_t)16 * kWideNB * (std::min(k, 2 * kStep) + 8) * 2);
+    }
+    auto kernel = ffn_kernel<MODE, PLANES>;
+    const int64_t slots = (int64_t)resident_blocks(reinterpret_cast<const void*>(kernel), lds) * cu_count();
+    // row blocks per wave (the down product, when the LDS holds all of K):
+    // the most that still give every resident workgroup an item when all
+    // max_act experts are routed
+    int rpw = 1;
+    if (MODE == 1 && p.whole_k) {
+        for (int r = 2; r <= 8; r *= 2) {
+            if (tiles % r || (int64_t)a.max_act * (tiles / r) * p.nsplit < slots) break;
+            rpw = r;
+        }
+    }
+    const int extra = (a.wide && rpw > 1) ? kHotExtra * (tiles - tiles / rpw) * p.nsplit : 0;
+    const dim3 grid((unsigned)((int64_t)a.max_act * (tiles / rpw) * p.nsplit + extra));
+    return launch_timed(kernel, grid, dim3(kThreads), lds, s, t.start, t.stop, a, (int)lds, tiles, p.nsplit, rpw,
+                        extra);
 }
 
 template <int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
-    const int rows = MODE == 0 ? a.F : a.d;
-    const int tiles = rows / 64;
-    const dim3 grid((unsigned)(a.max_act * tiles * p.nsplit));
-    if (a.bitplane)
-        return launch_timed(ffn_kernel<MODE, true>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
-                            (int)p.lds, tiles, p.nsplit);
-    return launch_timed(ffn_kernel<MODE, false>, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a,
-                        (int)p.lds, tiles, p.nsplit);
+    return a.bitplane ? launch_ffn_k<MODE, true>(a, p, s, t) : launch_ffn_k<MODE, false>(a, p, s, t);
 }
 
 // Partial outputs are read once: non-temporal loads (17% faster for 4096
@@ -649,7 +837,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
 
 // LDS for the staged token rows: all of the K range for up to min(T, 16)
 // tokens if that fits 34 KB, else 34 KB (the kernel then stages K in chunks
-// sized by the expert's actual token count).
+// sized by the pass's actual token count; a wide pass of 64 tokens holds at
+// least two steps: 64 x 264 halves fit).
 FfnPlan plan_ffn(int K, int T, int nsplit) {
     FfnPlan p;
     p.nt_alloc = T < 16 ? (T < 1 ? 1 : T) : 16;
@@ -661,6 +850,7 @@ FfnPlan plan_ffn(int K, int T, int nsplit) {
     const size_t floor_bytes = (size_t)16 * (8 * kStep + 8) * 2;
     const size_t cap = 34 * 1024 > floor_bytes ? 34 * 1024 : floor_bytes;
     p.lds = full < cap ? full : cap;
+    p.whole_k = full <= cap;
     return p;
 }
 

@@ -146,6 +146,7 @@ struct FfnPlan {
     int nt_alloc;     // token rows the LDS is sized for
     int nsplit;       // workgroups along K (down product only)
     size_t lds;       // dynamic LDS bytes
+    bool whole_k;     // the LDS holds every K step of nt_alloc token rows
 };
 FfnPlan plan_ffn(int K, int T, int nsplit);
 // K-splits of the down product for a layer (partials summed by the combine)
@@ -164,6 +165,7 @@ struct FfnArgs {
     int d, F, k, max_act;
     int P;               // pair stride of the split partial outputs O[split][P][d]
     int bitplane;        // 1: bitplane pages (the table's bits are depths 1..8)
+    int wide;            // 1: an expert may have more than 16 tokens (wide passes)
 };
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});

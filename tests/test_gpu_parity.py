@@ -412,6 +412,57 @@ def test_large_batch_matrix_core_path(T):
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
 
 
+@pytest.mark.parametrize("layout", ["eq2", "bitplane"])
+def test_skewed_routing_on_the_streaming_path(layout):
+    """Importance-skewed routing of a decode batch: expert 0 takes all 150
+    tokens (three passes of 64 in the kernel for experts with more than 16
+    tokens), experts 1-3 between 17 and 64, the rest few or none; every
+    output against the oracle."""
+    from oracle import bitplane
+    wl = synth.WORKLOADS["decode_fine"].scaled(name=f"skew_{layout}", E=16, d=256, F=384, k=2, T=150)
+    masters = synth.expert_weights(wl)
+    layer, _ = make_layer(wl, masters, max_tokens=wl.T, layout=layout)
+    bits = [8, 4, 3, 4, 8, 3, 4, 3, 3, 4, 8, 3, 4, 4, 3, 8]
+    layer.quantize_experts(bits)
+    x, logits = synth.tokens(wl)
+    logits[:, 0] += 20.0                       # every token's first expert
+    logits[:40, 1] += 10.0
+    logits[40:90, 2] += 10.0
+    logits[90:110, 3] += 10.0
+    counts = torch.bincount(moe.route(logits, wl.k)[0].reshape(-1), minlength=wl.E)
+    assert int(counts[0]) == 150 and 16 < int(counts[1]) <= 64 and int(counts[3]) > 16
+    log(f"skewed ({layout}): counts {counts.tolist()}")
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    if layout == "eq2":
+        ref = oracle_y(x, logits, wl, masters, bits)
+    else:
+        ref = moe.forward(x.float(), logits, wl.k, bitplane.experts(*masters, bits))
+    compare_y(y, ref, f"skewed routing ({layout})")
+
+
+def test_hot_experts_on_multi_tile_workgroups():
+    """A layer wide enough (128 experts, d_model 2048) that each workgroup of
+    the down product covers several 64-row tiles: six experts take more than
+    16 tokens each (the first four get extra workgroups for their remaining
+    tiles, the last two keep passes of 16 tokens over their tile
+    sequences), the rest few; d_ff = 384 gives three K steps per tile, so
+    several tiles end inside one prefetch group. Every output against the
+    oracle."""
+    wl = synth.WORKLOADS["decode_fine"].scaled(name="hot_multi_tile", E=128, d=2048, F=384, k=2, T=200)
+    masters = synth.expert_weights(wl)
+    layer, _ = make_layer(wl, masters, max_tokens=wl.T)
+    bits = [(8, 4, 3)[e % 3] for e in range(wl.E)]
+    layer.quantize_experts(bits)
+    x, logits = synth.tokens(wl)
+    for h in range(6):
+        logits[30 * h:30 * h + 30, 7 * h + 1] += 10.0   # expert 7h+1: 30 tokens
+    counts = torch.bincount(moe.route(logits, wl.k)[0].reshape(-1), minlength=wl.E)
+    assert int((counts > 16).sum()) == 6
+    log(f"hot experts {torch.nonzero(counts > 16).reshape(-1).tolist()}, counts {counts[counts > 16].tolist()}")
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, bits), "hot experts, multi-tile workgroups")
+
+
 def test_small_batches_on_a_context_sized_for_large_ones():
     """A context whose workspace is sized for 2048 tokens (its partial-output
     buffer holds one split per pair) still splits the down product of a

@@ -90,6 +90,23 @@ def test_decode_fine_full():
     compare_y(y, oracle_y(x.cpu(), logits.cpu(), wl, host, bits), "decode_fine T=64")
 
 
+def test_decode_fine_skewed_full():
+    """decode_fine with routing skewed by importance (logits + log p_e, as
+    the benchmark's skewed line): the most important experts take far more
+    than 16 of the 64 tokens. Every output against the oracle."""
+    wl, layer, pool, host, L = layer_for("decode_fine", max_tokens=64)
+    bits = layer.set_budget(wl.budget_bits(), synth.importance(wl))
+    want, _ = alloc.solve(synth.importance(wl), L.tolist(), [wl.W_e] * wl.E, wl.budget_bits())
+    assert bits.tolist() == want
+    x, logits = synth.tokens(wl, device="cuda", seed=2)
+    logits = logits + torch.log(torch.tensor(synth.importance(wl), dtype=torch.float32, device="cuda"))
+    counts = torch.bincount(torch.topk(logits, wl.k, dim=1).indices.reshape(-1), minlength=wl.E)
+    log(f"  experts with more than 16 tokens: {int((counts > 16).sum())}, largest {int(counts.max())}")
+    assert int((counts > 16).sum()) > 4
+    y = layer.moe_forward(x, logits)
+    compare_y(y, oracle_y(x.cpu(), logits.cpu(), wl, host, bits), "decode_fine skewed T=64")
+
+
 def test_prefill_full():
     wl, layer, pool, host, L = layer_for("prefill", max_tokens=4096)
     check_loss_rows(layer, host, L, [0, 33, 63])

@@ -74,7 +74,7 @@ def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
     src = "kernels_gemm.hip" if workload == "prefill" else "kernels_ffn.hip"
-    for f in (src, "pw_internal.h", "dequant.h"):
+    for f in (src, "pw_internal.h", "dequant.h", "xscale.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -500,15 +500,23 @@ def main():
         # the other configurations, each on its own layer (one at a time on
         # the device)
         wls = {}
-        for key, w, bias, layout in (("decode_fine_T64", synth.WORKLOADS["decode_fine"], None, "eq2"),
-                                     ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew", "eq2"),
-                                     ("decode_fine_bitplane_T64", synth.WORKLOADS["decode_fine"], None, "bitplane"),
-                                     ("prefill_T4096", synth.WORKLOADS["prefill"], None, "eq2")):
+        for key, w, bias, layout, prof in (
+                ("decode_fine_T64", synth.WORKLOADS["decode_fine"], None, "eq2", "decode_fine"),
+                ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew", "eq2", "skewed"),
+                ("decode_fine_bitplane_T64", synth.WORKLOADS["decode_fine"], None, "bitplane", None),
+                ("prefill_T4096", synth.WORKLOADS["prefill"], None, "eq2", "prefill")):
             t0 = time.time()
-            res, _, _, _ = measure(w, w.T, args, log, 2 if w.name == "prefill" else args.pools,
-                                   skew_bias(w) if bias else None, layout=layout)
+            res, _, _, gu_bytes = measure(w, w.T, args, log, 2 if w.name == "prefill" else args.pools,
+                                          skew_bias(w) if bias else None, layout=layout)
             if bias:
                 res["routing"] = "logits + log p_e (Zipf 1.1 importance)"
+            # HBM bytes per gate/up launch from the committed counter summary
+            # (null once the kernel sources changed), and its ratio to the
+            # packed code bytes of the routed experts (decode)
+            traffic = traffic_from_profiles(prof, w.T) if prof else None
+            res["gate_up_traffic_bytes"] = traffic
+            if traffic and w.name != "prefill":
+                res["gate_up_traffic_over_code_bytes"] = traffic / gu_bytes
             wls[key] = res
             log(f"{key}: {res['tokens_per_s']:.0f} tokens/s ({time.time() - t0:.1f}s)")
         t0 = time.time()

@@ -64,9 +64,9 @@ __device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, int e
     if (slot == 0) g.act[atomicAdd(g.n_act, 1)] = e;
 }
 
-template <int PER>
+template <int PER, class Pre>
 __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork& w, int t,
-                                              int* s_ids, bool group) {
+                                              int* s_ids, bool group, Pre&& pre) {
     const int lane = threadIdx.x & 63;
     const float* row = a.logits + (int64_t)t * a.E;
     float v[PER];
@@ -75,6 +75,7 @@ __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork&
         const int e = lane + 64 * i;
         v[i] = e < a.E ? row[e] : -INFINITY;
     }
+    pre();
     int my_id = 0;
     float my_val = -INFINITY, top = -INFINITY;
     uint32_t taken = 0;   // bit i: v[i] already chosen
@@ -176,9 +177,12 @@ __device__ __forceinline__ uint64_t row_max_key(uint64_t k) {
 // the row call it with the same t; `valid` false for a row past the batch).
 // Top-k: k rounds of the row's largest key, each removed from its lane; the
 // softmax weights use the native base-2 exponential of (v - top) log2(e).
-template <int PER>
+// pre() runs after the logits loads are issued and before they are used
+// (the streaming router takes the token's activation statistics there, so
+// that both rows' loads are in flight together).
+template <int PER, class Pre>
 __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w, int t, bool valid,
-                                            int* s_ids, bool group) {
+                                            int* s_ids, bool group, Pre&& pre) {
     const int l16 = threadIdx.x & 15;
     const float* row = a.logits + (int64_t)t * a.E;
     float v[PER];
@@ -186,9 +190,13 @@ __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = l16 + 16 * i;
-        const bool in = valid && e < a.E;
-        v[i] = in ? row[e] : -INFINITY;
-        key[i] = in ? route_key(v[i], e) : 0ull;
+        v[i] = (valid && e < a.E) ? row[e] : -INFINITY;
+    }
+    pre();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = l16 + 16 * i;
+        key[i] = (valid && e < a.E) ? route_key(v[i], e) : 0ull;
     }
     int id0 = 0, id1 = 0;
     float val0 = -INFINITY, val1 = -INFINITY, top = -INFINITY;
@@ -230,24 +238,30 @@ __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w
     }
 }
 
+struct NoPre {
+    __device__ void operator()() const {}
+};
+
+template <class Pre = NoPre>
 __device__ __forceinline__ void route_row(const RouteArgs& a, const FwdWork& w, int t, bool valid, int* s_ids,
-                                          bool group = false) {
+                                          bool group = false, Pre&& pre = Pre{}) {
     const int per = (a.E + 15) / 16;
-    if (per == 1) route_row_t<1>(a, w, t, valid, s_ids, group);
-    else if (per == 2) route_row_t<2>(a, w, t, valid, s_ids, group);
-    else if (per <= 4) route_row_t<4>(a, w, t, valid, s_ids, group);
-    else if (per <= 8) route_row_t<8>(a, w, t, valid, s_ids, group);
-    else route_row_t<16>(a, w, t, valid, s_ids, group);
+    if (per == 1) route_row_t<1>(a, w, t, valid, s_ids, group, pre);
+    else if (per == 2) route_row_t<2>(a, w, t, valid, s_ids, group, pre);
+    else if (per <= 4) route_row_t<4>(a, w, t, valid, s_ids, group, pre);
+    else if (per <= 8) route_row_t<8>(a, w, t, valid, s_ids, group, pre);
+    else route_row_t<16>(a, w, t, valid, s_ids, group, pre);
 }
 
+template <class Pre = NoPre>
 __device__ __forceinline__ void route_token(const RouteArgs& a, const FwdWork& w, int t, int* s_ids,
-                                            bool group = false) {
+                                            bool group = false, Pre&& pre = Pre{}) {
     const int per = (a.E + 63) / 64;
-    if (per == 1) route_token_t<1>(a, w, t, s_ids, group);
-    else if (per == 2) route_token_t<2>(a, w, t, s_ids, group);
-    else if (per <= 4) route_token_t<4>(a, w, t, s_ids, group);
-    else if (per <= 8) route_token_t<8>(a, w, t, s_ids, group);
-    else route_token_t<16>(a, w, t, s_ids, group);
+    if (per == 1) route_token_t<1>(a, w, t, s_ids, group, pre);
+    else if (per == 2) route_token_t<2>(a, w, t, s_ids, group, pre);
+    else if (per <= 4) route_token_t<4>(a, w, t, s_ids, group, pre);
+    else if (per <= 8) route_token_t<8>(a, w, t, s_ids, group, pre);
+    else route_token_t<16>(a, w, t, s_ids, group, pre);
 }
 
 // Statistics of an activation row (xscale.h) by a group of L lanes (16: a
@@ -267,8 +281,11 @@ __device__ __forceinline__ XStat lanes_stat(const uint16_t* row, int d) {
     const int li = threadIdx.x & (L - 1);
     const uint4* r = reinterpret_cast<const uint4*>(row);
     uint32_t mx = 0;
-    double sum = 0.0;
-#pragma unroll 4
+    // eight independent partial sums (one per activation of a chunk): a
+    // single running sum made the fp64 adds one dependent chain per lane,
+    // most of the router's time at d_model 4096
+    double part[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
     for (int c = li; c < d / 8; c += L) {
         const uint4 u = r[c];
         const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
@@ -276,9 +293,11 @@ __device__ __forceinline__ XStat lanes_stat(const uint16_t* row, int d) {
         for (int h = 0; h < 4; ++h) {
             const uint32_t lo = ww[h] & 0x7fffu, hi = (ww[h] >> 16) & 0x7fffu;
             mx = max(mx, max(lo, hi));
-            sum += (double)__uint_as_float(lo << 16) + (double)__uint_as_float(hi << 16);
+            part[2 * h] += (double)__uint_as_float(lo << 16);
+            part[2 * h + 1] += (double)__uint_as_float(hi << 16);
         }
     }
+    double sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
     mx = max(mx, (uint32_t)dpp_i<kQuadXor1>((int)mx));
     sum += dpp_d<kQuadXor1>(sum);
     mx = max(mx, (uint32_t)dpp_i<kQuadXor2>((int)mx));
@@ -559,30 +578,36 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 }
 
 // ---- streaming kernels: top-k, grouping by atomics, token statistics ----
-// grid ceil(T / 4) (E <= 256: row r of block b handles token 4b + r) or T (a
-// wave per token), 64 threads. Block 0 also clears the other counter set for
-// the next forward (every kernel of the previous forward, which used it, has
+// grid ceil(T / 4), 256 threads: wave w of block b takes the statistics of
+// token 4b + w (all 64 lanes load the row at once); with at most 256 experts
+// wave 0 also routes the block's four tokens (row r of 16 lanes: token
+// 4b + r), issuing its logits loads before its statistics, else each wave
+// routes its own token. Block 0 also clears the other counter set for the
+// next forward (every kernel of the previous forward, which used it, has
 // finished).
-__global__ __launch_bounds__(64) void route_decode_kernel(RouteArgs a, FwdWork w) {
+__global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork w) {
     if (blockIdx.x == 0) {
-        for (int e = threadIdx.x; e < a.E; e += 64) w.dg_next.cnt[e] = 0;
+        for (int e = threadIdx.x; e < a.E; e += 256) w.dg_next.cnt[e] = 0;
         if (threadIdx.x == 0) w.dg_next.n_act[0] = 0;
     }
+    const int wave = threadIdx.x >> 6;
+    const int ts = blockIdx.x * 4 + wave;   // this wave's token for the statistics
+    auto stats = [&]() {
+        if (a.x && ts < a.T) {
+            const XStat st = lanes_stat<64>(a.x + (int64_t)ts * a.d, a.d);
+            if ((threadIdx.x & 63) == 0) w.xst[ts] = st;
+        }
+    };
     if (a.E <= kRowMaxExperts) {
-        const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
-        const bool valid = t < a.T;
-        route_row(a, w, valid ? t : a.T - 1, valid, nullptr, true);
-        if (valid && a.x) {
-            const XStat st = lanes_stat<16>(a.x + (int64_t)t * a.d, a.d);
-            if ((threadIdx.x & 15) == 0) w.xst[t] = st;
+        if (wave == 0) {
+            const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
+            const bool valid = t < a.T;
+            route_row(a, w, valid ? t : a.T - 1, valid, nullptr, true, stats);
+        } else {
+            stats();
         }
-    } else {
-        const int t = blockIdx.x;
-        route_token(a, w, t, nullptr, true);
-        if (a.x) {
-            const XStat st = lanes_stat<64>(a.x + (int64_t)t * a.d, a.d);
-            if (threadIdx.x == 0) w.xst[t] = st;
-        }
+    } else if (ts < a.T) {
+        route_token(a, w, ts, nullptr, true, stats);
     }
 }
 
@@ -654,8 +679,8 @@ hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
 }
 
 hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
-    const int blocks = a.E <= kRowMaxExperts ? (a.T + 3) / 4 : a.T;
-    return launch_timed(route_decode_kernel, dim3((unsigned)blocks), dim3(64), 0, s, t.start, t.stop, a, w);
+    return launch_timed(route_decode_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, t.start, t.stop, a,
+                        w);
 }
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,

@@ -43,6 +43,10 @@ namespace {
 constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / 64;
 constexpr int kRowMaxExperts = 256;             // 16 lanes per token up to this many experts
+// The streaming router takes the 16-lane rows only up to this many experts
+// (a wave per token beyond: fewer keys per lane, shorter rounds; 128 experts
+// x top-8 routed 2 us faster)
+constexpr int kRowDecodeMaxExperts = 64;
 // One workgroup routes and groups up to this many tokens (one pass of its
 // 64 rows of 16 lanes with at most 256 experts, one token per wave else);
 // beyond, the top-k is spread over many workgroups and only the grouping
@@ -54,8 +58,6 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
     return v > v2 || (v == v2 && e < e2);
 }
 
-// One wave routes token t: writes ids/g (and the ids to s_ids if given).
-// PER = logits held per lane (ceil(E / 64)).
 // The decode grouping of pair p = t k + j routed to expert e: the next
 // position of e's list; the expert's first pair appends it to the active list.
 __device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, int e, int p) {
@@ -64,66 +66,16 @@ __device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, int e
     if (slot == 0) g.act[atomicAdd(g.n_act, 1)] = e;
 }
 
-template <int PER, class Pre>
-__device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork& w, int t,
-                                              int* s_ids, bool group, Pre&& pre) {
-    const int lane = threadIdx.x & 63;
-    const float* row = a.logits + (int64_t)t * a.E;
-    float v[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < a.E ? row[e] : -INFINITY;
-    }
-    pre();
-    int my_id = 0;
-    float my_val = -INFINITY, top = -INFINITY;
-    uint32_t taken = 0;   // bit i: v[i] already chosen
-    for (int j = 0; j < a.k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = lane + 64 * i;
-            if (e < a.E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-                bv = v[i];
-                be = e;
-            }
-        }
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o);
-            const int oe = __shfl_xor(be, o);
-            if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (j == 0) top = bv;
-        if (lane == j) { my_id = be; my_val = bv; }
-    }
-    float sum_all = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        if (e < a.E) sum_all += expf(v[i] - top);
-    }
-    const float mine = lane < a.k ? expf(my_val - top) : 0.0f;
-    float den = a.renorm ? mine : sum_all;
-    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
-    if (lane < a.k) {
-        w.ids[(int64_t)t * a.k + lane] = my_id;
-        w.g[(int64_t)t * a.k + lane] = mine / den;
-        if (s_ids) s_ids[t * a.k + lane] = my_id;
-        if (group) group_pair(w.dg, w.tcap, my_id, t * a.k + lane);
-    }
-}
-
 // ---- 16 lanes per token (E <= 256) ----
 // A row of 16 lanes routes one token; lane i of the row holds the logits of
 // experts i, i + 16, ... . Reductions across the row use DPP (quad
 // permutations, then the half-row and row mirrors), which leaves the row's
 // result in every lane of the row without a trip through LDS.
+// (every pattern used here reads a valid lane of the same row, so the
+// instruction needs no old value: bound_ctrl, and no copy of x to keep)
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -171,6 +123,91 @@ __device__ __forceinline__ uint64_t row_max_key(uint64_t k) {
     k = o > k ? o : k;
     o = dpp_u64<kRowMirror>(k);
     return o > k ? o : k;
+}
+
+// Wave-wide reductions: the row result (DPP, as above), then row 1 takes
+// row 0's (row_bcast:15) and row 3 row 2's, then rows 2 and 3 take row 1's
+// (row_bcast:31): lane 63 holds the wave's result, read into a scalar.
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    k = row_max_key(k);
+    uint64_t o = ((uint64_t)(uint32_t)dpp_rows_i<kRowBcast15, 0xa>((int)(uint32_t)(k >> 32)) << 32) |
+                 (uint32_t)dpp_rows_i<kRowBcast15, 0xa>((int)(uint32_t)k);
+    k = o > k ? o : k;
+    o = ((uint64_t)(uint32_t)dpp_rows_i<kRowBcast31, 0xc>((int)(uint32_t)(k >> 32)) << 32) |
+        (uint32_t)dpp_rows_i<kRowBcast31, 0xc>((int)(uint32_t)k);
+    k = o > k ? o : k;
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row_sum(x);
+    x += __builtin_bit_cast(float, dpp_rows_i<kRowBcast15, 0xa>(__builtin_bit_cast(int, x)));
+    x += __builtin_bit_cast(float, dpp_rows_i<kRowBcast31, 0xc>(__builtin_bit_cast(int, x)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// One wave routes token t (lane l holds the logits of experts l, l + 64,
+// ...): k rounds of the wave's largest (logit, expert) key, each removed from
+// its lane; the wave-wide results are scalars. Writes ids/g (and the ids to
+// s_ids if given); k <= 64. pre() runs after the logits loads are issued.
+template <int PER, class Pre>
+__device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork& w, int t, int* s_ids,
+                                              bool group, Pre&& pre) {
+    const int lane = threadIdx.x & 63;
+    const float* row = a.logits + (int64_t)t * a.E;
+    float v[PER];
+    uint64_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < a.E ? row[e] : -INFINITY;
+    }
+    pre();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < a.E ? route_key(v[i], e) : 0ull;
+    }
+    int my_id = 0;
+    float my_val = -INFINITY, top = -INFINITY;
+    for (int j = 0; j < a.k; ++j) {
+        // this lane's largest key (a tree over its keys), then the wave's
+        uint64_t m[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) m[i] = key[i];
+#pragma unroll
+        for (int h = 1; h < PER; h *= 2)
+#pragma unroll
+            for (int i = 0; i + h < PER; i += 2 * h) m[i] = m[i + h] > m[i] ? m[i + h] : m[i];
+        const uint64_t best = wave_max_key(m[0]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) key[i] = key[i] == best ? 0ull : key[i];
+        const float bv = key_value(best);
+        if (j == 0) top = bv;
+        if (lane == j) { my_id = key_expert(best); my_val = bv; }
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+    float sum_all = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        if (e < a.E) sum_all += __builtin_amdgcn_exp2f((v[i] - top) * kLog2e);
+    }
+    const float mine = lane < a.k ? __builtin_amdgcn_exp2f((my_val - top) * kLog2e) : 0.0f;
+    const float den = wave_sum(a.renorm ? mine : sum_all);
+    if (lane < a.k) {
+        w.ids[(int64_t)t * a.k + lane] = my_id;
+        w.g[(int64_t)t * a.k + lane] = mine / den;
+        if (s_ids) s_ids[t * a.k + lane] = my_id;
+        if (group) group_pair(w.dg, w.tcap, my_id, t * a.k + lane);
+    }
 }
 
 // The row of 16 lanes containing this thread routes token t (all lanes of
@@ -579,7 +616,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 
 // ---- streaming kernels: top-k, grouping by atomics, token statistics ----
 // grid ceil(T / 4), 256 threads: wave w of block b takes the statistics of
-// token 4b + w (all 64 lanes load the row at once); with at most 256 experts
+// token 4b + w (all 64 lanes load the row at once); with at most 64 experts
 // wave 0 also routes the block's four tokens (row r of 16 lanes: token
 // 4b + r), issuing its logits loads before its statistics, else each wave
 // routes its own token. Block 0 also clears the other counter set for the
@@ -598,7 +635,7 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork 
             if ((threadIdx.x & 63) == 0) w.xst[ts] = st;
         }
     };
-    if (a.E <= kRowMaxExperts) {
+    if (a.E <= kRowDecodeMaxExperts) {
         if (wave == 0) {
             const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
             const bool valid = t < a.T;

@@ -382,12 +382,16 @@ struct ExpertRef {
 // NB: blocks of 16 tokens per pass over the codes (1, or 4 for the experts
 // that receive more than 16 tokens, whose passes prefetch two steps, the
 // most of 64 token rows the LDS holds).
-// rpw: row blocks of 16 per wave (the down product's NB = 1 passes only; the
-// host picks rpw > 1 only when the LDS holds every step of the pass's token
-// rows). The wave walks
-// its rpw blocks' steps as one sequence, so that the prefetch ring runs on
-// across block boundaries; a block's output is written after its last step.
-template <int MODE, class C, int NB>
+// SEQ: 0, one 16-row block per wave (rpw = 1); 1, rpw row blocks of 16 per
+// wave (the down product's NB = 1 passes, picked when the LDS holds every
+// step of the pass's token rows), walked as one sequence of steps so that
+// the prefetch ring runs on across block boundaries; a block's output is
+// written right after its last step. (A compile-time choice: the sequence's
+// per-step bookkeeping costs the single-block case about 4%. Gate/up
+// sequences, their sums kept in LDS until after the loop, ran 10% slower on
+// the 128-expert decode layer: one round of longer workgroups, all starting
+// at once, against two rounds that overlap.)
+template <int MODE, class C, int NB, int SEQ>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const ExpertRef& ex, int rt, int sp,
                                          int ks0, int nsteps, int rpw, _Float16* xs, int* tok, int* prs) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
@@ -405,7 +409,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
-    constexpr bool kSeq = MODE == 1 && NB == 1;   // several row blocks per wave
+    static_assert(SEQ == 0 || (MODE == 1 && NB == 1), "row-block sequences: the down product's NB = 1 passes");
+    constexpr bool kSeq = SEQ != 0;   // several row blocks per wave
     const int R = kSeq ? rpw : 1;
     const int total = R * nsteps;   // steps of the wave's sequence
     const int row0 = (rt * 4 + wave) * R * 16;
@@ -535,8 +540,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
             if constexpr (kSeq) {
                 if (cs == nsteps - 1) {
                     write_out(ci);
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[0][0] = f32x4{0.f, 0.f, 0.f, 0.f};
                     ++ci;
                     cs = 0;
                     cbo = 0;
@@ -590,7 +594,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
 // One workgroup's share of an expert: row tile rt, K split sp. PLANES:
 // bitplane pages (a kernel of its own, so that the Eq. 2 kernel's register
 // allocation does not depend on the bitplane decoding).
-template <int MODE, bool PLANES, int NB>
+template <int MODE, bool PLANES, int NB, int SEQ>
 __device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, int e, int rem,
                                          _Float16* xs, int* tok, int* prs) {
     const DecodeGroup& dg = a.w.dg;
@@ -603,19 +607,19 @@ __device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int ns
     if constexpr (PLANES) {
         // bitplane pages: b is the depth, 1 .. 8 planes
         switch (b) {
-            case 1: ffn_tile<MODE, PlaneCodec<1>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 2: ffn_tile<MODE, PlaneCodec<2>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 3: ffn_tile<MODE, PlaneCodec<3>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 4: ffn_tile<MODE, PlaneCodec<4>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 5: ffn_tile<MODE, PlaneCodec<5>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 6: ffn_tile<MODE, PlaneCodec<6>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            case 7: ffn_tile<MODE, PlaneCodec<7>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
-            default: ffn_tile<MODE, PlaneCodec<8>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 1: ffn_tile<MODE, PlaneCodec<1>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 2: ffn_tile<MODE, PlaneCodec<2>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 3: ffn_tile<MODE, PlaneCodec<3>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 4: ffn_tile<MODE, PlaneCodec<4>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 5: ffn_tile<MODE, PlaneCodec<5>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 6: ffn_tile<MODE, PlaneCodec<6>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            case 7: ffn_tile<MODE, PlaneCodec<7>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
+            default: ffn_tile<MODE, PlaneCodec<8>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs); break;
         }
     } else {
-        if (b == 4) ffn_tile<MODE, Eq2Codec<4>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
-        else if (b == 8) ffn_tile<MODE, Eq2Codec<8>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
-        else ffn_tile<MODE, Eq2Codec<3>, NB>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
+        if (b == 4) ffn_tile<MODE, Eq2Codec<4>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
+        else if (b == 8) ffn_tile<MODE, Eq2Codec<8>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
+        else ffn_tile<MODE, Eq2Codec<3>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
     }
 }
 
@@ -677,7 +681,7 @@ constexpr int kHotExtra = 16;
 // routed workgroups take its first tiles/rpw tiles and, for the first
 // kHotExtra hot experts, the extra workgroups the rest; a later hot expert
 // keeps the passes of 16 tokens over its workgroups' rpw-tile sequences.
-template <int MODE, bool PLANES>
+template <int MODE, bool PLANES, int SEQ>
 __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles,
                                                                           int nsplit, int rpw, int extra) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
         const int h = blockIdx.x / per;
         const int e = hot_expert(dg, h);
         if (e < 0) return;
-        ffn_role<MODE, PLANES, kWideNB>(a, lds_bytes, nsplit, 1, e, own * nsplit + (blockIdx.x - h * per), xs,
+        ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, own * nsplit + (blockIdx.x - h * per), xs,
                                         tok, prs);
         return;
     }
@@ -701,9 +705,9 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
     if (ai >= dg.n_act[0]) return;
     const int rem = blk - ai * per_expert;
     if (a.wide && dg.cnt[e] > 16 && (rpw == 1 || hot_rank(dg, ai) < kHotExtra))
-        ffn_role<MODE, PLANES, kWideNB>(a, lds_bytes, nsplit, 1, e, rem, xs, tok, prs);
+        ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, rem, xs, tok, prs);
     else
-        ffn_role<MODE, PLANES, 1>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
+        ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
 }
 
 // Resident workgroups of a kernel per CU at an LDS size, and the CU count
@@ -745,18 +749,29 @@ hipError_t launch_ffn_k(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTime
         const int k = (MODE == 0 ? a.d : a.F) / p.nsplit;
         lds = std::max(lds, (size_t)16 * kWideNB * (std::min(k, 2 * kStep) + 8) * 2);
     }
-    auto kernel = ffn_kernel<MODE, PLANES>;
-    const int64_t slots = (int64_t)resident_blocks(reinterpret_cast<const void*>(kernel), lds) * cu_count();
-    // row blocks per wave (the down product, when the LDS holds all of K):
-    // the most that still give every resident workgroup an item when all
-    // max_act experts are routed
+    // rpw = 1: one row block per wave; rpw > 1 (the down product, when the
+    // LDS holds all of K): the sequence variant. Among 1, 2, 4, 8 the one
+    // whose grid (all max_act experts routed) fills its last round of
+    // resident workgroups best, ties to the most rows per wave (fewer
+    // workgroup start-ups for the same bytes)
+    auto kernel_for = [](int r) { return r > 1 ? ffn_kernel<MODE, PLANES, MODE> : ffn_kernel<MODE, PLANES, 0>; };
     int rpw = 1;
     if (MODE == 1 && p.whole_k) {
-        for (int r = 2; r <= 8; r *= 2) {
-            if (tiles % r || (int64_t)a.max_act * (tiles / r) * p.nsplit < slots) break;
-            rpw = r;
+        double best = -1.0;
+        for (int r = 1; r <= 8; r *= 2) {
+            if (tiles % r) break;
+            const int64_t slots =
+                (int64_t)resident_blocks(reinterpret_cast<const void*>(kernel_for(r)), lds) * cu_count();
+            const int64_t blocks = (int64_t)a.max_act * (tiles / r) * p.nsplit;
+            const int64_t rounds = (blocks + slots - 1) / slots;
+            const double fill = (double)blocks / (double)(rounds * slots);
+            if (fill >= best - 1e-9) {
+                best = fill;
+                rpw = r;
+            }
         }
     }
+    auto kernel = kernel_for(rpw);
     const int extra = (a.wide && rpw > 1) ? kHotExtra * (tiles - tiles / rpw) * p.nsplit : 0;
     const dim3 grid((unsigned)((int64_t)a.max_act * (tiles / rpw) * p.nsplit + extra));
     return launch_timed(kernel, grid, dim3(kThreads), lds, s, t.start, t.stop, a, (int)lds, tiles, p.nsplit, rpw,

@@ -463,6 +463,31 @@ def test_hot_experts_on_multi_tile_workgroups():
     compare_y(y, oracle_y(x, logits, wl, masters, bits), "hot experts, multi-tile workgroups")
 
 
+def test_down_split_with_row_block_sequences():
+    """A batch whose down product is both split along K and walked in
+    sequences of row blocks per wave: 12 routed experts x 64 row tiles of
+    d_model 4096 give 768 workgroups per split, so two K splits of d_ff 1536
+    (6 steps each), and two row blocks per wave fill the 1024 resident
+    workgroups as well as one does (the launch takes the larger); the code
+    cursor then steps from one block's K range to the next block's.
+    3/4/8-bit experts; every output against the oracle."""
+    wl = TINY.scaled(name="split_seq", E=12, d=4096, F=1536, k=2, T=6,
+                     bits=(8, 4, 3, 4, 3, 8, 3, 4, 8, 3, 4, 3))
+    masters = synth.expert_weights(wl)
+    layer, _ = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    x, logits = synth.tokens(wl)
+    # every expert routed once: token t takes experts 2t and 2t + 1
+    logits = torch.full((wl.T, wl.E), -5.0)
+    for t in range(wl.T):
+        logits[t, 2 * t] = 2.0
+        logits[t, 2 * t + 1] = 1.0
+    counts = torch.bincount(moe.route(logits, wl.k)[0].reshape(-1), minlength=wl.E)
+    assert int((counts > 0).sum()) == 12
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y(x, logits, wl, masters, list(wl.bits)), "down split with row-block sequences")
+
+
 def test_small_batches_on_a_context_sized_for_large_ones():
     """A context whose workspace is sized for 2048 tokens (its partial-output
     buffer holds one split per pair) still splits the down product of a

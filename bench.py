@@ -372,7 +372,7 @@ def skew_bias(wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -2,11 +2,14 @@
 // Paging": the routed experts' pages are dequantized on the fly; Eq. 2 gives
 // the dequantized weight s_e * q). SwiGLU: h = silu(W1 x) * (W3 x), o = W2 h.
 //
-// One workgroup = 64 rows of one active expert, all of the expert's tokens;
-// each of its four waves streams one 16-row block, whose tiles (16 rows x
+// One workgroup = 64 rows of one routed expert (64 rpw rows when the down
+// product walks row-block sequences), all of the expert's tokens, 16 per
+// pass (64 for an expert with more than 16 tokens: wide passes); each of
+// its four waves streams one 16-row block at a time, whose tiles (16 rows x
 // 128 codes) are contiguous in the page, so every load instruction of a
 // wave reads one contiguous run. One 4B-byte load per lane per tile
-// (B = bits), prefetched several steps ahead; they are turned into exact
+// (B = bits; a bitplane page: one 4-byte word per plane), prefetched
+// several steps ahead; they are turned into exact
 // fp16 integers q in registers (dequant.h: magic-exponent OR, then one
 // packed fp16 subtract or multiply-add per pair) and multiplied on the
 // matrix cores (v_mfma_f32_16x16x32_f16: 16 weight rows x 16 token columns,
@@ -30,9 +33,9 @@
 #include <math.h>
 
 #include <algorithm>
-#include <utility>
-#include <mutex>
 #include <map>
+#include <mutex>
+#include <utility>
 
 #include "dequant.h"
 #include "pw_internal.h"
@@ -364,10 +367,11 @@ struct PlaneCodec {
 // MODE 0: gate/up + SwiGLU (NMAT = 2: W1, W3); MODE 1: down (NMAT = 1: W2),
 // over K-steps [ks0, ks0 + nsteps) (the down product may be split along K
 // across workgroups; split `sp` writes its own partial output).
-// The workgroup covers rows [64 rt, 64 rt + 64) of expert e; wave w owns 16
-// of them. Codes are prefetched PD steps ahead in a register ring; the main
-// loop issues its loads unconditionally so the ring stays full, and LDS
-// chunks of the token rows are staged before the first load when K fits.
+// The workgroup covers rows [64 rpw rt, 64 rpw (rt + 1)) of expert e; wave
+// w owns rpw consecutive 16-row blocks of them. Codes are prefetched PD
+// steps ahead in a register ring; the main loop issues a load for every step
+// (the last steps' loads repeat the last tile), so the ring stays full, and
+// LDS chunks of the token rows are staged before the first load when K fits.
 // The expert's page-table entry, pair count and pair list, read by the
 // kernel in one round of independent loads before its first code load
 // (with the first 16 entries of the list: p0 is this thread's).

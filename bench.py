@@ -70,12 +70,16 @@ def parse():
 def kernel_source_hash(workload: str) -> str:
     """Hash of the sources of the workload's gate/up kernel (the roofline
     kernel): the matrix-core kernels for prefill, the streaming kernels for
-    the decode workloads."""
+    the decode workloads. Comments and blank lines are left out, so that
+    edits of the prose alone keep the counters valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
     src = "kernels_gemm.hip" if workload == "prefill" else "kernels_ffn.hip"
     for f in (src, "pw_internal.h", "dequant.h", "xscale.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        text = open(os.path.join(csrc, f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

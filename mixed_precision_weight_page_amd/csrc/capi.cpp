@@ -206,7 +206,7 @@ FwdWork fwd_work(const pw_ctx* c, const WsView& v, int parity) {
     w.act = reinterpret_cast<int32_t*>(b + L.act);
     w.n_act = reinterpret_cast<int32_t*>(b + L.n_act);
     w.tiles = reinterpret_cast<TileDesc*>(b + L.tiles);
-    // the two counter sets: cnt [E], act [E], n_act, each set 256-byte aligned
+    // the two counter sets: cnt [E], act [E], n_act [2], each set 256-byte aligned
     auto set = [&](int i) {
         uint8_t* q = b + L.dg + (uint64_t)i * (L.dg_bytes / 2);
         DecodeGroup g;
@@ -214,6 +214,7 @@ FwdWork fwd_work(const pw_ctx* c, const WsView& v, int parity) {
         g.act = g.cnt + c->E;
         g.n_act = g.act + c->E;
         g.list = reinterpret_cast<int32_t*>(b + L.list);
+        g.E = c->E;
         return g;
     };
     w.dg = set(parity);
@@ -515,7 +516,7 @@ Layout workspace_layout(int E, int d, int F, int k, int max_tokens, int nsplit) 
     L.stats_end = scratch + align_up(8 * 3 * nblk * (uint64_t)E, kAlign);
     // the grouping counters keep their values between forwards: after
     // everything the statistics pass may overwrite
-    L.dg_bytes = 2 * align_up(4 * (2 * (uint64_t)E + 1), kAlign);
+    L.dg_bytes = 2 * align_up(4 * (2 * (uint64_t)E + 2), kAlign);
     L.dg = std::max(L.fwd_end, L.stats_end);
     L.total = L.dg + L.dg_bytes;
     return L;
@@ -793,7 +794,12 @@ static bool dense_path(const pw_ctx* c, int32_t T) {
 static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const float* logits, const void* x,
                              int32_t T, bool dense, bool scratch, hipStream_t s, KTimer t,
                              const int32_t** counts) {
-    RouteArgs ra{logits, static_cast<const uint16_t*>(x), c->d, T, c->E, c->k, c->desc.renorm, 1};
+    // bitplane pages: the streaming router lists the experts deeper than 4
+    // planes first (their workgroups decode the most planes per row and run
+    // longest: dispatched first, measured 7% faster on the 128-expert decode
+    // layer); Eq. 2 pages keep arrival order (heavy-first measured 2% slower)
+    RouteArgs ra{logits, static_cast<const uint16_t*>(x), c->d, T, c->E, c->k, c->desc.renorm, 1,
+                 bitplane(c) ? dev_table(c, c->cur).bits : nullptr};
     if (dense) {
         ra.x = nullptr;   // prep_x takes the statistics on this path
         HIP_TRY(c, launch_route(ra, w, dev_table(c, c->cur), s, t));
@@ -869,8 +875,8 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
     if (swap_mode(c)) {
         const SwapState ss = swap_state(c);
         const int S = n_slots(c);
-        HIP_TRY(c, launch_swap_in(ss, dense ? w.act : w.dg.act, dense ? w.n_act : w.dg.n_act, tab, c->E, S,
-                                  std::min(S, max_act), c->We, c->pool, c->host, slot_bytes(c), s));
+        HIP_TRY(c, launch_swap_in(ss, cnt, tab, c->E, S, std::min(S, max_act), c->We, c->pool, c->host,
+                                  slot_bytes(c), s));
         tab.off = ss.addr;
         base = nullptr;
     }

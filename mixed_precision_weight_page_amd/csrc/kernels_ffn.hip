@@ -634,17 +634,17 @@ __device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int ns
 constexpr int kWideNB = 4;
 
 // Experts with more than 16 tokens ("hot") among the routed ones, found by
-// one wave scanning the routed list (arrival order) with ballots; every
-// lane gets the same answer.
+// one wave scanning the m routed slots in order with ballots; every lane
+// gets the same answer.
 // hot_expert: the h-th hot expert (0-based), or -1 if there are fewer.
-__device__ __forceinline__ int hot_expert(const DecodeGroup& dg, int h) {
+__device__ __forceinline__ int hot_expert(const DecodeGroup& dg, int m, int h) {
     const int lane = threadIdx.x & 63;
-    const int n = dg.n_act[0];
+    const int nf = dg.n_act[0], nb = dg.n_act[1];
     int seen = 0;
-    for (int base = 0; base < n; base += 64) {
+    for (int base = 0; base < m; base += 64) {
         const int idx = base + lane;
-        const int e = idx < n ? dg.act[idx] : 0;
-        const bool hot = idx < n && dg.cnt[e] > 16;
+        const int e = idx < m ? slot_expert(dg, m, idx, nf, nb) : -1;
+        const bool hot = e >= 0 && dg.cnt[e] > 16;
         const uint64_t m = __ballot(hot);
         const int c = __popcll(m);
         if (seen + c > h) {
@@ -659,12 +659,13 @@ __device__ __forceinline__ int hot_expert(const DecodeGroup& dg, int h) {
 }
 
 // hot_rank: how many hot experts come before routed slot ai.
-__device__ __forceinline__ int hot_rank(const DecodeGroup& dg, int ai) {
+__device__ __forceinline__ int hot_rank(const DecodeGroup& dg, int m, int nf, int nb, int ai) {
     const int lane = threadIdx.x & 63;
     int seen = 0;
     for (int base = 0; base < ai; base += 64) {
         const int idx = base + lane;
-        const bool hot = idx < ai && dg.cnt[dg.act[idx]] > 16;
+        const int e = idx < ai ? slot_expert(dg, m, idx, nf, nb) : -1;
+        const bool hot = e >= 0 && dg.cnt[e] > 16;
         seen += __popcll(__ballot(hot));
     }
     return seen;
@@ -676,8 +677,10 @@ constexpr int kHotExtra = 16;
 
 // grid: `extra` workgroups for hot experts, then (routed expert slot, 64
 // rpw-row tile, K split) flattened; slots past the device-side routed count
-// exit at once. The slot's expert comes from the router's list (arrival
-// order); its page-table entry, pair count and first 16 pairs are then read
+// exit at once. The slot's expert comes from the router's list (with
+// bitplane pages the deeper experts first, so the longest workgroups are
+// dispatched first); its page-table entry, pair count and first 16 pairs
+// are then read
 // in one round of independent loads (the pair list has room for at least 16
 // entries). wide (set when the batch has more than 16 tokens): an expert may
 // be hot; a hot expert's 64-row tiles take wide passes, one tile per
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
     if ((int)blockIdx.x < extra) {
         const int per = (tiles - own) * nsplit;
         const int h = blockIdx.x / per;
-        const int e = hot_expert(dg, h);
+        const int e = hot_expert(dg, a.max_act, h);
         if (e < 0) return;
         ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, own * nsplit + (blockIdx.x - h * per), xs,
                                         tok, prs);
@@ -705,10 +708,12 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
     const int blk = blockIdx.x - extra;
     const int per_expert = own * nsplit;
     const int ai = blk / per_expert;
-    const int e = dg.act[ai];   // stale past the routed count, not used then
-    if (ai >= dg.n_act[0]) return;
+    // the counts and both candidates of the slot in one round of loads
+    const int nf = dg.n_act[0], nb = dg.n_act[1];
+    const int e = slot_expert(ai, a.max_act, nf, nb, dg.act[ai], dg.act[dg.E - a.max_act + ai]);
+    if (e < 0) return;
     const int rem = blk - ai * per_expert;
-    if (a.wide && dg.cnt[e] > 16 && (rpw == 1 || hot_rank(dg, ai) < kHotExtra))
+    if (a.wide && dg.cnt[e] > 16 && (rpw == 1 || hot_rank(dg, a.max_act, nf, nb, ai) < kHotExtra))
         ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, rem, xs, tok, prs);
     else
         ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);

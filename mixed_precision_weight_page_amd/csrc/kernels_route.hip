@@ -59,11 +59,16 @@ __device__ __forceinline__ bool better(float v, int e, float v2, int e2) {
 }
 
 // The decode grouping of pair p = t k + j routed to expert e: the next
-// position of e's list; the expert's first pair appends it to the active list.
-__device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, int e, int p) {
+// position of e's list; the expert's first pair enters it in the active
+// list, from the front (without widths, or if it is wider than 4 bits),
+// else from the back.
+__device__ __forceinline__ void group_pair(const DecodeGroup& g, int tcap, const int32_t* bits, int e, int p) {
     const int slot = atomicAdd(&g.cnt[e], 1);
     g.list[(int64_t)e * tcap + slot] = p;
-    if (slot == 0) g.act[atomicAdd(g.n_act, 1)] = e;
+    if (slot == 0) {
+        if (!bits || bits[e] > 4) g.act[atomicAdd(&g.n_act[0], 1)] = e;
+        else g.act[g.E - 1 - atomicAdd(&g.n_act[1], 1)] = e;
+    }
 }
 
 // ---- 16 lanes per token (E <= 256) ----
@@ -206,7 +211,7 @@ __device__ __forceinline__ void route_token_t(const RouteArgs& a, const FwdWork&
         w.ids[(int64_t)t * a.k + lane] = my_id;
         w.g[(int64_t)t * a.k + lane] = mine / den;
         if (s_ids) s_ids[t * a.k + lane] = my_id;
-        if (group) group_pair(w.dg, w.tcap, my_id, t * a.k + lane);
+        if (group) group_pair(w.dg, w.tcap, a.bits, my_id, t * a.k + lane);
     }
 }
 
@@ -265,13 +270,13 @@ __device__ __forceinline__ void route_row_t(const RouteArgs& a, const FwdWork& w
         w.ids[(int64_t)t * a.k + l16] = id0;
         w.g[(int64_t)t * a.k + l16] = m0 / den;
         if (s_ids) s_ids[t * a.k + l16] = id0;
-        if (group) group_pair(w.dg, w.tcap, id0, t * a.k + l16);
+        if (group) group_pair(w.dg, w.tcap, a.bits, id0, t * a.k + l16);
     }
     if (l16 + 16 < a.k) {
         w.ids[(int64_t)t * a.k + l16 + 16] = id1;
         w.g[(int64_t)t * a.k + l16 + 16] = m1 / den;
         if (s_ids) s_ids[t * a.k + l16 + 16] = id1;
-        if (group) group_pair(w.dg, w.tcap, id1, t * a.k + l16 + 16);
+        if (group) group_pair(w.dg, w.tcap, a.bits, id1, t * a.k + l16 + 16);
     }
 }
 
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork w) {
     if (blockIdx.x == 0) {
         for (int e = threadIdx.x; e < a.E; e += 256) w.dg_next.cnt[e] = 0;
-        if (threadIdx.x == 0) w.dg_next.n_act[0] = 0;
+        if (threadIdx.x < 2) w.dg_next.n_act[threadIdx.x] = 0;
     }
     const int wave = threadIdx.x >> 6;
     const int ts = blockIdx.x * 4 + wave;   // this wave's token for the statistics

@@ -27,8 +27,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kCopyThreads = 256;
 constexpr int64_t kCopyChunk = 256 * 1024;   // bytes per copy workgroup
 
-__global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, const int32_t* act,
-                                                                   const int32_t* n_act_p, DevTable tab, int E,
+__global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, const int32_t* cnt, DevTable tab, int E,
                                                                    int S, const uint8_t* pool,
                                                                    const uint8_t* host, uint64_t slot_bytes) {
     __shared__ int32_t s_slot[kMaxExperts];     // slot of each expert (-1: none)
@@ -38,17 +37,20 @@ __global__ __launch_bounds__(kPlanThreads) void swap_plan_kernel(SwapState st, c
     __shared__ int32_t s_cand[kMaxExperts];     // candidate slots in hand-out order
     __shared__ uint64_t s_key[kMaxExperts];
     __shared__ int32_t s_scan[kPlanThreads];
+    __shared__ int s_nact;
     const int tid = threadIdx.x;
     const uint32_t step = st.step[0] + 1;
-    const int n_act = n_act_p[0];
+    if (tid == 0) s_nact = 0;
+    __syncthreads();
+    // the active experts: those the router gave at least one pair
     for (int e = tid; e < E; e += kPlanThreads) {
         s_slot[e] = st.slot_of[e];
-        s_act[e] = 0;
+        s_act[e] = cnt[e] > 0;
+        if (s_act[e]) atomicAdd(&s_nact, 1);
     }
     for (int s = tid; s < S; s += kPlanThreads) s_exp[s] = st.expert_of[s];
     __syncthreads();
-    for (int i = tid; i < n_act; i += kPlanThreads) s_act[act[i]] = 1;
-    __syncthreads();
+    const int n_act = s_nact;
 
     // misses ranked by expert id: a block scan over the E flags, each thread
     // owning a contiguous run of ceil(E / threads) experts
@@ -169,10 +171,10 @@ __global__ __launch_bounds__(256) void swap_invalidate_kernel(SwapState st, cons
 
 }  // namespace
 
-hipError_t launch_swap_in(const SwapState& st, const int32_t* act, const int32_t* n_act, const DevTable& tab,
-                          int E, int S, int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host,
-                          uint64_t slot_bytes, hipStream_t s) {
-    swap_plan_kernel<<<1, kPlanThreads, 0, s>>>(st, act, n_act, tab, E, S, pool, host, slot_bytes);
+hipError_t launch_swap_in(const SwapState& st, const int32_t* cnt, const DevTable& tab, int E, int S,
+                          int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host, uint64_t slot_bytes,
+                          hipStream_t s) {
+    swap_plan_kernel<<<1, kPlanThreads, 0, s>>>(st, cnt, tab, E, S, pool, host, slot_bytes);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || max_copies <= 0) return err;
     const dim3 grid((unsigned)((slot_bytes + kCopyChunk - 1) / kCopyChunk), (unsigned)max_copies);

@@ -48,10 +48,25 @@ struct __attribute__((aligned(16))) TileDesc {
 // the router of one forward clears the set of the next.
 struct DecodeGroup {
     int32_t* cnt;     // [E] pairs routed to each expert
-    int32_t* n_act;   // [1] routed experts
-    int32_t* act;     // [E] routed experts, in arrival order
+    int32_t* n_act;   // [2] routed experts at the front of act, and at its back
+    int32_t* act;     // [E] routed experts in arrival order, from the front (all
+                      // of them, or those wider than 4 bits) and from the back
     int32_t* list;    // [E, tcap] pair indices of each expert, in arrival order
+    int E;            // entries of act
 };
+
+// The decode kernels' routed slots: m = min(E, pairs) slots, the first
+// n_act[0] holding the front of the router's list (act[i]), the last
+// n_act[1] its back (act[E - m + i]), none in between. When the router
+// orders by width, the wider experts are at the front: their workgroups
+// run longest and are dispatched first, the narrow ones fill in behind
+// them. Both candidates of a slot can be read before the counts arrive.
+__device__ __forceinline__ int slot_expert(int i, int m, int nf, int nb, int front, int back) {
+    return i < nf ? front : (i >= m - nb ? back : -1);
+}
+__device__ __forceinline__ int slot_expert(const DecodeGroup& g, int m, int i, int nf, int nb) {
+    return slot_expert(i, m, nf, nb, g.act[i], g.act[g.E - m + i]);
+}
 
 // Per-token statistics of the activations (xscale.h): e with max|x| 2^-e in
 // [2^14, 2^15) and n1 = sum |x| 2^-e over the row.
@@ -133,6 +148,8 @@ struct RouteArgs {
     int d;
     int T, E, k, renorm;
     int tiles;   // also the large-batch kernels' token tiles (FwdWork::tiles)
+    const int32_t* bits;   // [E] the table's widths, or NULL: the streaming router's active list
+                           // puts the experts wider than 4 bits first (else arrival order)
 };
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t = {});
@@ -200,9 +217,10 @@ struct SwapState {
     int32_t* copy_s;      // [S] slot of each copy
     uint64_t* addr;       // [E] page address for the current pass
 };
-hipError_t launch_swap_in(const SwapState& st, const int32_t* act, const int32_t* n_act, const DevTable& tab,
-                          int E, int S, int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host,
-                          uint64_t slot_bytes, hipStream_t s);
+// cnt: [E] pairs routed to each expert this pass (the active experts have cnt > 0)
+hipError_t launch_swap_in(const SwapState& st, const int32_t* cnt, const DevTable& tab, int E, int S,
+                          int max_copies, uint64_t We, uint8_t* pool, const uint8_t* host, uint64_t slot_bytes,
+                          hipStream_t s);
 hipError_t launch_swap_invalidate(const SwapState& st, const int32_t* list, int n, hipStream_t s);
 
 // ---- static scratch of the allocation-free forward (noalloc.hip) ----

@@ -156,3 +156,32 @@ def test_bitplane_rows_across_the_bf16_range():
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
     compare_y_rows(y, oracle_y_bp(x, logits, WL, masters, depth), "bitplane rows 2^-40..2^40")
+
+
+def test_deep_experts_first_with_hot_experts_and_idle_slots():
+    """The streaming kernels take bitplane experts deeper than 4 planes
+    first: the router lists them from the front of its active list and the
+    others from the back, with idle slots in between when fewer experts are
+    routed than the grid has slots. 128 experts at every depth 1..8, d_model
+    2048 (the down product walks row-block sequences), 200 tokens x top-2
+    (128 slots; 108 experts routed), six hot experts (more than 16
+    tokens), three deep and three shallow: the hot-expert scans (extra
+    workgroups for the first ones) run over both ends of the list. Every
+    output against the oracle."""
+    wl = synth.WORKLOADS["decode_fine"].scaled(name="bp_hot_order", E=128, d=2048, F=384, k=2, T=200)
+    masters = synth.expert_weights(wl)
+    depth = [1 + (5 * e) % 8 for e in range(wl.E)]
+    layer, _ = make_layer(wl, masters, max_tokens=wl.T, layout="bitplane")
+    layer.quantize_experts(depth)
+    x, logits = synth.tokens(wl)
+    hot = [e for e in range(wl.E) if depth[e] > 4][:3] + [e for e in range(wl.E) if depth[e] <= 4][3:6]
+    for h, e in enumerate(hot):
+        logits[30 * h:30 * h + 30, e] += 10.0   # 30 tokens each
+    counts = torch.bincount(moe.route(logits, wl.k)[0].reshape(-1), minlength=wl.E)
+    assert sorted(torch.nonzero(counts > 16).reshape(-1).tolist()) == sorted(hot)
+    routed = int((counts > 0).sum())
+    log(f"routed experts {routed} of {wl.E} (slots {min(wl.E, wl.T * wl.k)}), hot {hot}, "
+        f"deep routed {sum(1 for e in range(wl.E) if counts[e] > 0 and depth[e] > 4)}")
+    assert routed < wl.E
+    y = layer.moe_forward(x.cuda(), logits.cuda())
+    compare_y(y, oracle_y_bp(x, logits, wl, masters, depth), "bitplane deep-first order, hot experts")

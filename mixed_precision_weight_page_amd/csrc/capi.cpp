@@ -793,7 +793,7 @@ static bool dense_path(const pw_ctx* c, int32_t T) {
 // the per-expert counts.
 static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const float* logits, const void* x,
                              int32_t T, bool dense, bool scratch, hipStream_t s, KTimer t,
-                             const int32_t** counts) {
+                             const int32_t** counts, bool own_route = false) {
     // bitplane pages: the streaming router lists the experts deeper than 4
     // planes first (their workgroups decode the most planes per row and run
     // longest: dispatched first, measured 7% faster on the 128-expert decode
@@ -811,7 +811,14 @@ static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const
         HIP_TRY(c, launch_zero_i32(reinterpret_cast<int32_t*>(v.base + v.lay.dg), v.lay.dg_bytes / 4, s));
         if (!scratch) c->dg_clean = true;
     }
-    HIP_TRY(c, launch_route_decode(ra, w, s, t));
+    if (own_route) {
+        // the gate/up kernel routes this batch and fills the counter set
+        // (the timing events, if any, enclose no work)
+        if (t.start) HIP_TRY(c, hipEventRecord(t.start, s));
+        if (t.stop) HIP_TRY(c, hipEventRecord(t.stop, s));
+    } else {
+        HIP_TRY(c, launch_route_decode(ra, w, s, t));
+    }
     if (!scratch) c->dg_parity ^= 1;
     *counts = w.dg.cnt;
     return PW_OK;
@@ -865,8 +872,11 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
     const int64_t pairs = (int64_t)T * c->k;
     const int max_act = (int)std::min<int64_t>(c->E, pairs);
     const bool dense = dense_path(c, T);
+    // small decode batches are routed by the gate/up kernel itself (not with
+    // a host tier: its plan needs the counts before the expert kernels)
+    const bool own_route = !dense && !swap_mode(c) && own_route_ok(T, c->E, c->k);
     const int32_t* cnt = nullptr;
-    pw_status st = route_batch(c, v, w, logits, x, T, dense, scratch, s, tm[0], &cnt);
+    pw_status st = route_batch(c, v, w, logits, x, T, dense, scratch, s, tm[0], &cnt, own_route);
     if (st != PW_OK) return st;
     // pages: pool + offset, or with a host tier the addresses of this pass
     // (slot or host tier) after the missing pages are copied in
@@ -918,6 +928,11 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
         fa.bitplane = c->desc.layout == PW_LAYOUT_BITPLANE ? 1 : 0;
         // an expert may receive more than 16 tokens
         fa.wide = T > 16 ? 1 : 0;
+        fa.own_route = own_route ? 1 : 0;
+        fa.logits = logits;
+        fa.T = T;
+        fa.E = c->E;
+        fa.renorm = c->desc.renorm;
         // K splits of the down product for this batch, within the buffer
         const int64_t cap_pairs = (int64_t)v.nsplit * v.max_tokens * c->k;
         const int nsplit = down_splits(c->F, c->d, max_act, (int)std::min<int64_t>(cap_pairs / pairs, 1 << 30));

@@ -22,6 +22,9 @@
 // representable in fp32 fit the fp16 operands; the epilogues multiply the
 // powers back.
 //
+// Batches of at most 4 tokens over at most 64 experts skip the router
+// launch: the gate/up kernel routes them itself (gate_up_own_route_kernel).
+//
 // Why matrix cores for a memory-bound skinny product: with T_e tokens per
 // expert a VALU dot product costs T_e/2 instructions per weight (packed
 // dot2), which exceeds the VALU issue budget at HBM speed (about 2.5
@@ -39,6 +42,7 @@
 
 #include "dequant.h"
 #include "pw_internal.h"
+#include "route_dev.h"
 #include "xscale.h"
 
 namespace pw {
@@ -599,13 +603,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
 // bitplane pages (a kernel of its own, so that the Eq. 2 kernel's register
 // allocation does not depend on the bitplane decoding).
 template <int MODE, bool PLANES, int NB, int SEQ>
-__device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, int e, int rem,
-                                         _Float16* xs, int* tok, int* prs) {
-    const DecodeGroup& dg = a.w.dg;
-    const int rt = rem / nsplit, sp = rem - rt * nsplit;
-    const int32_t* list = dg.list + (int64_t)e * a.w.tcap;
-    const int b = a.tab.bits[e];
-    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15]};
+__device__ __forceinline__ void ffn_width(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, const ExpertRef& ex,
+                                          int b, int rt, int sp, _Float16* xs, int* tok, int* prs) {
     const int total = (MODE == 0 ? a.d : a.F) / kStep;
     const int nsteps = total / nsplit;
     if constexpr (PLANES) {
@@ -625,6 +624,17 @@ __device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int ns
         else if (b == 8) ffn_tile<MODE, Eq2Codec<8>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
         else ffn_tile<MODE, Eq2Codec<3>, NB, SEQ>(a, lds_bytes, ex, rt, sp, sp * nsteps, nsteps, rpw, xs, tok, prs);
     }
+}
+
+template <int MODE, bool PLANES, int NB, int SEQ>
+__device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, int e, int rem,
+                                         _Float16* xs, int* tok, int* prs) {
+    const DecodeGroup& dg = a.w.dg;
+    const int rt = rem / nsplit, sp = rem - rt * nsplit;
+    const int32_t* list = dg.list + (int64_t)e * a.w.tcap;
+    const int b = a.tab.bits[e];
+    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15]};
+    ffn_width<MODE, PLANES, NB, SEQ>(a, lds_bytes, nsplit, rpw, ex, b, rt, sp, xs, tok, prs);
 }
 
 // Experts that receive more than 16 tokens are served by wide passes,
@@ -719,6 +729,121 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
         ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
 }
 
+// Small batches (at most kOwnRouteTokens tokens, kOwnRouteExperts experts,
+// top-kOwnRouteTopK) skip the router launch: every gate/up workgroup routes
+// the whole batch itself (a row of 16 lanes per token, the router's top-k
+// and weights, route_dev.h) and takes every token's statistics (a wave per
+// token, its loads in flight with the logits'), so the routing costs no
+// round trip beyond the one the routed list would. The routed experts are
+// ordered by class, then id (Eq. 2 pages: those of at most 4 bits first;
+// bitplane pages: those deeper than 4 planes first, as the router orders
+// them), and workgroup (ai, tile) serves the ai-th; its pairs (in pair
+// order) stay in LDS. What the later kernels read is written by the
+// workgroups that own it: row tile 0 of each expert writes its pairs' ids,
+// weights and list; the first workgroup every token's statistics, every
+// expert's count and the routed list, and clears the next forward's
+// counters, as the router does. Every workgroup computes the same routing
+// from the same logits, so they agree on the order.
+constexpr int kOwnRouteTokens = 4;
+constexpr int kOwnRouteExperts = 64;
+constexpr int kOwnRouteTopK = 16;
+static_assert(kOwnRouteTokens <= kThreads / 64, "a wave per token for the statistics");
+static_assert(kOwnRouteTokens * kOwnRouteTopK <= 64, "the pairs fit one wave");
+
+template <int PER>
+__device__ __forceinline__ rdev::RowChoice own_topk(const FfnArgs& a, int t, bool valid, XStat* s_xst) {
+    const int l16 = threadIdx.x & 15;
+    const float* row = a.logits + (int64_t)t * a.E;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = l16 + 16 * i;
+        v[i] = (valid && e < a.E) ? row[e] : -INFINITY;
+    }
+    // wave w takes token w's statistics meanwhile
+    const int wave = threadIdx.x >> 6;
+    if (wave < a.T) {
+        const XStat st = rdev::lanes_stat<64>(a.x + (int64_t)wave * a.d, a.d);
+        if ((threadIdx.x & 63) == 0) s_xst[wave] = st;
+    }
+    return rdev::row_topk<PER>(v, a.E, a.k, a.renorm, valid);
+}
+
+// grid: (routed expert in class and id order, 64-row tile); positions past
+// the routed count exit once the routing is known
+template <bool PLANES>
+__global__ __launch_bounds__(kThreads, 3) void gate_up_own_route_kernel(FfnArgs a, int lds_bytes, int tiles) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+    __shared__ int tok[16 * kWideNB];
+    __shared__ int prs[16 * kWideNB];
+    __shared__ int s_ids[kOwnRouteTokens * kOwnRouteTopK];   // expert of each pair
+    __shared__ int s_cnt[kOwnRouteExperts];                   // pairs per expert
+    __shared__ int s_list[16];                                // this expert's pairs (Te <= T)
+    __shared__ XStat s_xst[kOwnRouteTokens];                  // by token
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ai = blockIdx.x / tiles, rt = blockIdx.x - ai * tiles;
+    const int my_bits = lane < a.E ? a.tab.bits[lane] : 0;   // the class of expert `lane`
+    if (tid < kOwnRouteExperts) s_cnt[tid] = 0;
+    // token t = tid / 16 by its row of lanes; lane l16 < k holds choice l16
+    const int t = tid >> 4, l16 = tid & 15;
+    const bool valid = t < a.T;
+    const int tc = valid ? t : 0;
+    rdev::RowChoice c;
+    if (a.E <= 16) c = own_topk<1>(a, tc, valid, s_xst);
+    else if (a.E <= 32) c = own_topk<2>(a, tc, valid, s_xst);
+    else c = own_topk<4>(a, tc, valid, s_xst);
+    __syncthreads();   // s_cnt cleared
+    const bool chosen = valid && l16 < a.k;
+    const int p = t * a.k + l16;
+    if (chosen) {
+        s_ids[p] = c.id0;
+        atomicAdd(&s_cnt[c.id0], 1);
+    }
+    __syncthreads();
+    // the routed experts by class, then id (every wave finds the same);
+    // this workgroup's expert is the ai-th
+    const bool act = lane < a.E && s_cnt[lane] > 0;
+    const bool first = (my_bits > 4) == (a.bitplane != 0);
+    const uint64_t m0 = __ballot(act && first), m1 = __ballot(act && !first);
+    const int n0 = __popcll(m0), n_act = n0 + __popcll(m1);
+    if (ai >= n_act) return;
+    const uint64_t mk = act && first ? m0 : m1;
+    const int arank = (act && first ? 0 : n0) +
+                      __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    const int e = __ffsll((unsigned long long)__ballot(act && arank == ai)) - 1;
+    // its pairs in pair order (at most one per token; T k <= 64: wave 0)
+    const int P = a.T * a.k;
+    const int Te = s_cnt[e];
+    const bool mine = tid < P && s_ids[tid] == e;
+    const uint64_t mm = __ballot(mine);
+    if (tid < 64 && mine)
+        s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u))] = tid;
+    if (rt == 0) {
+        if (chosen && c.id0 == e) {
+            a.w.ids[p] = e;
+            a.w.g[p] = c.g0;
+        }
+        if (ai == 0) {
+            if (tid < a.T) a.w.xst[tid] = s_xst[tid];
+            if (tid < a.E) {
+                a.w.dg.cnt[tid] = s_cnt[tid];
+                a.w.dg_next.cnt[tid] = 0;
+            }
+            if (tid < 64 && act) a.w.dg.act[arank] = lane;
+            if (tid < 2) {
+                a.w.dg.n_act[tid] = tid == 0 ? n_act : 0;
+                a.w.dg_next.n_act[tid] = 0;
+            }
+        }
+    }
+    __syncthreads();   // s_list complete
+    if (rt == 0 && tid < Te) a.w.dg.list[(int64_t)e * a.w.tcap + tid] = s_list[tid];
+    FfnArgs b = a;
+    b.w.xst = s_xst;
+    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], Te, s_list, s_list[tid & 15]};
+    ffn_width<0, PLANES, 1, 0>(b, lds_bytes, 1, 1, ex, a.tab.bits[e], rt, 0, xs, tok, prs);
+}
+
 // Resident workgroups of a kernel per CU at an LDS size, and the CU count
 // (cached: the occupancy query is host arithmetic, but not free).
 int resident_blocks(const void* kernel, size_t lds) {
@@ -789,8 +914,17 @@ hipError_t launch_ffn_k(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTime
 
 template <int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t) {
+    if (MODE == 0 && a.own_route) {
+        const int tiles = a.F / 64;
+        const dim3 grid((unsigned)((int64_t)a.max_act * tiles));
+        return a.bitplane ? launch_timed(gate_up_own_route_kernel<true>, grid, dim3(kThreads), p.lds, s, t.start,
+                                         t.stop, a, (int)p.lds, tiles)
+                          : launch_timed(gate_up_own_route_kernel<false>, grid, dim3(kThreads), p.lds, s, t.start,
+                                         t.stop, a, (int)p.lds, tiles);
+    }
     return a.bitplane ? launch_ffn_k<MODE, true>(a, p, s, t) : launch_ffn_k<MODE, false>(a, p, s, t);
 }
+
 
 // Partial outputs are read once: non-temporal loads (17% faster for 4096
 // tokens x top-6 than plain ones).
@@ -858,6 +992,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
 }
 
 }  // namespace
+
+bool own_route_ok(int T, int E, int k) {
+    return T <= kOwnRouteTokens && E <= kOwnRouteExperts && k <= kOwnRouteTopK;
+}
 
 // LDS for the staged token rows: all of the K range for up to min(T, 16)
 // tokens if that fits 34 KB, else 34 KB (the kernel then stages K in chunks

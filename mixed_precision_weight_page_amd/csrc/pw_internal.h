@@ -183,7 +183,14 @@ struct FfnArgs {
     int P;               // pair stride of the split partial outputs O[split][P][d]
     int bitplane;        // 1: bitplane pages (the table's bits are depths 1..8)
     int wide;            // 1: an expert may have more than 16 tokens (wide passes)
+    // own_route: the gate/up kernel routes the batch itself (own_route_ok):
+    // the logits [T, E] and the router's options
+    int own_route;
+    const float* logits;
+    int T, E, renorm;
 };
+// the gate/up kernel can route a batch of T tokens over E experts, top-k, itself
+bool own_route_ok(int T, int E, int k);
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,

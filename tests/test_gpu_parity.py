@@ -412,6 +412,28 @@ def test_large_batch_matrix_core_path(T):
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
 
 
+@pytest.mark.parametrize("E,k,renorm", [(8, 2, 0), (40, 1, 1), (64, 16, 0), (17, 8, 1)])
+def test_small_batches_routed_by_the_gate_up_kernel(E, k, renorm):
+    """Batches of at most 4 tokens over at most 64 experts are routed by the
+    gate/up kernel itself (no router launch): 1-4 tokens with planted equal
+    logits (ties go to the lower expert), 3/4/8-bit experts, then batches
+    routed by the router kernel (16 and 40 tokens) and again by the gate/up
+    kernel, so the counter sets each leaves behind serve the next. Every
+    output against the oracle."""
+    wl = synth.WORKLOADS["tiny"].scaled(name=f"own_route_{E}_{k}", E=E, d=256, F=384, k=k, T=40, renorm=renorm,
+                                        bits=tuple((8, 4, 3)[e % 3] for e in range(E)))
+    masters = synth.expert_weights(wl)
+    layer, _ = make_layer(wl, masters, max_tokens=wl.T)
+    layer.quantize_experts(wl.bits)
+    for step, T in enumerate((1, 4, 16, 3, 40, 2, 4)):
+        x, logits = synth.tokens(wl, T=T, seed=10 + step)
+        logits[0, E - 1] = logits[0, 0] = logits[0].max() + 1.0   # a tie at the top
+        if T > 1:
+            logits[1, :] = 0.5                                   # every logit equal
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"E={E} k={k} T={T}")
+
+
 @pytest.mark.parametrize("layout", ["eq2", "bitplane"])
 def test_skewed_routing_on_the_streaming_path(layout):
     """Importance-skewed routing of a decode batch: expert 0 takes all 150

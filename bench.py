@@ -74,8 +74,8 @@ def kernel_source_hash(workload: str) -> str:
     edits of the prose alone keep the counters valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixed_precision_weight_page_amd", "csrc")
-    src = "kernels_gemm.hip" if workload == "prefill" else "kernels_ffn.hip"
-    for f in (src, "pw_internal.h", "dequant.h", "xscale.h"):
+    srcs = ("kernels_gemm.hip",) if workload == "prefill" else ("kernels_ffn.hip", "route_dev.h")
+    for f in srcs + ("pw_internal.h", "dequant.h", "xscale.h"):
         text = open(os.path.join(csrc, f)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())

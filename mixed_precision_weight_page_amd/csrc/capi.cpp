@@ -793,7 +793,7 @@ static bool dense_path(const pw_ctx* c, int32_t T) {
 // the per-expert counts.
 static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const float* logits, const void* x,
                              int32_t T, bool dense, bool scratch, hipStream_t s, KTimer t,
-                             const int32_t** counts, bool own_route = false) {
+                             const int32_t** counts, int own_route = 0) {
     // bitplane pages: the streaming router lists the experts deeper than 4
     // planes first (their workgroups decode the most planes per row and run
     // longest: dispatched first, measured 7% faster on the 128-expert decode
@@ -811,12 +811,14 @@ static pw_status route_batch(pw_ctx* c, const WsView& v, const FwdWork& w, const
         HIP_TRY(c, launch_zero_i32(reinterpret_cast<int32_t*>(v.base + v.lay.dg), v.lay.dg_bytes / 4, s));
         if (!scratch) c->dg_clean = true;
     }
-    if (own_route) {
+    if (own_route == 1) {
         // the gate/up kernel routes this batch and fills the counter set
         // (the timing events, if any, enclose no work)
         if (t.start) HIP_TRY(c, hipEventRecord(t.start, s));
         if (t.stop) HIP_TRY(c, hipEventRecord(t.stop, s));
     } else {
+        // own_route 2: the gate/up kernel groups the pairs of these ids
+        ra.group = own_route == 2 ? 0 : 1;
         HIP_TRY(c, launch_route_decode(ra, w, s, t));
     }
     if (!scratch) c->dg_parity ^= 1;
@@ -874,7 +876,7 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
     const bool dense = dense_path(c, T);
     // small decode batches are routed by the gate/up kernel itself (not with
     // a host tier: its plan needs the counts before the expert kernels)
-    const bool own_route = !dense && !swap_mode(c) && own_route_ok(T, c->E, c->k);
+    const int own_route = (!dense && !swap_mode(c)) ? own_route_mode(T, c->E, c->k) : 0;
     const int32_t* cnt = nullptr;
     pw_status st = route_batch(c, v, w, logits, x, T, dense, scratch, s, tm[0], &cnt, own_route);
     if (st != PW_OK) return st;
@@ -928,7 +930,7 @@ static pw_status forward_core(pw_ctx* c, const WsView& v, const void* x, const f
         fa.bitplane = c->desc.layout == PW_LAYOUT_BITPLANE ? 1 : 0;
         // an expert may receive more than 16 tokens
         fa.wide = T > 16 ? 1 : 0;
-        fa.own_route = own_route ? 1 : 0;
+        fa.own_route = own_route;
         fa.logits = logits;
         fa.T = T;
         fa.E = c->E;

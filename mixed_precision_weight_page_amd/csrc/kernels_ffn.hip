@@ -22,8 +22,9 @@
 // representable in fp32 fit the fp16 operands; the epilogues multiply the
 // powers back.
 //
-// Batches of at most 4 tokens over at most 64 experts skip the router
-// launch: the gate/up kernel routes them itself (gate_up_own_route_kernel).
+// Batches of at most 16 tokens over at most 64 experts are grouped by the
+// gate/up kernel itself (gate_up_own_route_kernel), which up to 4 tokens
+// also routes them (no router launch).
 //
 // Why matrix cores for a memory-bound skinny product: with T_e tokens per
 // expert a VALU dot product costs T_e/2 instructions per weight (packed
@@ -729,26 +730,30 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
         ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
 }
 
-// Small batches (at most kOwnRouteTokens tokens, kOwnRouteExperts experts,
-// top-kOwnRouteTopK) skip the router launch: every gate/up workgroup routes
-// the whole batch itself (a row of 16 lanes per token, the router's top-k
-// and weights, route_dev.h) and takes every token's statistics (a wave per
-// token, its loads in flight with the logits'), so the routing costs no
-// round trip beyond the one the routed list would. The routed experts are
-// ordered by class, then id (Eq. 2 pages: those of at most 4 bits first;
-// bitplane pages: those deeper than 4 planes first, as the router orders
-// them), and workgroup (ai, tile) serves the ai-th; its pairs (in pair
-// order) stay in LDS. What the later kernels read is written by the
-// workgroups that own it: row tile 0 of each expert writes its pairs' ids,
-// weights and list; the first workgroup every token's statistics, every
-// expert's count and the routed list, and clears the next forward's
-// counters, as the router does. Every workgroup computes the same routing
-// from the same logits, so they agree on the order.
+// Small batches skip the routed-list round trip. Up to kOwnRouteTokens
+// tokens (at most kOwnRouteExperts experts, top-kOwnRouteTopK) there is no
+// router launch: every gate/up workgroup routes the whole batch itself (a
+// row of 16 lanes per token, the router's top-k and weights, route_dev.h)
+// and takes every token's statistics (a wave per token, its loads in flight
+// with the logits'). Up to kOwnGroupTokens tokens the router only routes
+// (ids, weights, statistics, no grouping atomics) and every gate/up
+// workgroup groups the pairs of its ids itself. Either way the workgroup
+// orders the routed experts by class, then id (Eq. 2 pages: those of at
+// most 4 bits first; bitplane pages: those deeper than 4 planes first, as
+// the router orders them), serves the ai-th, and keeps its pairs (in pair
+// order) in LDS: its page-table entry, token ids and token rows then come in
+// one round of loads. What the later kernels read is written by the
+// workgroups that own it: row tile 0 of each expert its list (and, routing
+// itself, its pairs' ids and weights); the first workgroup every expert's
+// count and the routed list (and the tokens' statistics), and it clears the
+// next forward's counters, as the router does. Every workgroup derives the
+// same grouping from the same logits or ids, so they agree on the order.
 constexpr int kOwnRouteTokens = 4;
+constexpr int kOwnGroupTokens = 16;
 constexpr int kOwnRouteExperts = 64;
 constexpr int kOwnRouteTopK = 16;
 static_assert(kOwnRouteTokens <= kThreads / 64, "a wave per token for the statistics");
-static_assert(kOwnRouteTokens * kOwnRouteTopK <= 64, "the pairs fit one wave");
+static_assert(kOwnGroupTokens * kOwnRouteTopK <= kThreads, "a thread per pair");
 
 template <int PER>
 __device__ __forceinline__ rdev::RowChoice own_topk(const FfnArgs& a, int t, bool valid, XStat* s_xst) {
@@ -769,35 +774,51 @@ __device__ __forceinline__ rdev::RowChoice own_topk(const FfnArgs& a, int t, boo
     return rdev::row_topk<PER>(v, a.E, a.k, a.renorm, valid);
 }
 
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // grid: (routed expert in class and id order, 64-row tile); positions past
-// the routed count exit once the routing is known
-template <bool PLANES>
+// the routed count exit once the grouping is known. ROUTE: route the batch
+// (else group the router's ids).
+template <bool PLANES, bool ROUTE>
 __global__ __launch_bounds__(kThreads, 3) void gate_up_own_route_kernel(FfnArgs a, int lds_bytes, int tiles) {
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
     __shared__ int tok[16 * kWideNB];
     __shared__ int prs[16 * kWideNB];
-    __shared__ int s_ids[kOwnRouteTokens * kOwnRouteTopK];   // expert of each pair
+    __shared__ int s_ids[kOwnGroupTokens * kOwnRouteTopK];   // expert of each pair
     __shared__ int s_cnt[kOwnRouteExperts];                   // pairs per expert
-    __shared__ int s_list[16];                                // this expert's pairs (Te <= T)
-    __shared__ XStat s_xst[kOwnRouteTokens];                  // by token
-    const int tid = threadIdx.x, lane = tid & 63;
+    __shared__ int s_list[kOwnGroupTokens];                   // this expert's pairs (Te <= T)
+    __shared__ int s_wcnt[kThreads / 64];
+    __shared__ XStat s_xst[kOwnRouteTokens];                  // by token (routing here)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ai = blockIdx.x / tiles, rt = blockIdx.x - ai * tiles;
     const int my_bits = lane < a.E ? a.tab.bits[lane] : 0;   // the class of expert `lane`
+    const int P = a.T * a.k;
     if (tid < kOwnRouteExperts) s_cnt[tid] = 0;
-    // token t = tid / 16 by its row of lanes; lane l16 < k holds choice l16
-    const int t = tid >> 4, l16 = tid & 15;
-    const bool valid = t < a.T;
-    const int tc = valid ? t : 0;
-    rdev::RowChoice c;
-    if (a.E <= 16) c = own_topk<1>(a, tc, valid, s_xst);
-    else if (a.E <= 32) c = own_topk<2>(a, tc, valid, s_xst);
-    else c = own_topk<4>(a, tc, valid, s_xst);
+    // pair p of this thread and its expert: routing here, token t = tid / 16
+    // by its row of lanes, lane l16 < k holding choice l16; else pair tid
+    rdev::RowChoice c{0, 0, 0.0f, 0.0f};
+    int p = tid, pe = 0;
+    bool chosen;
+    if constexpr (ROUTE) {
+        const int t = tid >> 4, l16 = tid & 15;
+        const bool valid = t < a.T;
+        const int tc = valid ? t : 0;
+        if (a.E <= 16) c = own_topk<1>(a, tc, valid, s_xst);
+        else if (a.E <= 32) c = own_topk<2>(a, tc, valid, s_xst);
+        else c = own_topk<4>(a, tc, valid, s_xst);
+        chosen = valid && l16 < a.k;
+        p = t * a.k + l16;
+        pe = c.id0;
+    } else {
+        chosen = tid < P;
+        if (chosen) pe = a.w.ids[tid];
+    }
     __syncthreads();   // s_cnt cleared
-    const bool chosen = valid && l16 < a.k;
-    const int p = t * a.k + l16;
     if (chosen) {
-        s_ids[p] = c.id0;
-        atomicAdd(&s_cnt[c.id0], 1);
+        s_ids[p] = pe;
+        atomicAdd(&s_cnt[pe], 1);
     }
     __syncthreads();
     // the routed experts by class, then id (every wave finds the same);
@@ -807,24 +828,24 @@ __global__ __launch_bounds__(kThreads, 3) void gate_up_own_route_kernel(FfnArgs 
     const uint64_t m0 = __ballot(act && first), m1 = __ballot(act && !first);
     const int n0 = __popcll(m0), n_act = n0 + __popcll(m1);
     if (ai >= n_act) return;
-    const uint64_t mk = act && first ? m0 : m1;
-    const int arank = (act && first ? 0 : n0) +
-                      __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    const int arank = (act && first) ? lanes_below(m0) : n0 + lanes_below(m1);
     const int e = __ffsll((unsigned long long)__ballot(act && arank == ai)) - 1;
-    // its pairs in pair order (at most one per token; T k <= 64: wave 0)
-    const int P = a.T * a.k;
+    // its pairs in pair order (at most one per token)
     const int Te = s_cnt[e];
     const bool mine = tid < P && s_ids[tid] == e;
     const uint64_t mm = __ballot(mine);
-    if (tid < 64 && mine)
-        s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u))] = tid;
+    if (lane == 0) s_wcnt[wave] = __popcll(mm);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wcnt[w];
+    if (mine) s_list[base + lanes_below(mm)] = tid;
     if (rt == 0) {
-        if (chosen && c.id0 == e) {
+        if (ROUTE && chosen && pe == e) {
             a.w.ids[p] = e;
             a.w.g[p] = c.g0;
         }
         if (ai == 0) {
-            if (tid < a.T) a.w.xst[tid] = s_xst[tid];
+            if (ROUTE && tid < a.T) a.w.xst[tid] = s_xst[tid];
             if (tid < a.E) {
                 a.w.dg.cnt[tid] = s_cnt[tid];
                 a.w.dg_next.cnt[tid] = 0;
@@ -839,7 +860,7 @@ __global__ __launch_bounds__(kThreads, 3) void gate_up_own_route_kernel(FfnArgs 
     __syncthreads();   // s_list complete
     if (rt == 0 && tid < Te) a.w.dg.list[(int64_t)e * a.w.tcap + tid] = s_list[tid];
     FfnArgs b = a;
-    b.w.xst = s_xst;
+    if (ROUTE) b.w.xst = s_xst;
     const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], Te, s_list, s_list[tid & 15]};
     ffn_width<0, PLANES, 1, 0>(b, lds_bytes, 1, 1, ex, a.tab.bits[e], rt, 0, xs, tok, prs);
 }
@@ -917,10 +938,11 @@ hipError_t launch_ffn(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer 
     if (MODE == 0 && a.own_route) {
         const int tiles = a.F / 64;
         const dim3 grid((unsigned)((int64_t)a.max_act * tiles));
-        return a.bitplane ? launch_timed(gate_up_own_route_kernel<true>, grid, dim3(kThreads), p.lds, s, t.start,
-                                         t.stop, a, (int)p.lds, tiles)
-                          : launch_timed(gate_up_own_route_kernel<false>, grid, dim3(kThreads), p.lds, s, t.start,
-                                         t.stop, a, (int)p.lds, tiles);
+        auto kernel = a.own_route == 1 ? (a.bitplane ? gate_up_own_route_kernel<true, true>
+                                                     : gate_up_own_route_kernel<false, true>)
+                                       : (a.bitplane ? gate_up_own_route_kernel<true, false>
+                                                     : gate_up_own_route_kernel<false, false>);
+        return launch_timed(kernel, grid, dim3(kThreads), p.lds, s, t.start, t.stop, a, (int)p.lds, tiles);
     }
     return a.bitplane ? launch_ffn_k<MODE, true>(a, p, s, t) : launch_ffn_k<MODE, false>(a, p, s, t);
 }
@@ -993,8 +1015,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FwdWork w, int d, int
 
 }  // namespace
 
-bool own_route_ok(int T, int E, int k) {
-    return T <= kOwnRouteTokens && E <= kOwnRouteExperts && k <= kOwnRouteTopK;
+int own_route_mode(int T, int E, int k) {
+    if (E > kOwnRouteExperts || k > kOwnRouteTopK) return 0;
+    return T <= kOwnRouteTokens ? 1 : (T <= kOwnGroupTokens ? 2 : 0);
 }
 
 // LDS for the staged token rows: all of the K range for up to min(T, 16)

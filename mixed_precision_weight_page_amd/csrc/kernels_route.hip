@@ -18,8 +18,9 @@
 // in slot order), so their router groups the pairs with atomic adds in the
 // same launch as the top-k: one kernel over many small workgroups, which
 // also takes each token's activation statistics (xscale.h). Batches of at
-// most 4 tokens over at most 64 experts are routed by the decode gate/up
-// kernel itself (kernels_ffn.hip), with the same top-k (route_dev.h).
+// most 16 tokens over at most 64 experts are grouped by the decode gate/up
+// kernel itself (kernels_ffn.hip; this router then skips its atomics), and
+// up to 4 tokens routed there too, with the same top-k (route_dev.h).
 //
 // The matrix-core kernels work on token tiles of a stable counting sort.
 // Up to 64 tokens (16 with more than 256 experts): one workgroup does
@@ -480,12 +481,12 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork 
         if (wave == 0) {
             const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
             const bool valid = t < a.T;
-            route_row(a, w, valid ? t : a.T - 1, valid, nullptr, true, stats);
+            route_row(a, w, valid ? t : a.T - 1, valid, nullptr, a.group != 0, stats);
         } else {
             stats();
         }
     } else if (ts < a.T) {
-        route_token(a, w, ts, nullptr, true, stats);
+        route_token(a, w, ts, nullptr, a.group != 0, stats);
     }
 }
 

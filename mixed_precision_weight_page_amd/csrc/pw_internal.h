@@ -150,6 +150,8 @@ struct RouteArgs {
     int tiles;   // also the large-batch kernels' token tiles (FwdWork::tiles)
     const int32_t* bits;   // [E] the table's widths, or NULL: the streaming router's active list
                            // puts the experts wider than 4 bits first (else arrival order)
+    int group = 1;         // the streaming router: 0 = ids, weights and statistics only (the
+                           // gate/up kernel groups the pairs)
 };
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,
                         KTimer t = {});
@@ -183,14 +185,17 @@ struct FfnArgs {
     int P;               // pair stride of the split partial outputs O[split][P][d]
     int bitplane;        // 1: bitplane pages (the table's bits are depths 1..8)
     int wide;            // 1: an expert may have more than 16 tokens (wide passes)
-    // own_route: the gate/up kernel routes the batch itself (own_route_ok):
-    // the logits [T, E] and the router's options
+    // own_route: 1, the gate/up kernel routes the batch itself; 2, it groups
+    // the pairs of the router's ids (own_route_mode); the logits [T, E] and
+    // the router's options
     int own_route;
     const float* logits;
     int T, E, renorm;
 };
-// the gate/up kernel can route a batch of T tokens over E experts, top-k, itself
-bool own_route_ok(int T, int E, int k);
+// 1: the gate/up kernel can route a batch of T tokens over E experts, top-k,
+// itself; 2: it can group the pairs of such a batch from the router's ids
+// (the router then only routes); 0: neither
+int own_route_mode(int T, int E, int k);
 hipError_t launch_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTimer t = {});
 hipError_t launch_combine(const FwdWork& w, int T, int d, int k, int P, int nsplit, float* y,

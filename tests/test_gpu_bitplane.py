@@ -52,7 +52,7 @@ def oracle_y_bp(x, logits, wl, masters, depth):
     return moe.forward(x.float(), logits, wl.k, bitplane.experts(*masters, depth), bool(wl.renorm))
 
 
-@pytest.mark.parametrize("T", [1, 40, 300])
+@pytest.mark.parametrize("T", [1, 12, 40, 300])
 def test_every_depth_pages_and_forward(T):
     masters = synth.expert_weights(WL)
     depth = [1 + e % 8 for e in range(WL.E)]

@@ -286,6 +286,20 @@ def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4, single_experts=
                                         f"scaled to all {len(experts)}"}}, y0
 
 
+def parity_line(bench, T, y_ref):
+    """The library's y on the oracle's first batch (the same seeded tokens
+    and logits as cpu_baseline's) against the oracle's float64 y: normwise
+    error and largest error over the largest |y|, with the bounds the
+    parity tests use."""
+    import torch
+    x, lg = bench.batches(T, 1, seed=99)[0]
+    y = bench.layers[0].moe_forward(x, lg)
+    torch.cuda.synchronize()
+    d = y.double().cpu() - y_ref
+    return {"normwise": float(d.norm() / y_ref.norm()), "max_abs_over_max_y": float(d.abs().max() / y_ref.abs().max()),
+            "bounds": [2e-3, 1e-2], "sample": f"the oracle's first {T}-token batch"}
+
+
 HBM = "GB/s"
 
 
@@ -495,10 +509,12 @@ def main():
         out["sweep"] = sw
     if not args.no_cpu_baseline:
         sample_T = T if args.workload != "prefill" else 64
-        cb, _ = cpu_baseline(b, sample_T, log)
+        cb, y_ref = cpu_baseline(b, sample_T, log)
         if args.workload == "prefill":
             cb["sample"] += " (64 of the 4096 tokens)"
         out["cpu_baseline"] = cb
+        out["parity"] = parity_line(b, sample_T, y_ref)
+        log(f"parity on the oracle's first batch: {out['parity']}")
     b.release()
     if default_run and not args.no_workloads:
         # the other configurations, each on its own layer (one at a time on

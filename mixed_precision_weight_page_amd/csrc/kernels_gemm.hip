@@ -120,23 +120,95 @@ __device__ __forceinline__ void permute32(const uint4 (&in)[4], uint4 out[4], in
     for (int q = 0; q < 4; ++q) out[q] = o.u[q];
 }
 
+// 8 consecutive bf16 activations scaled by 2^-e as fp16 in the K-slot
+// order of B-bit codes (B = 4 or 8: the order permutes within groups of 8).
+template <int B>
+__device__ __forceinline__ uint4 permute8(const uint4& in, int e) {
+    static_assert(B == 4 || B == 8, "orders within groups of 8");
+    const uint32_t ww[4] = {in.x, in.y, in.z, in.w};
+    _Float16 v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        v[2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
+        v[2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
+    }
+    union {
+        uint4 u;
+        _Float16 h[8];
+    } o;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o.h[s] = v[perm_slot<B>(s)];
+    return o.u;
+}
+
 // Token rows for the gate/up tiles, once per forward. One wave per token:
 // the token's statistics (xscale.h) into xst[t], then xp[i][t] = x[t] 2^-e
 // as fp16 in the K order of the codes of bit-width kBits[i], for each
-// bit-width some expert uses (bit i of mask). Lane l handles the
-// 32-activation groups l, l + 64, ..., read once more (from the cache) after
-// the statistics and written to every plane in use. grid ceil(T / 4).
+// bit-width some expert uses (bit i of mask). Up to 64 C 16-byte chunks
+// (d_model up to 512 C) the wave reads the row once, lane l holding chunks
+// l, l + 64, ... (each load and store instruction of the wave covers 1 KB
+// of consecutive bytes), and writes the 4- and 8-bit orders from those
+// registers; the 3-bit order, which permutes across 32 activations, reads
+// its 64-byte groups again (from the cache). Longer rows: statistics, then
+// every plane from a second read.
+template <int C>
 __global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int T, int d, int mask,
                                                           _Float16* xp, int64_t plane, XStat* xst) {
     const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     const uint16_t* row = x + (int64_t)t * d;
-    const XStat st = xsc::row_stat(row, d);
+    const int64_t base = (int64_t)t * d;
+    const int nch = d / 8;
+    XStat st;
+    if (nch <= 64 * C) {
+        const uint4* src = reinterpret_cast<const uint4*>(row);
+        uint4 in[C];
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int ch = lane + 64 * j;
+            in[j] = ch < nch ? src[ch] : uint4{0u, 0u, 0u, 0u};
+        }
+        // max |x| and sum |x| (eight partial sums per lane, fp64; the zero
+        // chunks past the row add nothing)
+        uint32_t mx = 0;
+        double part[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const uint32_t ww[4] = {in[j].x, in[j].y, in[j].z, in[j].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t lo = ww[h] & 0x7fffu, hi = (ww[h] >> 16) & 0x7fffu;
+                mx = max(mx, max(lo, hi));
+                part[2 * h] += (double)__uint_as_float(lo << 16);
+                part[2 * h + 1] += (double)__uint_as_float(hi << 16);
+            }
+        }
+        double sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            sum += __shfl_xor(sum, o);
+        }
+        const int e = xsc::x_exponent(__uint_as_float(mx << 16));
+        st = XStat{(float)ldexp(sum, -e), e};
+#pragma unroll
+        for (int i = 1; i < 3; ++i) {
+            if (!((mask >> i) & 1)) continue;
+            uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + base);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const int ch = lane + 64 * j;
+                if (ch < nch) dst[ch] = i == 1 ? permute8<4>(in[j], e) : permute8<8>(in[j], e);
+            }
+        }
+        mask &= 1;   // the 3-bit order below, if in use
+    } else {
+        st = xsc::row_stat(row, d);
+    }
     if (lane == 0) xst[t] = st;
     for (int grp = lane; grp < d / 32; grp += 64) {
-        const int64_t off = (int64_t)t * d + 32 * grp;
-        const uint4* src = reinterpret_cast<const uint4*>(x + off);
+        if (!mask) break;
+        const uint4* src = reinterpret_cast<const uint4*>(row + 32 * grp);
         const uint4 in[4] = {src[0], src[1], src[2], src[3]};
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -145,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void prep_x_kernel(const uint16_t* x, int
             if (i == 0) permute32<3>(in, o, st.e);
             else if (i == 1) permute32<4>(in, o, st.e);
             else permute32<8>(in, o, st.e);
-            uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + off);
+            uint4* dst = reinterpret_cast<uint4*>(xp + i * plane + base + 32 * grp);
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = o[q];
         }
@@ -490,7 +562,8 @@ bool gemm_supported(int d, int F) { return d % tile_rows<1>() == 0 && F % tile_r
 
 hipError_t launch_prep_x(const GemmArgs& a, hipStream_t s) {
     const int per_block = kThreads / 64;
-    return launch_timed(prep_x_kernel, dim3((unsigned)((a.T + per_block - 1) / per_block)), dim3(kThreads), 0, s,
+    auto kernel = a.d <= 8 * 64 * 8 ? prep_x_kernel<8> : prep_x_kernel<16>;
+    return launch_timed(kernel, dim3((unsigned)((a.T + per_block - 1) / per_block)), dim3(kThreads), 0, s,
                         (hipEvent_t) nullptr, (hipEvent_t) nullptr, a.x, a.T, a.d, a.bits_mask,
                         const_cast<_Float16*>(a.xp), a.xp_plane, a.w.xst);
 }

@@ -412,6 +412,28 @@ def test_large_batch_matrix_core_path(T):
     compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"matrix-core path T={T}")
 
 
+def test_small_batch_sweep():
+    """Seeded random small decode batches across the shapes whose routing
+    and grouping the gate/up kernel does itself (1-16 tokens, 1-64 experts,
+    top-1 to top-16, either normalisation, random widths), and just beyond
+    them (17 tokens, 65 experts). Every output against the oracle."""
+    rng = np.random.default_rng(7)
+    cases = [(int(rng.integers(1, 17)), int(rng.integers(1, 65)), None, int(rng.integers(0, 2))) for _ in range(24)]
+    cases += [(17, 12, 3, 0), (16, 65, 4, 1), (4, 64, 16, 0), (1, 1, 1, 0)]
+    for T, E, k, renorm in cases:
+        k = k or int(rng.integers(1, min(16, E) + 1))
+        bits = tuple(int(b) for b in rng.choice([3, 4, 8], size=E))
+        wl = synth.WORKLOADS["tiny"].scaled(name=f"sweep_{T}_{E}_{k}", E=E, d=256, F=128, k=k, T=T,
+                                            renorm=renorm, bits=bits)
+        masters = synth.expert_weights(wl)
+        layer, _ = make_layer(wl, masters, max_tokens=T)
+        layer.quantize_experts(wl.bits)
+        x, logits = synth.tokens(wl, seed=T * 1000 + E)
+        y = layer.moe_forward(x.cuda(), logits.cuda())
+        compare_y(y, oracle_y(x, logits, wl, masters, wl.bits), f"T={T} E={E} k={k} renorm={renorm}")
+        del layer
+
+
 @pytest.mark.parametrize("E,k,renorm", [(8, 2, 0), (40, 1, 1), (64, 16, 0), (17, 8, 1)])
 def test_small_batches_routed_by_the_gate_up_kernel(E, k, renorm):
     """Batches of at most 4 tokens over at most 64 experts are routed by the

@@ -50,8 +50,11 @@ struct DecodeGroup {
     int32_t* cnt;     // [E] pairs routed to each expert
     int32_t* n_act;   // [2] routed experts at the front of act, and at its back
     int32_t* act;     // [E] routed experts in arrival order, from the front (all
-                      // of them, or those wider than 4 bits) and from the back
+                      // of them, or those wider than 4 bits) and from the back;
+                      // in class and id order, from the front, when the gate/up
+                      // kernel groups the pairs
     int32_t* list;    // [E, tcap] pair indices of each expert, in arrival order
+                      // (in pair order when the gate/up kernel groups them)
     int E;            // entries of act
 };
 

@@ -102,83 +102,120 @@ using dq::perm_slot;
 // MODE 0 reads bf16 activations of the tokens in tok[], each row scaled by
 // its token's 2^-e; MODE 1 reads the (already scaled) fp16 SwiGLU rows of
 // the pairs in prs[] from H.
+// Loads per thread issued together before any is used: the row chunks of
+// a batch are in flight at once (one round trip per batch, not per chunk).
+template <int MODE, class C>
+__host__ __device__ constexpr int stage_batch() { return C::kPermSpan == 32 ? 1 : (MODE == 0 ? 4 : 2); }
+
 template <int MODE, class C>
 __device__ __forceinline__ void stage(_Float16* xs, int stride, const FfnArgs& a,
                                       const int* tok, const int* prs, int nt, int k0, int kc, int tid) {
+    constexpr int NBT = stage_batch<MODE, C>();
     if constexpr (C::kPermSpan == 32) {
-        // the order permutes across all 32 codes of a run
+        // the order permutes across all 32 codes of a run: 64 bytes (a
+        // group) per thread and item
         const int ngrp = kc / 32;
-        for (int idx = tid; idx < nt * ngrp; idx += kThreads) {
-            const int n = idx / ngrp, grp = idx - n * ngrp;
-            _Float16 v[32];
-            if constexpr (MODE == 0) {
-                const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 32 * grp);
-                const int e = a.w.xst[tok[n]].e;
+        const int total = nt * ngrp;
+        for (int base = tid; base < total; base += NBT * kThreads) {
+            uint4 u[NBT][4];
+            int ex[NBT];
+#pragma unroll
+            for (int j = 0; j < NBT; ++j) {
+                const int idx = base + j * kThreads;
+                if (idx < total) {
+                    const int n = idx / ngrp, grp = idx - n * ngrp;
+                    const uint4* src = MODE == 0
+                        ? reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 32 * grp)
+                        : reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 32 * grp);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) u[j][q] = src[q];
+                    ex[j] = MODE == 0 ? a.w.xst[tok[n]].e : 0;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NBT; ++j) {
+                const int idx = base + j * kThreads;
+                if (idx >= total) continue;
+                const int n = idx / ngrp, grp = idx - n * ngrp;
+                _Float16 v[32];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint4 u = src[q];
-                    const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+                    if constexpr (MODE == 0) {
+                        const uint32_t ww[4] = {u[j][q].x, u[j][q].y, u[j][q].z, u[j][q].w};
 #pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        v[8 * q + 2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
-                        v[8 * q + 2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
+                        for (int h = 0; h < 4; ++h) {
+                            v[8 * q + 2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), ex[j]);
+                            v[8 * q + 2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), ex[j]);
+                        }
+                    } else {
+                        union {
+                            uint4 u;
+                            _Float16 h[8];
+                        } t;
+                        t.u = u[j][q];
+#pragma unroll
+                        for (int h = 0; h < 8; ++h) v[8 * q + h] = t.h[h];
                     }
                 }
-            } else {
-                const uint4* src = reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 32 * grp);
+                union {
+                    uint4 u[4];
+                    _Float16 h[32];
+                } o;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int s = 0; s < 32; ++s) o.h[s] = v[C::perm(s)];
+                uint4* dst = reinterpret_cast<uint4*>(xs + n * stride + 32 * grp);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = o.u[q];
+            }
+        }
+    } else {
+        // 4- and 8-bit orders permute within groups of 8: one 16-byte chunk
+        // of 8 activations per thread and item
+        const int nch = kc / 8;
+        const int total = nt * nch;
+        for (int base = tid; base < total; base += NBT * kThreads) {
+            uint4 u[NBT];
+            int ex[NBT];
+#pragma unroll
+            for (int j = 0; j < NBT; ++j) {
+                const int idx = base + j * kThreads;
+                if (idx < total) {
+                    const int n = idx / nch, ch = idx - n * nch;
+                    u[j] = MODE == 0 ? *reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 8 * ch)
+                                     : *reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 8 * ch);
+                    ex[j] = MODE == 0 ? a.w.xst[tok[n]].e : 0;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NBT; ++j) {
+                const int idx = base + j * kThreads;
+                if (idx >= total) continue;
+                const int n = idx / nch, ch = idx - n * nch;
+                _Float16 v[8];
+                if constexpr (MODE == 0) {
+                    const uint32_t ww[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        v[2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), ex[j]);
+                        v[2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), ex[j]);
+                    }
+                } else {
                     union {
                         uint4 u;
                         _Float16 h[8];
                     } t;
-                    t.u = src[q];
+                    t.u = u[j];
 #pragma unroll
-                    for (int h = 0; h < 8; ++h) v[8 * q + h] = t.h[h];
+                    for (int h = 0; h < 8; ++h) v[h] = t.h[h];
                 }
-            }
-            union {
-                uint4 u[4];
-                _Float16 h[32];
-            } o;
-#pragma unroll
-            for (int s = 0; s < 32; ++s) o.h[s] = v[C::perm(s)];
-            uint4* dst = reinterpret_cast<uint4*>(xs + n * stride + 32 * grp);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = o.u[q];
-        }
-    } else {
-        // 4- and 8-bit orders permute within groups of 8: one 16-byte chunk
-        // of 8 activations per thread and iteration
-        const int nch = kc / 8;
-        for (int idx = tid; idx < nt * nch; idx += kThreads) {
-            const int n = idx / nch, ch = idx - n * nch;
-            _Float16 v[8];
-            if constexpr (MODE == 0) {
-                const uint4 u = *reinterpret_cast<const uint4*>(a.x + (int64_t)tok[n] * a.d + k0 + 8 * ch);
-                const int e = a.w.xst[tok[n]].e;
-                const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    v[2 * h] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] & 0xffffu), e);
-                    v[2 * h + 1] = (_Float16)xsc::bf16_scaled((uint16_t)(ww[h] >> 16), e);
-                }
-            } else {
                 union {
                     uint4 u;
                     _Float16 h[8];
-                } t;
-                t.u = *reinterpret_cast<const uint4*>(a.w.H + (int64_t)prs[n] * a.F + k0 + 8 * ch);
+                } o;
 #pragma unroll
-                for (int h = 0; h < 8; ++h) v[h] = t.h[h];
+                for (int s = 0; s < 8; ++s) o.h[s] = v[C::perm(s)];
+                *reinterpret_cast<uint4*>(xs + n * stride + 8 * ch) = o.u;
             }
-            union {
-                uint4 u;
-                _Float16 h[8];
-            } o;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) o.h[s] = v[C::perm(s)];
-            *reinterpret_cast<uint4*>(xs + n * stride + 8 * ch) = o.u;
         }
     }
 }

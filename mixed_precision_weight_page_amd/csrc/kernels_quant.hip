@@ -29,15 +29,30 @@ __device__ __forceinline__ const void* matrix_base(const void* w1, const void* w
     return mtx == 0 ? w1 : (mtx == 1 ? w3 : w2);
 }
 
-// Four consecutive weights as fp32 (fp16 masters convert exactly).
-__device__ __forceinline__ void load4(const void* base, int64_t idx, int f16, float v[4]) {
-    if (f16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const _Float16*>(base) + idx);
+// Four consecutive weights of fp16 (F16) or fp32 masters: the raw load and
+// its conversion to fp32 (fp16 converts exactly) are separate, so that a
+// thread's loads can all be issued before the first is used (the master
+// type is a template parameter: no branch between the loads).
+template <bool F16>
+struct Raw4 {
+    typedef uint2 type;
+};
+template <>
+struct Raw4<false> {
+    typedef float4 type;
+};
+template <bool F16>
+__device__ __forceinline__ typename Raw4<F16>::type load4_raw(const void* base, int64_t idx) {
+    if constexpr (F16) return *reinterpret_cast<const uint2*>(static_cast<const _Float16*>(base) + idx);
+    else return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+}
+template <bool F16>
+__device__ __forceinline__ void to_f32(const typename Raw4<F16>::type& u, float v[4]) {
+    if constexpr (F16) {
         const _Float16* h = reinterpret_cast<const _Float16*>(&u);
         v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
     } else {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
     }
 }
 
@@ -84,9 +99,10 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-// grid (3*M / kStatChunk, E)
+// grid (3*M / kStatChunk, E); every load of a thread in flight at once
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* w1, const void* w3,
-                                                          const void* w2, int f16, int64_t M,
+                                                          const void* w2, int64_t M,
                                                           uint32_t* absmax, uint32_t* flags) {
     const int e = blockIdx.y;
     const int64_t start = (int64_t)blockIdx.x * kStatChunk;
@@ -94,10 +110,14 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* w1, const 
     const void* base = matrix_base(w1, w3, w2, mtx);
     const int64_t off = (int64_t)e * M + (start - (int64_t)mtx * M);
     uint32_t m = 0, bad = 0;
-#pragma unroll 4
+    typename Raw4<F16>::type raw[kPerThread / 4];
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i)
+        raw[i] = load4_raw<F16>(base, off + (int64_t)(i * kThreads + threadIdx.x) * 4);
+#pragma unroll
     for (int i = 0; i < kPerThread / 4; ++i) {
         float v[4];
-        load4(base, off + (int64_t)(i * kThreads + threadIdx.x) * 4, f16, v);
+        to_f32<F16>(raw[i], v);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t a = __float_as_uint(v[j]) & 0x7fffffffu;
@@ -121,8 +141,9 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* w1, const 
 // grid (3*M / kStatChunk, E): per-block partial sums of (w - s q)^2 for
 // b = 3, 4, 8 in fp64 (bitplane pages: of (w - s8 c / 2)^2 at depths 3, 4,
 // 8), written in block order (no atomics).
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, const void* w3,
-                                                                const void* w2, int f16,
+                                                                const void* w2,
                                                                 int64_t M,
                                                                 const uint32_t* absmax,
                                                                 double* partial, int planes) {
@@ -140,9 +161,16 @@ __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, 
         inv_s[i] = s[i] > 0.0f ? 1.0f / s[i] : 0.0f;
     }
     double acc[3] = {0.0, 0.0, 0.0};
-    for (int i = 0; i < kPerThread / 4; ++i) {
+    // the loads of four iterations in flight at once
+    for (int i0 = 0; i0 < kPerThread / 4; i0 += 4) {
+      typename Raw4<F16>::type raw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+          raw[k] = load4_raw<F16>(base, off + (int64_t)((i0 + k) * kThreads + threadIdx.x) * 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
         float v[4];
-        load4(base, off + (int64_t)(i * kThreads + threadIdx.x) * 4, f16, v);
+        to_f32<F16>(raw[k], v);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (planes) {
@@ -163,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void loss_partial_kernel(const void* w1, 
                 }
             }
         }
+      }
     }
     __shared__ double red[kThreads / 64][3];
 #pragma unroll
@@ -263,8 +292,9 @@ __device__ __forceinline__ uint32_t plane_word(const uint8_t* codes, int j) {
 // (16-row block, 128-code step) order). Bitplane pages (planes != 0): the
 // codes are u8 of Eq. 2 at 8 bits with scale s8 (the table's scale), and
 // planes first[i] .. depth - 1 of the i-th listed expert are written.
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const void* w3,
-                                                        const void* w2, int f16, int d, int F,
+                                                        const void* w2, int d, int F,
                                                         DevTable tab, const int32_t* list,
                                                         const int32_t* first, int planes,
                                                         uint8_t* pool) {
@@ -288,13 +318,18 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const vo
     const int st = (int)(tt - rb * steps);
     const void* base = matrix_base(w1, w3, w2, mtx);
     uint8_t* codes = s_codes[wave];
-    // rows 2i + lane / 32 of the tile, weights 4 (lane % 32) .. +4
+    // rows 2i + lane / 32 of the tile, weights 4 (lane % 32) .. +4; all
+    // eight loads in flight before the first is used
     const int half = lane >> 5, c4 = 4 * (lane & 31);
+    typename Raw4<F16>::type raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        raw[i] = load4_raw<F16>(base, (int64_t)e * M + (rb * 16 + 2 * i + half) * K + st * 128 + c4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = 2 * i + half;
         float v[4];
-        load4(base, (int64_t)e * M + (rb * 16 + row) * K + st * 128 + c4, f16, v);
+        to_f32<F16>(raw[i], v);
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -320,7 +355,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const void* w1, const vo
 hipError_t launch_absmax(const void* w1, const void* w3, const void* w2, int f16, int E,
                          int64_t M, uint32_t* absmax, uint32_t* flags, hipStream_t s) {
     dim3 grid((unsigned)(3 * M / kStatChunk), (unsigned)E);
-    absmax_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, M, absmax, flags);
+    if (f16) absmax_kernel<true><<<grid, kThreads, 0, s>>>(w1, w3, w2, M, absmax, flags);
+    else absmax_kernel<false><<<grid, kThreads, 0, s>>>(w1, w3, w2, M, absmax, flags);
     return hipGetLastError();
 }
 
@@ -328,7 +364,8 @@ hipError_t launch_loss(const void* w1, const void* w3, const void* w2, int f16, 
                        int64_t M, const uint32_t* absmax, double* partial, double* loss, int planes,
                        hipStream_t s) {
     const int nblk = (int)(3 * M / kStatChunk);
-    loss_partial_kernel<<<dim3(nblk, E), kThreads, 0, s>>>(w1, w3, w2, f16, M, absmax, partial, planes);
+    if (f16) loss_partial_kernel<true><<<dim3(nblk, E), kThreads, 0, s>>>(w1, w3, w2, M, absmax, partial, planes);
+    else loss_partial_kernel<false><<<dim3(nblk, E), kThreads, 0, s>>>(w1, w3, w2, M, absmax, partial, planes);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     loss_final_kernel<<<E, kThreads, 0, s>>>(partial, nblk, 3 * M, loss);
@@ -341,7 +378,8 @@ hipError_t launch_pack(const void* w1, const void* w3, const void* w2, int f16, 
     if (nlist == 0) return hipSuccess;
     const int64_t M = (int64_t)F * d;
     dim3 grid((unsigned)(3 * M / 8192), (unsigned)nlist);
-    pack_kernel<<<grid, kThreads, 0, s>>>(w1, w3, w2, f16, d, F, tab, list, first, planes, pool);
+    if (f16) pack_kernel<true><<<grid, kThreads, 0, s>>>(w1, w3, w2, d, F, tab, list, first, planes, pool);
+    else pack_kernel<false><<<grid, kThreads, 0, s>>>(w1, w3, w2, d, F, tab, list, first, planes, pool);
     return hipGetLastError();
 }
 

@@ -5,7 +5,15 @@ baseline may import this package. The GPU library never imports, links or
 calls it, and it shares no code with the library: the only common dependency
 is the seeded input generator in ``synth``.
 
-Plain, slow and written to be checked by eye against the pages:
+Plain, slow and written to be checked by eye against the pages. The
+reference of the GPU parity tests is the plain C++ oracle:
+
+* ``c_oracle`` ``cpu_oracle.cpp`` (Eq. 2's scale, codes, pages and loss;
+             Eq. 1's allocation; the router and the float64 forward pass)
+             through ctypes; built with g++ on first use.
+
+A second oracle, written separately in float64 PyTorch, agrees with it and
+covers the rest:
 
 * ``quant``  Eq. 2 of the PagedWeight page (section "Implementation Details"):
              per-expert scale, codes, the page byte layout, the loss table.

@@ -17,8 +17,8 @@ so that weights come from HBM, not from the 256 MB Infinity Cache.
 roofline: the gate/up kernel (two thirds of the packed bytes), algorithmic
 bytes = packed W1 + W3 bytes of the experts the step routes to, divided by
 the kernel's mean duration from HIP events on the forward's stream.
-cpu_baseline: the CPU oracle (float64 PyTorch) timed on a bounded sample, on
-all host cores and single-threaded.
+cpu_baseline: the plain C++ CPU oracle (float64) timed on a bounded sample,
+on all host cores and single-threaded.
 
 One workload alone: --workload decode_fine | skewed | bitplane | prefill | dynamic | kvtrace | swap | tiny.
 """
@@ -220,70 +220,52 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4, single_experts=2):
-    """The oracle (float64, from the fp32 masters) on T-token batches of the
-    same layer: each batch quantizes its routed experts and runs the forward.
+def cpu_baseline(bench, T, log, min_seconds=10.0, max_batches=4):
+    """The plain C++ oracle (float64, from the fp32 masters) on T-token
+    batches of the same layer: each batch routes its tokens, quantizes the
+    experts they route to and runs the forward.
 
     All host threads (up to 16, the machine's CPU share per GPU): whole batches
-    one after another until min_seconds or max_batches. One thread: the
-    first batch's first `single_experts` routed experts only (each
-    quantized, then the SwiGLU of its tokens), scaled to all the batch's
-    routed experts (the oracle's cost is linear in them), labelled
-    extrapolated."""
-    import torch
-
-    from oracle import moe
+    one after another until min_seconds or max_batches (experts quantized
+    one per thread, tokens spread over the threads). One thread: the first
+    batch, whole."""
+    from oracle import c_oracle
     nproc = os.cpu_count() or 1
     batches = bench.batches(T, max_batches, seed=99)
+    w = [m.cpu() for m in bench.masters]   # host copies of the masters, not timed
 
-    def host_experts(experts):
-        return [m[experts].cpu() for m in bench.masters]   # not timed
+    def one_batch(x, lg, threads):
+        t0 = time.time()
+        y = c_oracle.moe_forward_quantized(x, lg, bench.wl.k, *w, bench.bits, bool(bench.wl.renorm),
+                                           nthreads=threads)
+        return time.time() - t0, y
 
-    # all threads: the oracle's whole forward
     threads = min(16, nproc)
-    torch.set_num_threads(threads)
     total, done, n_exp, y0 = 0.0, 0, [], None
     for x, lg in batches:
         x, lg = x.cpu(), lg.cpu()
-        ids, _ = moe.route(lg, bench.wl.k)
-        experts = sorted(set(ids.flatten().tolist()))
-        w = host_experts(experts)
-        remap = {e: i for i, e in enumerate(experts)}
-        t0 = time.time()
-        getter = moe.quantized_experts(*w, [bench.bits[e] for e in experts])
-        y = moe.forward(x, lg, bench.wl.k, lambda e: getter(remap[e]))
-        total += time.time() - t0
+        ids, _ = c_oracle.route(lg, bench.wl.k)
+        n_exp.append(len(set(ids.reshape(-1).tolist())))
+        dt, y = one_batch(x, lg, threads)
+        total += dt
         done += 1
-        n_exp.append(len(experts))
         y0 = y if y0 is None else y0
         if total >= min_seconds:
             break
     log(f"oracle, {threads} threads: {done} batches of {T} tokens in {total:.1f}s")
-    # one thread: part of the first batch
-    torch.set_num_threads(1)
     x, lg = batches[0]
-    x64 = x.cpu().double()
-    ids, _ = moe.route(lg.cpu(), bench.wl.k)
-    experts = sorted(set(ids.flatten().tolist()))
-    some = experts[:single_experts]
-    w = host_experts(some)
-    t0 = time.time()
-    getter = moe.quantized_experts(*w, [bench.bits[e] for e in some])
-    for i, e in enumerate(some):
-        rows = (ids == e).nonzero(as_tuple=True)[0]
-        moe.expert_ffn(x64[rows], *getter(i))
-    t1 = (time.time() - t0) * len(experts) / len(some)
-    torch.set_num_threads(threads)
-    log(f"oracle, 1 thread: {len(some)} of {len(experts)} experts, batch extrapolated to {t1:.1f}s")
+    t1, _ = one_batch(x.cpu(), lg.cpu(), 1)
+    log(f"oracle, 1 thread: one batch of {T} tokens in {t1:.1f}s")
+    import torch
     return {"value": T * done / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "nproc": nproc, "cpu_model": cpu_model(),
-            "sample": f"{done} batch(es) of {T} tokens of the same layer, each quantizing its routed experts "
-                      f"({', '.join(map(str, n_exp))}) from fp32 masters and running the float64 forward "
-                      f"(host copies of the masters excluded), {threads} threads; {cpu_model()}, nproc {nproc}",
+            "sample": f"the plain C++ oracle: {done} batch(es) of {T} tokens of the same layer, each routing its "
+                      f"tokens, quantizing the experts they route to ({', '.join(map(str, n_exp))}) from the fp32 "
+                      f"masters and running the float64 forward (host copies of the masters excluded), "
+                      f"{threads} threads; {cpu_model()}, nproc {nproc}",
             "single_thread": {"value": T / t1, "unit": "tokens/s", "cores": 1,
-                              "sample": f"extrapolated: {len(some)} of the {len(experts)} experts one batch of {T} "
-                                        f"tokens routes to, each quantized and run on its tokens, single-threaded, "
-                                        f"scaled to all {len(experts)}"}}, y0
+                              "sample": f"the first of those batches ({n_exp[0]} experts), whole, one thread"}}, \
+        torch.from_numpy(y0)
 
 
 def parity_line(bench, T, y_ref):
@@ -549,38 +531,33 @@ def main():
 
 
 def cpu_requant_baseline(masters, wl, p, L, log, min_seconds=10.0):
-    """The oracle's re-precision on the host: Eq. 1 solved for the first
-    budget of the schedule (the library's measured loss table as input),
-    then experts re-quantized from the fp16 masters into pages (max |w|,
-    scale, codes, packed page), alternating 8/4/3 bits, until
-    min_seconds; GB/s counts master bytes read plus page bytes written, as
-    requant_GBps does."""
-    import torch
-
-    from oracle import alloc, quant
-    threads = min(16, os.cpu_count() or 1)
-    torch.set_num_threads(threads)
+    """The plain C++ oracle's re-precision on the host, one thread: Eq. 1
+    solved for the first budget of the schedule (the library's measured loss
+    table as input), then experts re-quantized from the fp16 masters into
+    pages (max |w|, scale, codes, packed page), alternating 8/4/3 bits,
+    until min_seconds; GB/s counts master bytes read plus page bytes
+    written, as requant_GBps does."""
+    from oracle import c_oracle
     W = [wl.W_e] * wl.E
     t0 = time.time()
-    alloc.solve(list(p), L.tolist(), W, wl.budget_bits(wl.schedule[0]))
+    c_oracle.allocate(list(p), L, W, wl.budget_bits(wl.schedule[0]))
     t_solve = time.time() - t0
     total, nbytes, done = 0.0, 0.0, 0
     for e in range(wl.E):
-        w = [m[e].cpu() for m in masters]                # fp16, not timed
+        w = [m[e].cpu().float().numpy() for m in masters]   # fp16 -> fp32 exactly, not timed
         b = (8, 4, 3)[e % 3]
         t0 = time.time()
-        s = quant.scale(quant.expert_absmax(w), b)
-        quant.expert_page(w[0], w[1], w[2], b, s)
+        c_oracle.quantize_expert(w[0], w[1], w[2], b)
         total += time.time() - t0
         nbytes += wl.W_e * (2 + b / 8)
         done += 1
         if total >= min_seconds:
             break
-    log(f"oracle re-precision: solve {t_solve:.2f}s, {done} experts in {total:.1f}s")
-    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"Eq. 1 for {wl.E} experts in {t_solve * 1e3:.0f} ms, then {done} experts re-quantized "
-                      f"from fp16 masters into pages at 8/4/3 bits (master bytes read + page bytes written "
-                      f"per second, as requant_GBps); {cpu_model()}"}
+    log(f"oracle re-precision: solve {t_solve:.3f}s, {done} experts in {total:.1f}s")
+    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the plain C++ oracle, one thread: Eq. 1 for {wl.E} experts in {t_solve * 1e3:.1f} ms, then "
+                      f"{done} experts re-quantized from fp16 masters into pages at 8/4/3 bits (master bytes read + "
+                      f"page bytes written per second, as requant_GBps); {cpu_model()}"}
 
 
 def bench_dynamic(args, wl, log, cpu=True):

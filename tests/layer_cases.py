@@ -1,5 +1,8 @@
 """Shared helpers of the GPU tests: build a layer on cuda from synthetic
-masters, compute the oracle's reference on the CPU, compare."""
+masters, compute the oracle's reference on the CPU, compare. The reference
+pages, scales and outputs come from the plain C++ oracle (oracle/c_oracle.py);
+the Python oracle, pinned and compared with it separately, serves the
+bitplane layout, the scheduler and the host tier."""
 from __future__ import annotations
 
 import os
@@ -9,7 +12,7 @@ import numpy as np
 import torch
 
 import synth
-from oracle import alloc, moe, quant
+from oracle import alloc, c_oracle, moe, quant
 from pagemap import page_rows, tiled_row
 
 YTOL_NORM = 2e-3        # normwise relative error of y
@@ -90,28 +93,28 @@ def check_pages(layer, pool: torch.Tensor, masters, bits, experts=None, rows_per
     for e in experts:
         b = int(bits[e])
         ent = table[e]
-        m = quant.expert_absmax((w1[e], w3[e], w2[e]))
-        s = quant.scale(m, b)
+        s, q, want_page = c_oracle.quantize_expert(w1[e], w3[e], w2[e], b, want_page=rows_per_matrix is None)
         assert ent["bits"] == b, (e, ent)
         assert ent["scale"] == s, (e, ent["scale"], s)
-        assert ent["nbytes"] == quant.page_nbytes(d, F, b)
+        assert ent["nbytes"] == c_oracle.page_bytes(d, F, b)
         assert ent["offset"] % 256 == 0
         page = pool_h[ent["offset"]:ent["offset"] + ent["nbytes"]]
         if rows_per_matrix is None:
             # the device page read back through the tests' map of the tile
             # layout, against the oracle's row-major page
-            want = quant.expert_page(w1[e], w3[e], w2[e], b, s)
+            want = torch.from_numpy(want_page)
             got = page_rows(page, d, F, b)
             if not torch.equal(got, want):
                 bad = int((got != want).nonzero()[0])
                 raise AssertionError(f"expert {e} ({b} bits): first differing byte {bad}")
         else:
             off = 0
-            for mat in (w1[e], w3[e], w2[e]):
+            for mi, mat in enumerate((w1[e], w3[e], w2[e])):
                 rows, K = mat.shape
                 nb = rows * K * b // 8
+                qm = q[mi * d * F:(mi + 1) * d * F].reshape(rows, K)
                 for r in rng.choice(rows, size=min(rows, rows_per_matrix), replace=False):
-                    want = quant.pack_rows(quant.stored(quant.codes(mat[r:r + 1], s, b), b), b)[0]
+                    want = torch.from_numpy(c_oracle.pack_rows(qm[r:r + 1], b)[0])
                     got = torch.tensor(list(tiled_row(page[off:off + nb], K, b, int(r))), dtype=torch.uint8)
                     assert torch.equal(got, want), (e, b, int(r))
                 off += nb
@@ -125,12 +128,15 @@ def check_pages(layer, pool: torch.Tensor, masters, bits, experts=None, rows_per
 def oracle_bits(wl, masters, B, L=None):
     w1, w3, w2 = masters
     if L is None:
-        _, L = quant.loss_table(w1, w3, w2)
+        L = c_oracle.loss_table(w1, w3, w2, nthreads=cpu_threads())
     p = synth.importance(wl)
-    bits, _ = alloc.solve(p, L.tolist(), [wl.W_e] * wl.E, B)
+    bits, _ = c_oracle.allocate(p, L, [wl.W_e] * wl.E, B)
     return bits, L
 
 
 def oracle_y(x, logits, wl, masters, bits):
+    """y of the plain C++ oracle (float64) for bf16 x, from the fp masters
+    quantized at bits."""
     w1, w3, w2 = masters
-    return moe.moe_forward_quantized(x.float(), logits, wl.k, w1, w3, w2, bits, bool(wl.renorm))
+    y = c_oracle.moe_forward_quantized(x, logits, wl.k, w1, w3, w2, bits, bool(wl.renorm), nthreads=cpu_threads())
+    return torch.from_numpy(y)

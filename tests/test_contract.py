@@ -48,3 +48,16 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_cpp_oracle_shares_nothing_with_the_library():
+    """The plain C++ oracle includes only standard headers, and no library
+    source or Python module of the package names it."""
+    import re
+    src = open(os.path.join(ROOT, "oracle", "cpu_oracle.cpp")).read()
+    includes = re.findall(r'#include\s*[<"]([^>"]+)[>"]', src)
+    assert includes and all(h in ("math.h", "stdint.h", "string.h", "vector") for h in includes), includes
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                assert "cpu_oracle" not in open(os.path.join(dirpath, f)).read(), f

@@ -10,7 +10,7 @@ import synth
 from layer_cases import (check_pages, compare_y, cpu_threads, log, make_layer, oracle_bits,
                          oracle_y)
 from oracle import sched as osched
-from oracle import alloc, moe, quant
+from oracle import alloc, c_oracle, moe, quant
 
 pytestmark = pytest.mark.gpu
 
@@ -97,7 +97,7 @@ def test_loss_table_matches_oracle(wl):
     masters = synth.expert_weights(wl)
     layer, _ = make_layer(wl, masters, max_tokens=8)
     got = layer.get_loss_table()
-    _, want = quant.loss_table(*masters)
+    want = c_oracle.loss_table(*masters, nthreads=cpu_threads())
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
     assert np.all(got[:, 2] < got[:, 1])   # 8 bits beat 4 bits
 
@@ -192,14 +192,14 @@ def test_reprecision_schedule():
     wl = SMALL_DYN
     masters = synth.expert_weights(wl)
     layer, pool = make_layer(wl, masters, max_tokens=wl.T)
-    _, L = quant.loss_table(*masters)
+    L = c_oracle.loss_table(*masters, nthreads=cpu_threads())
     p = synth.importance(wl)
     prev_bits, prev_pool, prev_table = None, None, None
     for step, avg in enumerate(wl.schedule):
         B = wl.budget_bits(avg)
         bits = layer.set_budget(B, p)
         torch.cuda.synchronize()
-        want, _ = alloc.solve(p, L.tolist(), [wl.W_e] * wl.E, B)
+        want, _ = c_oracle.allocate(p, L, [wl.W_e] * wl.E, B)
         assert bits.tolist() == want, avg
         check_pages(layer, pool, masters, bits)
         table = layer.get_page_table()
@@ -305,7 +305,7 @@ def test_budget_scheduler_follows_a_kv_trace():
     masters = synth.expert_weights(wl)
     layer, pool = make_layer(wl, masters, max_tokens=wl.T)
     p = synth.importance(wl)
-    _, Ltab = quant.loss_table(*masters)
+    Ltab = c_oracle.loss_table(*masters, nthreads=cpu_threads())
     W = [wl.W_e] * wl.E
     pool8 = osched.pool_nbytes(W, [8] * wl.E)
     memory, reserve, h, n = pool8 + pool8 // 8, pool8 // 16, 0.05, 3
@@ -321,7 +321,7 @@ def test_budget_scheduler_follows_a_kv_trace():
         action, B, pressure = got
         seen.add(action)
         if action != osched.KEEP:
-            bits_want, _ = alloc.solve(p, Ltab.tolist(), W, B)
+            bits_want, _ = c_oracle.allocate(p, Ltab, W, B)
             table = layer.get_page_table()
             bits = [int(e["bits"]) for e in table]
             assert bits == list(bits_want), t

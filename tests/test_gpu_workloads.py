@@ -16,7 +16,7 @@ import torch
 
 import synth
 from layer_cases import check_pages, compare_y, cpu_threads, log, make_layer, oracle_y
-from oracle import alloc, quant
+from oracle import c_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def layer_for(name, max_tokens):
         t0 = time.time()
         dev = synth.expert_weights(wl, device="cuda", seed=0)
         host = tuple(m.cpu() for m in dev)
-        _, L = quant.loss_table(*host)
+        L = c_oracle.loss_table(*host, nthreads=cpu_threads())
         log(f"{name}: masters + oracle loss table {time.time() - t0:.1f}s")
         _cache[name] = (wl, dev, host, L)
     wl, dev, host, L = _cache[name]
@@ -59,7 +59,7 @@ def budget_and_pages(wl, layer, pool, host, L, B, sample_experts):
     t0 = time.time()
     bits = layer.set_budget(B, p)
     torch.cuda.synchronize()
-    want, _ = alloc.solve(p, L.tolist(), [wl.W_e] * wl.E, B)
+    want, _ = c_oracle.allocate(p, L, [wl.W_e] * wl.E, B)
     assert bits.tolist() == want
     assert int(bits.astype(np.int64).sum()) * wl.W_e <= B
     check_pages(layer, pool, host, bits, experts=sample_experts)
@@ -96,7 +96,7 @@ def test_decode_fine_skewed_full():
     than 16 of the 64 tokens. Every output against the oracle."""
     wl, layer, pool, host, L = layer_for("decode_fine", max_tokens=64)
     bits = layer.set_budget(wl.budget_bits(), synth.importance(wl))
-    want, _ = alloc.solve(synth.importance(wl), L.tolist(), [wl.W_e] * wl.E, wl.budget_bits())
+    want, _ = c_oracle.allocate(synth.importance(wl), L, [wl.W_e] * wl.E, wl.budget_bits())
     assert bits.tolist() == want
     x, logits = synth.tokens(wl, device="cuda", seed=2)
     logits = logits + torch.log(torch.tensor(synth.importance(wl), dtype=torch.float32, device="cuda"))

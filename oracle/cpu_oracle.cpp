@@ -144,7 +144,10 @@ int orc_quantize_expert(const float* w1, const float* w3, const float* w2, int d
     return 0;
 }
 
-// L(b): mean over the expert's 3 d F weights of (w - s q)^2
+// L(b): mean over the expert's 3 d F weights of (w - s q)^2. The squared
+// errors are summed row by row (W1, W3: F rows of d; W2: d rows of F), then
+// the row sums: the sum's relative rounding error stays below
+// (row length + rows) 2^-53 instead of 3 d F 2^-53.
 double orc_loss(const float* w1, const float* w3, const float* w2, int d, int F, int b) {
     const int64_t n = (int64_t)d * F;
     double m = orc_absmax(w1, n);
@@ -155,9 +158,15 @@ double orc_loss(const float* w1, const float* w3, const float* w2, int d, int F,
     const float* mats[3] = {w1, w3, w2};
     double total = 0.0;
     for (int t = 0; t < 3; ++t) {
-        for (int64_t i = 0; i < n; ++i) {
-            const double e = (double)mats[t][i] - (double)s * code_of(mats[t][i], s, b);
-            total += e * e;
+        const int rows = t < 2 ? F : d, K = t < 2 ? d : F;
+        for (int r = 0; r < rows; ++r) {
+            double row = 0.0;
+            for (int j = 0; j < K; ++j) {
+                const float w = mats[t][(int64_t)r * K + j];
+                const double e = (double)w - (double)s * code_of(w, s, b);
+                row += e * e;
+            }
+            total += row;
         }
     }
     return total / (double)(3 * n);

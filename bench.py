@@ -400,7 +400,14 @@ def main():
         return
     if args.workload == "bitplane":
         wl = synth.WORKLOADS["decode_fine"]
-        res, _, _, _ = measure(wl, wl.T, args, log, args.pools, layout="bitplane")
+        res, _, _, gu_bytes = measure(wl, wl.T, args, log, args.pools, layout="bitplane")
+        # planes read per gate/up launch (depth x W1, W3 bits of the routed
+        # experts) and the counters' HBM bytes (null once the kernels changed)
+        res["gate_up_code_bytes_per_launch"] = gu_bytes
+        traffic = traffic_from_profiles("bitplane", wl.T)
+        res["gate_up_traffic_bytes"] = traffic
+        if traffic:
+            res["gate_up_traffic_over_code_bytes"] = traffic / gu_bytes
         print(json.dumps({"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
                           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
                           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
@@ -505,7 +512,7 @@ def main():
         for key, w, bias, layout, prof in (
                 ("decode_fine_T64", synth.WORKLOADS["decode_fine"], None, "eq2", "decode_fine"),
                 ("decode_fine_skewed_T64", synth.WORKLOADS["decode_fine"], "skew", "eq2", "skewed"),
-                ("decode_fine_bitplane_T64", synth.WORKLOADS["decode_fine"], None, "bitplane", None),
+                ("decode_fine_bitplane_T64", synth.WORKLOADS["decode_fine"], None, "bitplane", "bitplane"),
                 ("prefill_T4096", synth.WORKLOADS["prefill"], None, "eq2", "prefill")):
             t0 = time.time()
             res, _, _, gu_bytes = measure(w, w.T, args, log, 2 if w.name == "prefill" else args.pools,

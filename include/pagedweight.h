@@ -159,7 +159,9 @@ pw_status pw_set_budget(pw_ctx* ctx, uint64_t budget_bits, const double* importa
  * Per token: the top_k largest logits (equal values -> lower expert index),
  * g = softmax weight (see desc.renorm), y = sum_j g_j * W2 (silu(W1 x) *
  * (W3 x)) with W = s_e * q read from the pages. 0 <= T <= max_tokens; T = 0
- * does nothing. Asynchronous: no host synchronisation. */
+ * does nothing. Asynchronous: no host synchronisation. Not replayable from
+ * a captured graph (the grouping counters it uses alternate between calls
+ * on the host side); pw_moe_forward_noalloc is. */
 pw_status pw_moe_forward(pw_ctx* ctx, const void* x, const float* logits, int32_t T,
                          float* y, void* stream);
 
@@ -175,7 +177,10 @@ pw_status pw_moe_forward(pw_ctx* ctx, const void* x, const float* logits, int32_
  * 128 experts, d_model 2048, d_ff 768, top-8 need about 27 MiB). Every call
  * on a device shares that device's array: calls that may overlap on one
  * device (several streams, several contexts) race and must be serialized by
- * the caller. The context's pages must exist (PW_ERR_STATE otherwise). */
+ * the caller. The context's pages must exist (PW_ERR_STATE otherwise). It
+ * only launches kernels on the stream (its counters are cleared by a kernel
+ * on every call), so a call captured in a graph may be replayed, with the
+ * inputs it was captured with updated in place between replays. */
 pw_status pw_moe_forward_noalloc(pw_ctx* ctx, const void* x, const float* logits, int32_t T, float* y,
                                  void* stream);
 

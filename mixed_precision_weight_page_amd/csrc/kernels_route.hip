@@ -466,11 +466,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 // finished).
 __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork w) {
     if (blockIdx.x == 0) {
-        for (int e = threadIdx.x; e < a.E; e += 256) w.dg_next.cnt[e] = 0;
+        for (int e = threadIdx.x; e < a.E; e += blockDim.x) w.dg_next.cnt[e] = 0;
         if (threadIdx.x < 2) w.dg_next.n_act[threadIdx.x] = 0;
     }
     const int wave = threadIdx.x >> 6;
-    const int ts = blockIdx.x * 4 + wave;   // this wave's token for the statistics
+    const int ts = blockIdx.x * (blockDim.x >> 6) + wave;   // this wave's token for the statistics
     auto stats = [&]() {
         if (a.x && ts < a.T) {
             const XStat st = lanes_stat<64>(a.x + (int64_t)ts * a.d, a.d);
@@ -558,6 +558,10 @@ hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
 }
 
 hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
+    // beyond 64 experts every token is one wave's own work: one wave per
+    // workgroup spreads the tokens over as many CUs
+    if (a.E > kRowDecodeMaxExperts)
+        return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(64), 0, s, t.start, t.stop, a, w);
     return launch_timed(route_decode_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, t.start, t.stop, a,
                         w);
 }

@@ -477,7 +477,11 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork 
             if ((threadIdx.x & 63) == 0) w.xst[ts] = st;
         }
     };
-    if (a.E <= kRowDecodeMaxExperts) {
+    if (a.E <= kRowDecodeMaxExperts && blockDim.x == 64) {
+        // one token per workgroup: its first row of 16 lanes routes it, all
+        // 64 lanes take its statistics
+        route_row(a, w, ts, (threadIdx.x >> 4) == 0, nullptr, a.group != 0, stats);
+    } else if (a.E <= kRowDecodeMaxExperts) {
         if (wave == 0) {
             const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
             const bool valid = t < a.T;
@@ -558,12 +562,9 @@ hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
 }
 
 hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
-    // beyond 64 experts every token is one wave's own work: one wave per
-    // workgroup spreads the tokens over as many CUs
-    if (a.E > kRowDecodeMaxExperts)
-        return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(64), 0, s, t.start, t.stop, a, w);
-    return launch_timed(route_decode_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, t.start, t.stop, a,
-                        w);
+    // one token per 64-thread workgroup (no workgroup barriers on either
+    // path): the tokens spread over as many CUs
+    return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(64), 0, s, t.start, t.stop, a, w);
 }
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,

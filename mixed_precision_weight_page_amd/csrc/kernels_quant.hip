@@ -63,16 +63,20 @@ __device__ __forceinline__ float scale_of(float m, int qm) {
 }
 
 // round-half-to-even of the exact quotient w / s (s > 0), without a
-// divide: r = rint(w * (1/s)) is within one of the correctly rounded
-// quotient (the product is off by a few units in the last place of a value
-// of magnitude at most qmax), and the two neighbouring midpoints are then
-// tested exactly: fma(-(r +- 1/2), s, w) is w - (r +- 1/2) s rounded once,
-// so its sign (and whether it is zero) is that of the exact difference.
-// Scales below 2^-100 take the fp64 path so that the difference cannot
-// underflow.
+// divide. p = w * (1/s) rounds twice (1/s and the product), so it differs
+// from w / s by at most |p| 2^-22; r = rint(p), and p - r is exact (both are
+// multiples of p's last place and |p - r| <= 1/2). If p is closer to r than
+// 1/2 - |p| 2^-22, so is w / s, and r is its rounding: nearly every weight
+// ends there. Otherwise r is within one of the correctly rounded quotient
+// and the two neighbouring midpoints are tested exactly: fma(-(r +- 1/2),
+// s, w) is w - (r +- 1/2) s rounded once, so its sign (and whether it is
+// zero) is that of the exact difference. Scales below 2^-100 take the fp64
+// path so that the difference cannot underflow.
 __device__ __forceinline__ float round_quotient(float w, float s, float inv_s) {
     if (s < 7.8886091e-31f) return (float)rint((double)w / (double)s);
-    float r = rintf(w * inv_s);
+    const float p = w * inv_s;
+    float r = rintf(p);
+    if (fabsf(p - r) < fmaf(fabsf(p), -2.384185791015625e-07f, 0.5f)) return r;
     const float hi = fmaf(-(r + 0.5f), s, w);   // sign of w/s - (r + 1/2)
     const float lo = fmaf(-(r - 0.5f), s, w);   // sign of w/s - (r - 1/2)
     const bool odd = ((int)r) & 1;

@@ -457,40 +457,30 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 }
 
 // ---- streaming kernels: top-k, grouping by atomics, token statistics ----
-// grid ceil(T / 4), 256 threads: wave w of block b takes the statistics of
-// token 4b + w (all 64 lanes load the row at once); with at most 64 experts
-// wave 0 also routes the block's four tokens (row r of 16 lanes: token
-// 4b + r), issuing its logits loads before its statistics, else each wave
-// routes its own token. Block 0 also clears the other counter set for the
-// next forward (every kernel of the previous forward, which used it, has
-// finished).
-__global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a, FwdWork w) {
+// grid T, one token per workgroup (no workgroup barriers, so the tokens
+// spread over as many CUs). Up to 64 experts, 64 threads: the first row of
+// 16 lanes routes token t (its logits loads issued before the statistics),
+// all 64 lanes take the token's statistics. Beyond, 128 threads: wave 0
+// routes the token while wave 1 takes its statistics. Block 0 also clears
+// the other counter set for the next forward (every kernel of the previous
+// forward, which used it, has finished).
+__global__ __launch_bounds__(128) void route_decode_kernel(RouteArgs a, FwdWork w) {
     if (blockIdx.x == 0) {
         for (int e = threadIdx.x; e < a.E; e += blockDim.x) w.dg_next.cnt[e] = 0;
         if (threadIdx.x < 2) w.dg_next.n_act[threadIdx.x] = 0;
     }
-    const int wave = threadIdx.x >> 6;
-    const int ts = blockIdx.x * (blockDim.x >> 6) + wave;   // this wave's token for the statistics
+    const int t = blockIdx.x;
     auto stats = [&]() {
-        if (a.x && ts < a.T) {
-            const XStat st = lanes_stat<64>(a.x + (int64_t)ts * a.d, a.d);
-            if ((threadIdx.x & 63) == 0) w.xst[ts] = st;
+        if (a.x) {
+            const XStat st = lanes_stat<64>(a.x + (int64_t)t * a.d, a.d);
+            if ((threadIdx.x & 63) == 0) w.xst[t] = st;
         }
     };
-    if (a.E <= kRowDecodeMaxExperts && blockDim.x == 64) {
-        // one token per workgroup: its first row of 16 lanes routes it, all
-        // 64 lanes take its statistics
-        route_row(a, w, ts, (threadIdx.x >> 4) == 0, nullptr, a.group != 0, stats);
-    } else if (a.E <= kRowDecodeMaxExperts) {
-        if (wave == 0) {
-            const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
-            const bool valid = t < a.T;
-            route_row(a, w, valid ? t : a.T - 1, valid, nullptr, a.group != 0, stats);
-        } else {
-            stats();
-        }
-    } else if (ts < a.T) {
-        route_token(a, w, ts, nullptr, a.group != 0, stats);
+    if (a.E > kRowDecodeMaxExperts) {
+        if (threadIdx.x < 64) route_token(a, w, t, nullptr, a.group != 0);
+        else stats();
+    } else {
+        route_row(a, w, t, threadIdx.x < 16, nullptr, a.group != 0, stats);
     }
 }
 
@@ -562,9 +552,11 @@ hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
 }
 
 hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
-    // one token per 64-thread workgroup (no workgroup barriers on either
-    // path): the tokens spread over as many CUs
-    return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(64), 0, s, t.start, t.stop, a, w);
+    // one token per workgroup (no workgroup barriers on either path): the
+    // tokens spread over as many CUs; beyond 64 experts two waves per token
+    // (routing, statistics)
+    return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(a.E > kRowDecodeMaxExperts ? 128 : 64), 0, s,
+                        t.start, t.stop, a, w);
 }
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,

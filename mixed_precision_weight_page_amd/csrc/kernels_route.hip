@@ -457,11 +457,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a, FwdWork w) {
 }
 
 // ---- streaming kernels: top-k, grouping by atomics, token statistics ----
-// grid T, one token per workgroup (no workgroup barriers, so the tokens
-// spread over as many CUs). Up to 64 experts, 64 threads: the first row of
-// 16 lanes routes token t (its logits loads issued before the statistics),
-// all 64 lanes take the token's statistics. Beyond, 128 threads: wave 0
-// routes the token while wave 1 takes its statistics. Block 0 also clears
+// grid T, 128 threads: one token per workgroup (no workgroup barriers, so
+// the tokens spread over as many CUs). Wave 0 routes token t (up to 64
+// experts with its first row of 16 lanes, beyond with the whole wave) while
+// wave 1 takes the token's statistics. Block 0 also clears
 // the other counter set for the next forward (every kernel of the previous
 // forward, which used it, has finished).
 __global__ __launch_bounds__(128) void route_decode_kernel(RouteArgs a, FwdWork w) {
@@ -476,12 +475,9 @@ __global__ __launch_bounds__(128) void route_decode_kernel(RouteArgs a, FwdWork 
             if ((threadIdx.x & 63) == 0) w.xst[t] = st;
         }
     };
-    if (a.E > kRowDecodeMaxExperts) {
-        if (threadIdx.x < 64) route_token(a, w, t, nullptr, a.group != 0);
-        else stats();
-    } else {
-        route_row(a, w, t, threadIdx.x < 16, nullptr, a.group != 0, stats);
-    }
+    if (threadIdx.x >= 64) stats();
+    else if (a.E > kRowDecodeMaxExperts) route_token(a, w, t, nullptr, a.group != 0);
+    else route_row(a, w, t, threadIdx.x < 16, nullptr, a.group != 0);
 }
 
 // grid (E, C), 256 threads: rank of expert e's pairs in token order among
@@ -552,11 +548,8 @@ hipError_t launch_zero_i32(int32_t* p, uint64_t n, hipStream_t s) {
 }
 
 hipError_t launch_route_decode(const RouteArgs& a, const FwdWork& w, hipStream_t s, KTimer t) {
-    // one token per workgroup (no workgroup barriers on either path): the
-    // tokens spread over as many CUs; beyond 64 experts two waves per token
-    // (routing, statistics)
-    return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(a.E > kRowDecodeMaxExperts ? 128 : 64), 0, s,
-                        t.start, t.stop, a, w);
+    // one token per workgroup, two waves (routing, statistics)
+    return launch_timed(route_decode_kernel, dim3((unsigned)a.T), dim3(128), 0, s, t.start, t.stop, a, w);
 }
 
 hipError_t launch_route(const RouteArgs& a, const FwdWork& w, const DevTable& tab, hipStream_t s,

@@ -183,6 +183,25 @@ def allocate_brute(p, L, W, B):
     return _solve(lib().orc_allocate_brute, p, L, W, B)
 
 
+def allocate_layers(ps, Ls, Ws, B, layer_weights=None):
+    """Eq. 1 with one budget B over the experts of several layers: the
+    objective sum_l w_l sum_e p_{l,e} L_{l,e}(b) and the constraint are sums
+    over the union of the layers' experts, so this is the DP above on that
+    union with importances w_l p_{l,e}. Returns (per-layer bit lists,
+    objective)."""
+    n = len(ps)
+    w = [1.0] * n if layer_weights is None else [float(v) for v in layer_weights]
+    p_all = np.concatenate([w[l] * np.asarray(ps[l], dtype=np.float64) for l in range(n)])
+    L_all = np.concatenate([np.asarray(Ls[l], dtype=np.float64).reshape(-1, 3) for l in range(n)])
+    W_all = np.concatenate([np.asarray(Ws[l], dtype=np.uint64) for l in range(n)])
+    bits, obj = allocate(p_all, L_all, W_all, B)
+    out, i = [], 0
+    for l in range(n):
+        out.append(bits[i:i + len(ps[l])])
+        i += len(ps[l])
+    return out, obj
+
+
 def route(logits, k: int, renorm: bool = False):
     """(ids int32 [T, k], g float64 [T, k])."""
     l = _f32(logits)

@@ -10,7 +10,7 @@ import synth
 from layer_cases import (check_pages, compare_y, cpu_threads, log, make_layer, oracle_bits,
                          oracle_y)
 from oracle import sched as osched
-from oracle import alloc, c_oracle, moe, quant
+from oracle import c_oracle, moe
 
 pytestmark = pytest.mark.gpu
 
@@ -133,12 +133,12 @@ def test_budget_shared_by_two_layers():
         pools.append(pool)
         masters.append(m)
         ps.append(list(synth.importance(wl)))
-        Ls.append(quant.loss_table(*m)[1])
+        Ls.append(c_oracle.loss_table(*m, nthreads=cpu_threads()))
     B = int(4.5 * sum(wl.E * wl.W_e for wl in wls))
     log("two layers: set_budget_layers")
     bits, obj = set_budget_layers(layers, B, ps, layer_weights=[1.0, 2.0])
     torch.cuda.synchronize()
-    want, want_obj = alloc.solve_layers(ps, Ls, [[wl.W_e] * wl.E for wl in wls], B, [1.0, 2.0])
+    want, want_obj = c_oracle.allocate_layers(ps, Ls, [[wl.W_e] * wl.E for wl in wls], B, [1.0, 2.0])
     assert [b.tolist() for b in bits] == want
     assert obj == pytest.approx(want_obj, rel=1e-12)
     assert sum(int(b.astype(np.int64).sum()) * wl.W_e for b, wl in zip(bits, wls)) <= B

@@ -234,6 +234,36 @@ def test_allocation_identical_experts_follow_importance():
         assert all(bits[e] >= bits[e + 1] for e in range(E - 1)), (avg, bits)
 
 
+def test_allocation_over_several_layers():
+    """One budget over two or three layers: enumeration over the union of
+    their experts (importances times the layer weights) and the Python
+    oracle's solver give the same bits and objective."""
+    rng = random.Random(107)
+    for trial in range(60):
+        n = rng.randint(2, 3)
+        ps, Ls, Ws = [], [], []
+        for _ in range(n):
+            E = rng.randint(1, 3)
+            ps.append([rng.random() for _ in range(E)])
+            Ls.append([[l4 + rng.uniform(1e-3, 1.0), l4, l4 - rng.uniform(1e-4, 1e-3)]
+                       for l4 in (rng.uniform(0.01, 0.5) for _ in range(E))])
+            Ws.append([rng.choice([2, 3, 4])] * E)
+        lw = [rng.uniform(0.5, 2.0) for _ in range(n)]
+        tot = sum(sum(W) for W in Ws)
+        B = rng.randint(3 * tot, 8 * tot)
+        got, obj = C.allocate_layers(ps, Ls, Ws, B, lw)
+        flat_p = [lw[l] * v for l in range(n) for v in ps[l]]
+        flat_L = [row for l in range(n) for row in Ls[l]]
+        flat_W = [v for W in Ws for v in W]
+        want_bits, want_obj = C.allocate_brute(flat_p, flat_L, flat_W, B)
+        # random problems have a unique optimum; both sum the objective in
+        # expert order
+        assert [b for bl in got for b in bl] == want_bits, trial
+        assert obj == want_obj
+        py_bits, py_obj = alloc.solve_layers(ps, Ls, Ws, B, lw)
+        assert obj == pytest.approx(py_obj, rel=1e-12, abs=0)
+
+
 def test_router_ties_and_closed_forms():
     ids, g = C.route(np.array([[0.5, 2.0, -1.0, 2.0]], dtype=np.float32), 2)
     assert ids.tolist() == [[1, 3]]

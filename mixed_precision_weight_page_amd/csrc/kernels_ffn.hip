@@ -423,6 +423,8 @@ struct ExpertRef {
     int Te;
     const int32_t* list;
     int p0;
+    int tb0 = 0;     // first token of the workgroup's passes
+    int tstep = 0;   // tokens between its passes (0: one pass after another)
 };
 
 // NB: blocks of 16 tokens per pass over the codes (1, or 4 for the experts
@@ -469,7 +471,8 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int lds_bytes, const 
         ap[m] = C::source(page + (MODE == 0 ? m : 2) * mat_bytes + ((int64_t)(row0 / 16) * KS + ks0) * SB);
     const int loff = C::lane_offset(lane);
 
-    for (int tb = 0; tb < Te; tb += 16 * NB) {
+    const int tstep = ex.tstep ? ex.tstep : 16 * NB;
+    for (int tb = ex.tb0; tb < Te; tb += tstep) {
         const int nt = min(16 * NB, Te - tb);
         const int nblk = (nt + 15) >> 4;
         // steps per LDS chunk: all of them if nt rows fit, else a multiple of
@@ -666,12 +669,12 @@ __device__ __forceinline__ void ffn_width(const FfnArgs& a, int lds_bytes, int n
 
 template <int MODE, bool PLANES, int NB, int SEQ>
 __device__ __forceinline__ void ffn_role(const FfnArgs& a, int lds_bytes, int nsplit, int rpw, int e, int rem,
-                                         _Float16* xs, int* tok, int* prs) {
+                                         _Float16* xs, int* tok, int* prs, int tb0 = 0, int tstep = 0) {
     const DecodeGroup& dg = a.w.dg;
     const int rt = rem / nsplit, sp = rem - rt * nsplit;
     const int32_t* list = dg.list + (int64_t)e * a.w.tcap;
     const int b = a.tab.bits[e];
-    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15]};
+    const ExpertRef ex{a.pool + a.tab.off[e], a.tab.scale[e], dg.cnt[e], list, list[threadIdx.x & 15], tb0, tstep};
     ffn_width<MODE, PLANES, NB, SEQ>(a, lds_bytes, nsplit, rpw, ex, b, rt, sp, xs, tok, prs);
 }
 
@@ -723,19 +726,41 @@ __device__ __forceinline__ int hot_rank(const DecodeGroup& dg, int m, int nf, in
 // their own when a workgroup covers several row tiles.
 constexpr int kHotExtra = 16;
 
-// grid: `extra` workgroups for hot experts, then (routed expert slot, 64
-// rpw-row tile, K split) flattened; slots past the device-side routed count
-// exit at once. The slot's expert comes from the router's list (with
-// bitplane pages the deeper experts first, so the longest workgroups are
-// dispatched first); its page-table entry, pair count and first 16 pairs
-// are then read
-// in one round of independent loads (the pair list has room for at least 16
-// entries). wide (set when the batch has more than 16 tokens): an expert may
-// be hot; a hot expert's 64-row tiles take wide passes, one tile per
-// workgroup. With rpw = 1 that is its routed workgroups; with rpw > 1 its
-// routed workgroups take its first tiles/rpw tiles and, for the first
-// kHotExtra hot experts, the extra workgroups the rest; a later hot expert
-// keeps the passes of 16 tokens over its workgroups' rpw-tile sequences.
+// Gate/up: the first kHotSplit hot experts have each 64-row tile served by
+// kHotShares workgroups, share j taking the passes of 16 tokens that start
+// at 16 j, 16 (j + kHotShares), ... (one wide pass of 64 tokens costs about
+// three passes of 16 on one workgroup, so a hot expert's tiles would
+// otherwise outlast the rest of the launch). Each share streams the tile's
+// codes; the extra shares of one tile sit 8 workgroups apart, so that they
+// run on one XCD and its L2 serves the repeated reads.
+constexpr int kHotSplit = 8;
+constexpr int kHotShares = 4;
+
+// extra workgroup i -> (unit u = hot expert h x row tiles + tile, share j
+// in 1 .. kHotShares - 1); u past the units launched: none
+__device__ __forceinline__ void split_unit(int i, int& u, int& j) {
+    constexpr int G = 8 * (kHotShares - 1);
+    const int q = i / G, r = i - q * G;
+    j = 1 + r / 8;
+    u = q * 8 + (r & 7);
+}
+
+// grid: `extra` workgroups for hot experts (gate/up: the token shares of
+// the first kHotSplit; down: tiles beyond the routed workgroups' own), then
+// (routed expert slot, 64 rpw-row tile, K split) flattened; slots past the
+// device-side routed count exit at once. The slot's expert comes from the
+// router's list (with bitplane pages the deeper experts first, so the
+// longest workgroups are dispatched first); its page-table entry, pair count
+// and first 16 pairs are then read in one round of independent loads (the
+// pair list has room for at least 16 entries). wide (set when the batch has
+// more than 16 tokens): an expert may be hot. Gate/up: the tiles of the
+// first kHotSplit hot experts are shared by token passes as above, those of
+// later hot experts take wide passes. Down: a hot expert's 64-row tiles take
+// wide passes, one tile per workgroup. With rpw = 1 that is its routed
+// workgroups; with rpw > 1 its routed workgroups take its first tiles/rpw
+// tiles and, for the first kHotExtra hot experts, the extra workgroups the
+// rest; a later hot expert keeps the passes of 16 tokens over its
+// workgroups' rpw-tile sequences.
 template <int MODE, bool PLANES, int SEQ>
 __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArgs a, int lds_bytes, int tiles,
                                                                           int nsplit, int rpw, int extra) {
@@ -744,27 +769,50 @@ __global__ __launch_bounds__(kThreads, MODE == 0 ? 3 : 4) void ffn_kernel(FfnArg
     __shared__ int prs[16 * kWideNB];   // the pairs t k + j of the current pass
     const DecodeGroup& dg = a.w.dg;
     const int own = tiles / rpw;   // 64-row tiles of a hot expert its routed workgroups take
-    if ((int)blockIdx.x < extra) {
+    // the workgroup's expert, share of it (row tile and K split), token
+    // passes and pass width; one call site per width
+    int e, rem, tb0 = 0, tstep = 0;
+    bool wide = false;
+    if (MODE == 0 && (int)blockIdx.x < extra) {
+        int u, j;
+        split_unit(blockIdx.x, u, j);
+        const int h = u / (tiles * nsplit);
+        if (h >= kHotSplit) return;
+        // the same on every lane: kept in a scalar register
+        e = __builtin_amdgcn_readfirstlane(hot_expert(dg, a.max_act, h));
+        if (e < 0) return;
+        rem = u - h * tiles * nsplit;
+        tb0 = 16 * j;
+        tstep = 16 * kHotShares;
+    } else if ((int)blockIdx.x < extra) {
         const int per = (tiles - own) * nsplit;
         const int h = blockIdx.x / per;
-        const int e = hot_expert(dg, a.max_act, h);
+        e = hot_expert(dg, a.max_act, h);
         if (e < 0) return;
-        ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, own * nsplit + (blockIdx.x - h * per), xs,
-                                        tok, prs);
-        return;
+        rem = own * nsplit + (blockIdx.x - h * per);
+        wide = true;
+    } else {
+        const int blk = blockIdx.x - extra;
+        const int per_expert = own * nsplit;
+        const int ai = blk / per_expert;
+        // the counts and both candidates of the slot in one round of loads
+        const int nf = dg.n_act[0], nb = dg.n_act[1];
+        e = slot_expert(ai, a.max_act, nf, nb, dg.act[ai], dg.act[dg.E - a.max_act + ai]);
+        if (e < 0) return;
+        rem = blk - ai * per_expert;
+        if (a.wide && dg.cnt[e] > 16) {
+            if constexpr (MODE == 0) {
+                if (hot_rank(dg, a.max_act, nf, nb, ai) < kHotSplit) tstep = 16 * kHotShares;
+                else wide = true;
+            } else {
+                wide = rpw == 1 || hot_rank(dg, a.max_act, nf, nb, ai) < kHotExtra;
+            }
+        }
     }
-    const int blk = blockIdx.x - extra;
-    const int per_expert = own * nsplit;
-    const int ai = blk / per_expert;
-    // the counts and both candidates of the slot in one round of loads
-    const int nf = dg.n_act[0], nb = dg.n_act[1];
-    const int e = slot_expert(ai, a.max_act, nf, nb, dg.act[ai], dg.act[dg.E - a.max_act + ai]);
-    if (e < 0) return;
-    const int rem = blk - ai * per_expert;
-    if (a.wide && dg.cnt[e] > 16 && (rpw == 1 || hot_rank(dg, a.max_act, nf, nb, ai) < kHotExtra))
+    if (wide)
         ffn_role<MODE, PLANES, kWideNB, 0>(a, lds_bytes, nsplit, 1, e, rem, xs, tok, prs);
     else
-        ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs);
+        ffn_role<MODE, PLANES, 1, SEQ>(a, lds_bytes, nsplit, rpw, e, rem, xs, tok, prs, tb0, tstep);
 }
 
 // Small batches skip the routed-list round trip. Up to kOwnRouteTokens
@@ -964,7 +1012,11 @@ hipError_t launch_ffn_k(const FfnArgs& a, const FfnPlan& p, hipStream_t s, KTime
         }
     }
     auto kernel = kernel_for(rpw);
-    const int extra = (a.wide && rpw > 1) ? kHotExtra * (tiles - tiles / rpw) * p.nsplit : 0;
+    // gate/up: the hot experts' extra token shares, in whole groups of 8
+    // units; down: the hot experts' tiles beyond their routed workgroups'
+    const int units = kHotSplit * tiles * p.nsplit;
+    const int extra = MODE == 0 ? (a.wide ? (units + 7) / 8 * 8 * (kHotShares - 1) : 0)
+                                : ((a.wide && rpw > 1) ? kHotExtra * (tiles - tiles / rpw) * p.nsplit : 0);
     const dim3 grid((unsigned)((int64_t)a.max_act * (tiles / rpw) * p.nsplit + extra));
     return launch_timed(kernel, grid, dim3(kThreads), lds, s, t.start, t.stop, a, (int)lds, tiles, p.nsplit, rpw,
                         extra);

@@ -733,7 +733,7 @@ constexpr int kHotExtra = 16;
 // otherwise outlast the rest of the launch). Each share streams the tile's
 // codes; the extra shares of one tile sit 8 workgroups apart, so that they
 // run on one XCD and its L2 serves the repeated reads.
-constexpr int kHotSplit = 8;
+constexpr int kHotSplit = 16;
 constexpr int kHotShares = 4;
 
 // extra workgroup i -> (unit u = hot expert h x row tiles + tile, share j

@@ -509,13 +509,13 @@ def test_hot_experts_on_multi_tile_workgroups():
 
 @pytest.mark.parametrize("layout", ["eq2", "bitplane"])
 def test_more_hot_experts_than_shared_gate_up_tiles(layout):
-    """Twelve experts take more than 16 tokens: the gate/up tiles of the
-    first eight (in routed order) are shared by four workgroups, each taking
-    every fourth pass of 16 tokens (one of them has 100 tokens: seven passes
-    over its four shares), the other four take wide passes of up to 64
-    tokens. Every output against the oracle."""
+    """Twenty experts take more than 16 tokens: the gate/up tiles of the
+    first sixteen (in routed order) are shared by four workgroups, each
+    taking every fourth pass of 16 tokens (one expert has 100 tokens: seven
+    passes over its four shares if it is among them), the other four take
+    wide passes of up to 64 tokens. Every output against the oracle."""
     from oracle import bitplane
-    wl = synth.WORKLOADS["decode_fine"].scaled(name=f"hot_shares_{layout}", E=128, d=512, F=384, k=2, T=320)
+    wl = synth.WORKLOADS["decode_fine"].scaled(name=f"hot_shares_{layout}", E=128, d=512, F=384, k=2, T=480)
     masters = synth.expert_weights(wl)
     layer, _ = make_layer(wl, masters, max_tokens=wl.T, layout=layout)
     bits = ([(8, 4, 3)[e % 3] for e in range(wl.E)] if layout == "eq2"
@@ -523,10 +523,10 @@ def test_more_hot_experts_than_shared_gate_up_tiles(layout):
     layer.quantize_experts(bits)
     x, logits = synth.tokens(wl)
     logits[:100, 2] += 10.0                             # expert 2: 100 tokens
-    for h in range(1, 12):
+    for h in range(1, 20):
         logits[100 + 20 * (h - 1):120 + 20 * (h - 1), 5 * h + 2] += 10.0   # expert 5h+2: 20 tokens
     counts = torch.bincount(moe.route(logits, wl.k)[0].reshape(-1), minlength=wl.E)
-    assert int((counts > 16).sum()) == 12 and int(counts[2]) >= 100
+    assert int((counts > 16).sum()) == 20 and int(counts[2]) >= 100
     log(f"hot experts ({layout}) {torch.nonzero(counts > 16).reshape(-1).tolist()}, counts {counts[counts > 16].tolist()}")
     y = layer.moe_forward(x.cuda(), logits.cuda())
     if layout == "eq2":
